@@ -1,0 +1,166 @@
+"""Seeded synthetic inputs for the KLA scan: the five named workloads and
+arbitrary shapes.
+
+This module only draws random numbers and shapes them into gate tensors; it
+holds none of the filter's arithmetic.  Both the CPU oracle and the HIP
+library are fed from here, so both sides always see the same tensors.
+
+Recipe (every workload):
+  * draw four float64 tensors of shape [B, H, T, D] from one seeded
+    ``torch.Generator`` in the order z_a, z_p, z_phi, y (standard normals, or
+    fair coin flips for the "hard" gates);
+  * map them to gates in float64;
+  * round each gate once to the input dtype (fp32 round-to-nearest-even; bf16
+    via fp32, then round-to-nearest-even).
+The initial posterior is lam0 = 1, eta0 = 0 (fp32, [B, H, D]) unless a test
+asks for a random one.
+
+Gate families:
+  std  : a = sigmoid(z_a + 2), p = softplus(z_p), phi = softplus(z_phi),
+         b = phi * y
+  slow : a = 1 - 1e-3 * sigmoid(z_a), p = 1e-4 * softplus(z_p),
+         phi = softplus(z_phi), b = phi * y
+  hard : a in {1e-3, 1}, p in {0, 1}, phi in {0, 1e4}, y in {-1, +1}, each
+         equiprobable, b = phi * y
+softplus(x) = log(1 + e^x) computed as logaddexp(0, x); sigmoid(x) =
+1 / (1 + e^-x).
+
+The gate scales follow the KLA parameterisation reviewed on the Pith page for
+arXiv 2602.10743 (a decay in (0, 1], learned process noise, non-negative
+evidence precision) and the layer shapes of its MAD and MQAR hyper-parameter
+tables (H * D = 1024 and 4096 channels, sequence length 2048 and longer).
+The data sets themselves are not used: these tensors stand in for them.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    key: int
+    name: str
+    B: int
+    H: int
+    T: int
+    D: int
+    dtype: str  # "f32" or "bf16": dtype of a, p, phi, b
+    gates: str  # "std", "slow" or "hard"
+    seed: int
+
+    @property
+    def shape(self):
+        return (self.B, self.H, self.T, self.D)
+
+    @property
+    def elements(self) -> int:
+        return self.B * self.H * self.T * self.D
+
+    @property
+    def channels(self) -> int:
+        return self.B * self.H * self.D
+
+    def describe(self) -> str:
+        return "%s B=%d H=%d T=%d D=%d %s gates=%s seed=%d" % (
+            self.name, self.B, self.H, self.T, self.D, self.dtype, self.gates, self.seed)
+
+
+WORKLOADS = {
+    0: Workload(0, "tiny-ref", 1, 1, 256, 16, "f32", "std", 0),
+    1: Workload(1, "small-lm-layer", 8, 16, 2048, 64, "f32", "std", 1),
+    2: Workload(2, "1b-scale-layer", 4, 32, 8192, 128, "bf16", "std", 2),
+    3: Workload(3, "long-context", 1, 32, 131072, 128, "f32", "slow", 3),
+    4: Workload(4, "state-tracking-stress", 256, 8, 512, 32, "f32", "hard", 4),
+}
+
+TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _round(x64: torch.Tensor, dtype: str) -> torch.Tensor:
+    x32 = x64.to(torch.float32)
+    if dtype == "f32":
+        return x32
+    if dtype == "bf16":
+        return x32.to(torch.bfloat16)
+    raise ValueError("unknown dtype %r" % dtype)
+
+
+def _softplus(x: torch.Tensor) -> torch.Tensor:
+    return torch.logaddexp(torch.zeros_like(x), x)
+
+
+def _draw(shape, gen, device, gates):
+    if gates == "hard":
+        return torch.randint(0, 2, shape, generator=gen, device=device).to(torch.float64)
+    return torch.randn(shape, generator=gen, device=device, dtype=torch.float64)
+
+
+def make_gates(shape, gates: str = "std", dtype: str = "f32", seed: int = 0,
+               device="cpu"):
+    """Returns dict(a, p, phi, b) of tensors of `shape` ([B, H, T, D])."""
+    device = torch.device(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    shape = tuple(int(s) for s in shape)
+
+    z = _draw(shape, gen, device, gates)
+    if gates == "std":
+        a64 = torch.sigmoid(z + 2.0)
+    elif gates == "slow":
+        a64 = 1.0 - 1e-3 * torch.sigmoid(z)
+    elif gates == "hard":
+        a64 = torch.where(z > 0.5, 1.0, 1e-3)
+    else:
+        raise ValueError("unknown gate family %r" % gates)
+    a = _round(a64, dtype)
+    del z, a64
+
+    z = _draw(shape, gen, device, gates)
+    if gates == "std":
+        p64 = _softplus(z)
+    elif gates == "slow":
+        p64 = 1e-4 * _softplus(z)
+    else:
+        p64 = torch.where(z > 0.5, 1.0, 0.0)
+    p = _round(p64, dtype)
+    del z, p64
+
+    z = _draw(shape, gen, device, gates)
+    if gates in ("std", "slow"):
+        phi64 = _softplus(z)
+    else:
+        phi64 = torch.where(z > 0.5, 1e4, 0.0)
+    phi = _round(phi64, dtype)
+    del z
+
+    z = _draw(shape, gen, device, gates)
+    y = z if gates in ("std", "slow") else torch.where(z > 0.5, 1.0, -1.0)
+    b = _round(phi64 * y, dtype)
+    del z, y, phi64
+    return {"a": a, "p": p, "phi": phi, "b": b}
+
+
+def make_initial_state(B, H, D, random: bool = False, seed: int = 0, device="cpu"):
+    """lam0, eta0 as fp32 [B, H, D]: (1, 0), or lam0 = softplus(N) + 0.1 and
+    eta0 = lam0 * N when random."""
+    device = torch.device(device)
+    if not random:
+        return (torch.ones((B, H, D), dtype=torch.float32, device=device),
+                torch.zeros((B, H, D), dtype=torch.float32, device=device))
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed) + 7919)
+    z1 = torch.randn((B, H, D), generator=gen, device=device, dtype=torch.float64)
+    z2 = torch.randn((B, H, D), generator=gen, device=device, dtype=torch.float64)
+    lam0 = _softplus(z1) + 0.1
+    return lam0.to(torch.float32), (lam0 * z2).to(torch.float32)
+
+
+def make_workload(key: int, device="cpu", seed: int | None = None):
+    """Gates and initial state of a named workload (0..4)."""
+    w = WORKLOADS[key]
+    g = make_gates(w.shape, w.gates, w.dtype, w.seed if seed is None else seed, device)
+    g["lam0"], g["eta0"] = make_initial_state(w.B, w.H, w.D, device=device)
+    return g

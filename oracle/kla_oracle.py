@@ -1,0 +1,113 @@
+"""ctypes wrapper around ``kla_oracle.c`` (the float64 covariance-form filter).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  The arithmetic lives
+in ``kla_oracle.c``; this module only converts arrays and calls it.
+
+The filter follows the "KLA Part 1" primer, section 5.1 (one predict and one
+update per token, a missing observation being zero precision) applied per
+channel as the Pith review of arXiv 2602.10743 prescribes for the diagonal
+model ("Load-bearing premise").
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "kla_oracle.c")
+LIBRARY = os.path.join(_HERE, "libkla_oracle.so")
+
+GCC_FLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+             "-shared", "-fPIC", "-std=c99"]
+
+
+def build_oracle(out: str = LIBRARY, src: str = SOURCE) -> str:
+    """Compiles an oracle source into a shared library with gcc; returns its path."""
+    tmp = out + ".tmp%d" % os.getpid()
+    subprocess.run(["gcc", *GCC_FLAGS, src, "-o", tmp, "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
+
+
+class OracleLibrary:
+    """One loaded copy of the oracle shared library."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        dp = ctypes.POINTER(ctypes.c_double)
+        lib.kla_oracle_scan.argtypes = [dp] * 9 + [ctypes.c_int64] * 4 + [ctypes.c_int]
+        lib.kla_oracle_scan.restype = ctypes.c_int
+        lib.kla_oracle_threads.argtypes = [ctypes.c_int]
+        lib.kla_oracle_threads.restype = ctypes.c_int
+        self._lib = lib
+        self.path = path
+
+    def threads(self, nthreads: int | None = None) -> int:
+        return int(self._lib.kla_oracle_threads(int(nthreads or 0)))
+
+    def scan(self, a, p, phi, b, lam0=None, eta0=None, nthreads: int | None = None):
+        """Runs the float64 filter.
+
+        a, p, phi, b: array-likes of shape [B, H, T, D] (any float dtype; the
+        values are upcast to float64 exactly).  lam0, eta0: [B, H, D],
+        default 1 and 0.  Returns (lam, eta, eta_abs), float64 [B, H, T, D].
+        """
+        a = _as_f64(a)
+        if a.ndim != 4:
+            raise ValueError("gates must be [B, H, T, D]")
+        B, H, T, D = a.shape
+        shape = (B, H, T, D)
+        p, phi, b = (_as_f64(x, shape) for x in (p, phi, b))
+        lam0 = _as_f64(np.ones((B, H, D)) if lam0 is None else lam0, (B, H, D))
+        eta0 = _as_f64(np.zeros((B, H, D)) if eta0 is None else eta0, (B, H, D))
+        lam, eta, eta_abs = np.empty(shape), np.empty(shape), np.empty(shape)
+        rc = self._lib.kla_oracle_scan(
+            _ptr(a), _ptr(p), _ptr(phi), _ptr(b), _ptr(lam0), _ptr(eta0),
+            _ptr(lam), _ptr(eta), _ptr(eta_abs), B, H, T, D, int(nthreads or 0))
+        if rc != 0:
+            raise ValueError("oracle rejected the sizes")
+        return lam, eta, eta_abs
+
+
+def _as_f64(x, shape=None):
+    if hasattr(x, "detach"):  # a torch tensor: copy to host, upcast exactly
+        x = x.detach().to("cpu")
+        x = x.double().numpy() if x.dtype.is_floating_point else x.numpy()
+    arr = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    if shape is not None and arr.shape != tuple(shape):
+        raise ValueError("expected shape %s, got %s" % (tuple(shape), arr.shape))
+    return arr
+
+
+def _ptr(arr):
+    return arr.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+_lock = threading.Lock()
+_default = None
+
+
+def _library() -> OracleLibrary:
+    global _default
+    with _lock:
+        if _default is None:
+            if (not os.path.exists(LIBRARY)
+                    or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE)):
+                build_oracle()
+            _default = OracleLibrary(LIBRARY)
+        return _default
+
+
+def oracle_threads(nthreads: int | None = None) -> int:
+    """Threads the oracle's parallel loop uses for a given request."""
+    return _library().threads(nthreads)
+
+
+def oracle_scan(a, p, phi, b, lam0=None, eta0=None, nthreads: int | None = None):
+    """The float64 oracle; see ``OracleLibrary.scan``."""
+    return _library().scan(a, p, phi, b, lam0, eta0, nthreads)

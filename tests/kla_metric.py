@@ -1,0 +1,79 @@
+"""Parity metric between fp32 scan outputs and the float64 oracle.
+
+Readings of "maximum relative error" for this scan (the pages print none):
+
+* lam (posterior precision, always > 0, a sum of non-negative terms):
+  max |lam_hat - lam| / lam.
+* eta (information mean) is a signed sum that can cancel to near zero, so a
+  plain relative error is ill-posed there.  Its error is divided by the
+  cancellation-free magnitude eta_abs (the same recursion with |b| and a
+  non-negative start), floored at lam * 2^-126 so that only posterior means
+  |eta| / lam below fp32's normal range are forgiven:
+  max |eta_hat - eta| / max(eta_abs, lam * 2^-126).
+* Range: where the exact value rounds to an fp32 overflow, the output must be
+  the infinity of the same sign; everywhere else it must be finite.  Any NaN
+  fails.
+
+The plain |eta_hat - eta| / |eta| over elements that do not cancel
+(|eta| >= 0.1 eta_abs) is reported too, without a gate.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+TINY = 2.0 ** -126
+
+TOL_F32 = 1e-4   # fp32 gate inputs
+TOL_BF16 = 2e-2  # bf16 gate inputs (oracle runs on the same bf16 values)
+
+
+def _np(x):
+    if hasattr(x, "detach"):
+        return x.detach().to("cpu").numpy()
+    return np.asarray(x)
+
+
+def compare(lam_hat, eta_hat, lam, eta, eta_abs) -> dict:
+    """Returns the error report of fp32 outputs against float64 oracle values."""
+    lam_hat = _np(lam_hat).astype(np.float64)
+    eta_hat = _np(eta_hat).astype(np.float64)
+    lam, eta, eta_abs = (np.asarray(x, dtype=np.float64) for x in (lam, eta, eta_abs))
+    with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+        lam32 = lam.astype(np.float32)
+        eta32 = eta.astype(np.float32)
+        lam_over = np.isinf(lam32)
+        eta_over = np.isinf(eta32)
+
+        rep = {"n": int(lam.size)}
+        rep["nan"] = int(np.isnan(lam_hat).sum() + np.isnan(eta_hat).sum())
+        # overflow rule
+        bad_inf = (lam_over & (lam_hat != np.inf)).sum()
+        bad_inf += (eta_over & (eta_hat != np.sign(eta) * np.inf)).sum()
+        bad_inf += (~lam_over & ~np.isfinite(lam_hat)).sum()
+        bad_inf += (~eta_over & ~np.isfinite(eta_hat)).sum()
+        rep["range_violations"] = int(bad_inf)
+        rep["lam_overflow"] = int(lam_over.sum())
+        rep["eta_overflow"] = int(eta_over.sum())
+
+        ok = ~lam_over & np.isfinite(lam_hat)
+        lam_err = np.abs(lam_hat - lam) / lam
+        rep["lam_max_rel"] = float(lam_err[ok].max()) if ok.any() else 0.0
+
+        ok = ~eta_over & ~lam_over & np.isfinite(eta_hat)
+        den = np.maximum(eta_abs, lam * TINY)
+        eta_err = np.abs(eta_hat - eta) / den
+        rep["eta_max_scaled"] = float(eta_err[ok].max()) if ok.any() else 0.0
+
+        plain = ok & (np.abs(eta) >= 0.1 * eta_abs) & (eta != 0)
+        rel = np.abs(eta_hat - eta) / np.abs(eta)
+        rep["eta_max_rel_noncancel"] = float(rel[plain].max()) if plain.any() else 0.0
+    return rep
+
+
+def assert_parity(rep: dict, tol: float, what: str = ""):
+    msg = "%s %r" % (what, rep)
+    assert rep["nan"] == 0, msg
+    assert rep["range_violations"] == 0, msg
+    assert rep["lam_max_rel"] <= tol, msg
+    assert rep["eta_max_scaled"] <= tol, msg

@@ -1,0 +1,177 @@
+"""Benchmark of the forward KLA scan (libkla) on one MI355X.
+
+A step is one kla_scan_fwd call over one batch of synthetic gates: the whole
+scan (chunk matrices, carry look-back, replay and output writes) in a single
+kernel launch.  Inputs are generated on the GPU and are resident in HBM
+before timing; two input/output sets alternate so that the 256 MB Infinity
+Cache cannot serve one step from the previous one.
+
+Prints one JSON line: throughput in scanned elements (B*H*T*D) per second,
+the roofline of the scan kernel (HBM bound; algorithmic bytes are 4 gate
+reads + 2 float32 writes per element) and the float64 CPU oracle timed on a
+sample of the same workload as a baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+KERNEL_SOURCE = os.path.join(ROOT, "linear_attention_sequence_kla_amd", "csrc", "kla_scan.hip")
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def bytes_per_element(dtype: str) -> int:
+    return 4 * (4 if dtype == "f32" else 2) + 2 * 4
+
+
+def load_traffic(workload_key: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic_workload%d.json" % workload_key)
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_sha256_16") != kernel_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, g_dev, budget_s: float = 12.0):
+    """Times the float64 oracle on the host on a bounded sample of the
+    workload (whole slabs, full T), scaled to elements per second."""
+    from oracle import oracle_scan, oracle_threads
+    threads = len(os.sched_getaffinity(0))
+    used = oracle_threads(threads)
+    # Sample: leading slabs (b, h) with every channel and the full sequence.
+    slabs_total = w.B * w.H
+    per_slab = w.T * w.D
+    n_slabs = max(1, min(slabs_total, int(2e8 // max(per_slab, 1))))
+    sel = {}
+    for k in ("a", "p", "phi", "b"):
+        x = g_dev[k].reshape(slabs_total, w.T, w.D)[:n_slabs]
+        sel[k] = x.to("cpu").double().numpy().reshape(1, n_slabs, w.T, w.D)
+    lam0 = g_dev["lam0"].reshape(slabs_total, w.D)[:n_slabs].cpu().double().numpy()
+    eta0 = g_dev["eta0"].reshape(slabs_total, w.D)[:n_slabs].cpu().double().numpy()
+    lam0 = lam0.reshape(1, n_slabs, w.D)
+    eta0 = eta0.reshape(1, n_slabs, w.D)
+    elems = n_slabs * per_slab
+    reps, t_total = 0, 0.0
+    while t_total < budget_s and reps < 50:
+        t0 = time.perf_counter()
+        oracle_scan(sel["a"], sel["p"], sel["phi"], sel["b"], lam0, eta0, nthreads=used)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    return {"value": elems * reps / t_total, "unit": "elements/s", "cores": used,
+            "kind": "oracle",
+            "sample": "%d of %d slabs (all %d channels, full T=%d), %d runs, %.1f s"
+                      % (n_slabs, slabs_total, w.D, w.T, reps, t_total)}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=1,
+                    help="0..4; the headline is 1 (small-LM layer)")
+    ap.add_argument("--sets", type=int, default=2, help="input/output sets to rotate")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the scan's channels are independent, so each "
+              "GPU of a data-parallel job runs this same kernel on its own share; "
+              "--gpus %d is not supported here" % args.gpus, file=sys.stderr)
+        return 2
+
+    import torch
+
+    from kla_inputs import WORKLOADS, make_workload
+    from linear_attention_sequence_kla_amd import get_workspace, scan_fwd, workspace_health
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sets = []
+    for k in range(args.sets):
+        g = make_workload(args.workload, device=dev, seed=w.seed + 1000 * k)
+        lam = torch.empty(w.shape, dtype=torch.float32, device=dev)
+        eta = torch.empty(w.shape, dtype=torch.float32, device=dev)
+        sets.append((g, (lam, eta)))
+    torch.cuda.synchronize(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        g, out = sets[i % len(sets)]
+        scan_fwd(g["a"], g["p"], g["phi"], g["b"], g["lam0"], g["eta0"], out=out)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize(dev)
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    health = workspace_health(get_workspace(0, dev, stream))
+    if health != 0:
+        print("warning: workspace health word %#x" % health, file=sys.stderr)
+
+    n = w.elements
+    ms_step = wall * 1e3 / args.steps
+    k_avg = sum(kernel_ms) / len(kernel_ms)
+    bpe = bytes_per_element(w.dtype)
+    achieved = n * bpe / (k_avg * 1e-3) / 1e9
+    traffic = load_traffic(args.workload)
+    rec = {
+        "metric": "KLA scan elements (B*H*T*D)/s and achieved HBM GB/s vs peak, 1 MI355X",
+        "value": n / (ms_step * 1e-3),
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": w.describe(), "B": w.B, "H": w.H, "T": w.T, "D": w.D,
+                   "io_dtype": w.dtype, "elements": n, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "kla_scan_kernel", "kernel_ms_avg": k_avg,
+                     "kernel_ms_min": min(kernel_ms), "bytes_per_element": bpe},
+        "health": health,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, sets[0][0])
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,127 @@
+/*
+ * kla.h -- C ABI of libkla: the forward pass of the Kalman Linear Attention
+ * (KLA) scan on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (Pith review of arXiv 2602.10743, "What carries the
+ * argument" and "Circularity check"; "KLA Part 1" primer, sections 2 and
+ * 5.1).  Every channel (b, h, d) of a [B, H, T, D] tensor runs its own scalar
+ * Kalman filter in information form.  With the posterior precision lam and
+ * information mean eta before the first token given by lam0, eta0, each token
+ * t = 1..T applies
+ *
+ *     predict:  lam_prior = lam_{t-1} / (a_t^2 + p_t lam_{t-1})
+ *     update:   lam_t     = lam_prior + phi_t
+ *     mean:     eta_t     = f_t eta_{t-1} + b_t,
+ *               f_t       = a_t / (a_t^2 + p_t lam_{t-1})
+ *
+ * i.e. lam_t = M_t(lam_{t-1}) is the Moebius map of the 2x2 matrix
+ * M_t = [[1 + p_t phi_t, a_t^2 phi_t], [p_t, a_t^2]] and eta follows an
+ * affine recursion whose forget gate is the precision ratio.  a_t is the
+ * state decay, p_t the process-noise variance, phi_t the precision of the
+ * token's evidence and b_t its information (phi_t times the observed value).
+ * Both recursions are associative, so the library evaluates them as a
+ * chunked parallel scan; the result equals the sequential filter up to
+ * rounding.
+ *
+ * Outputs: lam[..., t-1, :] and eta[..., t-1, :] hold lam_t and eta_t, the
+ * posterior after token t.  The last time row is the final state: passing it
+ * as lam0/eta0 of a following call continues the same sequence.
+ */
+#ifndef KLA_H
+#define KLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define KLA_API __attribute__((visibility("default")))
+#else
+#define KLA_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KLA_OK = 0,
+    KLA_ERR_INVALID_ARG = 1,  /* null pointer, negative size, overflow, aliasing */
+    KLA_ERR_UNSUPPORTED = 2,  /* dtype or alignment the library does not handle */
+    KLA_ERR_WORKSPACE = 3,    /* workspace missing, too small or misaligned */
+    KLA_ERR_HIP = 4           /* the HIP runtime reported an error */
+} kla_status;
+
+typedef enum {
+    KLA_DTYPE_F32 = 0,  /* IEEE binary32 */
+    KLA_DTYPE_BF16 = 1  /* bfloat16 (upper half of a binary32) */
+} kla_dtype;
+
+/*
+ * Bytes of device workspace kla_scan_fwd needs for this problem.  Returns 0
+ * when the sizes are invalid (negative or overflowing) or when the problem is
+ * empty (some size is 0, so there is nothing to do).
+ */
+KLA_API size_t kla_scan_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int64_t D,
+                                   kla_dtype in_dtype);
+
+/*
+ * Forward KLA scan.
+ *
+ *   a, p, phi, b  device pointers, [B, H, T, D] row-major (D fastest), all of
+ *                 dtype in_dtype; naturally aligned (4 B for f32, 2 B for bf16).
+ *                 Domain: a > 0, p >= 0, phi >= 0, all finite, and every
+ *                 per-token factor (1 + p phi, a^2 phi, |b| p, |b| a^2) below
+ *                 2^120.  Outside it the results are unspecified; NaN inputs
+ *                 propagate.
+ *   lam0, eta0    device pointers, [B, H, D] float32: the posterior precision
+ *                 (> 0) and information mean before the first token.  Either
+ *                 may be NULL, meaning lam0 = 1 and eta0 = 0 for every channel.
+ *   lam, eta      device pointers, [B, H, T, D] float32 outputs, 4-B aligned.
+ *                 They must not overlap each other, an input or the workspace.
+ *                 Values whose float32 rounding overflows are written as
+ *                 +-infinity.
+ *   B, H, T, D    sizes.  If any is 0 the call does nothing and returns KLA_OK.
+ *   workspace     device memory of at least kla_scan_fwd_workspace_size(...)
+ *                 bytes, 256-B aligned, owned by the caller.  It must be
+ *                 zero-filled before its first use; every call leaves it ready
+ *                 for the next one, so it is zeroed once, not per call.  Calls
+ *                 that run at the same time must use different workspaces.
+ *   stream        the hipStream_t to enqueue on (NULL: the null stream).
+ *
+ * The call validates its arguments on the host and returns an error before
+ * enqueueing anything (no partial writes).  On KLA_OK the work is enqueued
+ * and runs asynchronously on `stream`; the caller keeps every buffer alive
+ * until it completes.  The library allocates and frees nothing and holds no
+ * global state; it is re-entrant and thread-safe.
+ */
+KLA_API kla_status kla_scan_fwd(const void *a, const void *p, const void *phi,
+                        const void *b, kla_dtype in_dtype,
+                        const float *lam0, const float *eta0,
+                        float *lam, float *eta,
+                        int64_t B, int64_t H, int64_t T, int64_t D,
+                        void *workspace, size_t workspace_bytes,
+                        void *stream);
+
+/*
+ * Reads the workspace's health word after the calls that used it have
+ * completed (it synchronizes `stream`).  *flags_out is 0 when every call so
+ * far ran normally; bit 0 is set if a chunk gave up waiting for the carry of
+ * its predecessor (its outputs are then wrong).  The word is cleared by the
+ * read.  Returns KLA_ERR_WORKSPACE for a NULL workspace.
+ */
+KLA_API kla_status kla_workspace_health(void *workspace, uint32_t *flags_out, void *stream);
+
+/* Static text for a status code. */
+KLA_API const char *kla_status_string(kla_status s);
+
+/*
+ * Thread-local text describing the last error the calling thread got from
+ * this library (argument name, HIP error string), or "" if none.
+ */
+KLA_API const char *kla_last_error_detail(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KLA_H */

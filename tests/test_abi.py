@@ -1,0 +1,108 @@
+"""The C ABI on the CPU: the library loads, exports what include/kla.h
+declares, sizes its workspace, and rejects bad arguments before touching the
+GPU (none of these calls launch anything)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kla.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from linear_attention_sequence_kla_amd import library
+    return library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"KLA_API\s+[\w\s\*]*?\b(kla_\w+)\s*\(", text)
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    assert {"kla_scan_fwd", "kla_scan_fwd_workspace_size", "kla_status_string",
+            "kla_last_error_detail", "kla_workspace_health"} <= set(names)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code, name in enumerate(["KLA_OK", "KLA_ERR_INVALID_ARG", "KLA_ERR_UNSUPPORTED",
+                                 "KLA_ERR_WORKSPACE", "KLA_ERR_HIP"]):
+        assert lib.kla_status_string(code).decode() == name
+
+
+def test_workspace_size(lib):
+    ws = lib.kla_scan_fwd_workspace_size
+    assert ws(0, 1, 1, 1, 0) == 0          # empty problem
+    assert ws(-1, 1, 1, 1, 0) == 0         # invalid
+    assert ws(1, 1, 1, 1, 7) == 0          # unknown dtype
+    assert ws(2 ** 40, 2 ** 40, 1, 1, 0) == 0  # overflow
+    small = ws(1, 1, 256, 16, 0)
+    assert small > 256 and small % 8 == 0
+    # grows with the number of tiles, same for both dtypes
+    assert ws(8, 16, 2048, 64, 0) > small
+    assert ws(8, 16, 2048, 64, 0) == ws(8, 16, 2048, 64, 1)
+
+
+def _call(lib, a=1, p=1, phi=1, b=1, dtype=0, lam=0x1000000, eta=0x2000000,
+          shape=(1, 1, 4, 4), ws=0x4000000, ws_bytes=1 << 20):
+    vp = ctypes.c_void_p
+    B, H, T, D = shape
+    st = lib.kla_scan_fwd(vp(a * 0x100000), vp(p * 0x200000), vp(phi * 0x300000),
+                          vp(b * 0x400000), dtype, None, None, vp(lam), vp(eta),
+                          B, H, T, D, vp(ws), ws_bytes, None)
+    return st, lib.kla_last_error_detail().decode()
+
+
+def test_argument_errors_before_launch(lib):
+    # Fake pointers: safe only where no GPU could run a launch that slipped through.
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("uses fake device pointers; argument errors are tested on GPUs elsewhere")
+    # null gate
+    st, msg = _call(lib, a=0)
+    assert st == 1 and "a is NULL" in msg
+    # negative size
+    st, msg = _call(lib, shape=(1, -1, 4, 4))
+    assert st == 1 and "negative" in msg
+    # unknown dtype
+    st, _ = _call(lib, dtype=5)
+    assert st == 2
+    # null workspace / too small / misaligned
+    st, _ = _call(lib, ws=0)
+    assert st == 3
+    st, msg = _call(lib, ws_bytes=16)
+    assert st == 3 and "needs" in msg
+    st, _ = _call(lib, ws=0x4000010)
+    assert st == 3
+    # output overlapping an input
+    st, msg = _call(lib, lam=0x100000)
+    assert st == 1 and "overlaps" in msg
+    # misaligned output
+    st, _ = _call(lib, lam=0x1000002)
+    assert st == 2
+    # outputs overlapping each other, and the workspace
+    st, msg = _call(lib, eta=0x1000004)
+    assert st == 1 and "overlaps" in msg
+    st, msg = _call(lib, ws=0x1000000 - 256)
+    assert st == 1 and "overlaps" in msg
+    # empty problem: nothing to do, no pointer needed
+    st, _ = _call(lib, a=0, shape=(1, 1, 0, 4))
+    assert st == 0
+    # slab too large for 32-bit offsets
+    st, msg = _call(lib, shape=(1, 1, 1 << 31, 64), ws_bytes=1 << 62)
+    assert st in (1, 2)
+
+
+def test_health_rejects_null(lib):
+    out = ctypes.c_uint32(0)
+    assert lib.kla_workspace_health(None, ctypes.byref(out), None) == 3

@@ -1,0 +1,199 @@
+"""GPU parity: libkla's scan (through the C ABI) against the float64 oracle.
+
+Both sides get the same seeded tensors from kla_inputs.  The bar is the
+metric of kla_metric: max relative error 1e-4 on lam and 1e-4 on eta scaled
+by its cancellation-free magnitude for fp32 gates, 2e-2 for bf16 gates, the
+fp32 overflow rule, and no NaN.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from kla_inputs import WORKLOADS, make_gates, make_initial_state, make_workload
+from kla_metric import TOL_BF16, TOL_F32, assert_parity, compare
+from oracle import oracle_scan
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def run_gpu(g, use_state=True):
+    from linear_attention_sequence_kla_amd import scan_fwd
+    lam0 = g["lam0"].to(DEV) if use_state else None
+    eta0 = g["eta0"].to(DEV) if use_state else None
+    lam, eta = scan_fwd(g["a"].to(DEV), g["p"].to(DEV), g["phi"].to(DEV), g["b"].to(DEV),
+                        lam0, eta0)
+    torch.cuda.synchronize(DEV)
+    return lam, eta
+
+
+def health():
+    from linear_attention_sequence_kla_amd import get_workspace, workspace_health
+    return workspace_health(get_workspace(0, DEV, torch.cuda.current_stream(DEV)))
+
+
+def full_parity(g, tol, what):
+    lam, eta = run_gpu(g)
+    assert health() == 0, what
+    ref = oracle_scan(g["a"], g["p"], g["phi"], g["b"], g["lam0"], g["eta0"])
+    rep = compare(lam.cpu(), eta.cpu(), *ref)
+    _say("%s: %s" % (what, rep))
+    assert_parity(rep, tol, what)
+    return rep
+
+
+@pytest.mark.parametrize("key", [0, 1, 4])
+def test_workload_full(key):
+    w = WORKLOADS[key]
+    _say("workload %s" % w.describe())
+    g = make_workload(key, device="cpu")
+    rep = full_parity(g, TOL_F32, w.describe())
+    if key == 4:
+        # the hard gates do overflow fp32 somewhere: the rule was exercised
+        assert rep["lam_overflow"] > 0 and rep["eta_overflow"] > 0
+
+
+def _sample_channels(C, n, seed):
+    rng = np.random.default_rng(seed)
+    picks = set(rng.choice(C, size=min(n, C), replace=False).tolist())
+    picks.update({0, C - 1, min(63, C - 1), min(64, C - 1)})
+    return np.array(sorted(picks))
+
+
+def _gather(x, D, q):
+    """x: [B, H, T, D] on any device -> [1, 1, T, len(q)] (channels q)."""
+    B, H, T, _ = x.shape
+    flat = x.reshape(B * H, T, D)
+    slab = torch.as_tensor(q // D, device=x.device)
+    d = torch.as_tensor(q % D, device=x.device)
+    return flat[slab, :, d].transpose(0, 1).reshape(1, 1, T, len(q)).contiguous()
+
+
+@pytest.mark.parametrize("key", [2, 3])
+def test_workload_full_size_sampled(key):
+    """Full-size launch; the oracle checks a sample of whole channels."""
+    w = WORKLOADS[key]
+    _say("workload %s (sampled channels)" % w.describe())
+    g = make_workload(key, device=DEV)
+    from linear_attention_sequence_kla_amd import scan_fwd
+    lam, eta = scan_fwd(g["a"], g["p"], g["phi"], g["b"], g["lam0"], g["eta0"])
+    torch.cuda.synchronize(DEV)
+    assert health() == 0
+    q = _sample_channels(w.channels, 384, seed=key)
+    gs = {k: _gather(g[k], w.D, q).cpu() for k in ("a", "p", "phi", "b")}
+    lam0 = g["lam0"].reshape(-1)[torch.as_tensor(q, device=DEV)].reshape(1, 1, -1).cpu()
+    eta0 = g["eta0"].reshape(-1)[torch.as_tensor(q, device=DEV)].reshape(1, 1, -1).cpu()
+    ref = oracle_scan(gs["a"], gs["p"], gs["phi"], gs["b"], lam0, eta0)
+    rep = compare(_gather(lam, w.D, q).cpu(), _gather(eta, w.D, q).cpu(), *ref)
+    _say("%s: %s" % (w.describe(), rep))
+    assert_parity(rep, TOL_BF16 if w.dtype == "bf16" else TOL_F32, w.describe())
+    # every output is finite and lam > 0 over the whole tensor
+    assert bool(torch.isfinite(lam).all()) and bool(torch.isfinite(eta).all())
+    assert bool((lam > 0).all())
+
+
+SHAPES = [
+    # (B, H, T, D, gates, dtype)
+    (1, 1, 1, 1, "std", "f32"),          # a single token, a single channel
+    (1, 1, 127, 1, "std", "f32"),        # T below one tile, D below a wave
+    (1, 1, 128, 64, "std", "f32"),       # exactly one tile
+    (1, 1, 129, 64, "std", "f32"),       # one row into a second tile
+    (2, 3, 1000, 7, "std", "f32"),       # ragged everything
+    (3, 2, 517, 100, "slow", "f32"),     # column groups straddle slabs
+    (1, 2, 4099, 33, "hard", "f32"),     # long ragged T with hard gates
+    (2, 2, 300, 128, "std", "bf16"),     # bf16
+    (1, 1, 5000, 200, "slow", "bf16"),   # bf16, ragged D > 64
+    (5, 1, 64, 13, "hard", "f32"),       # T below one wave's rows
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s[:4])) + s[4] + s[5])
+def test_shapes(shape):
+    B, H, T, D, fam, dtype = shape
+    _say("shape %s" % (shape,))
+    g = make_gates((B, H, T, D), fam, dtype, seed=B * 1000 + T)
+    g["lam0"], g["eta0"] = make_initial_state(B, H, D, random=True, seed=T)
+    full_parity(g, TOL_BF16 if dtype == "bf16" else TOL_F32, str(shape))
+
+
+def test_default_initial_state():
+    """NULL lam0/eta0 means lam0 = 1, eta0 = 0."""
+    g = make_gates((2, 2, 300, 40), "std", "f32", seed=5)
+    lam, eta = run_gpu(g, use_state=False)
+    ones, zeros = make_initial_state(2, 2, 40)
+    ref = oracle_scan(g["a"], g["p"], g["phi"], g["b"], ones, zeros)
+    assert_parity(compare(lam.cpu(), eta.cpu(), *ref), TOL_F32, "default state")
+
+
+def test_segmenting_matches_one_call():
+    """Passing the last row of one call as the initial state of the next
+    continues the sequence."""
+    from linear_attention_sequence_kla_amd import scan_fwd
+    g = make_gates((2, 4, 3000, 64), "std", "f32", seed=9)
+    gd = {k: v.to(DEV) for k, v in g.items()}
+    lam0, eta0 = (x.to(DEV) for x in make_initial_state(2, 4, 64, random=True, seed=9))
+    lam, eta = scan_fwd(gd["a"], gd["p"], gd["phi"], gd["b"], lam0, eta0)
+    k = 1111
+    part = lambda x, s: x[:, :, s].contiguous()  # noqa: E731
+    l1, e1 = scan_fwd(*(part(gd[n], slice(0, k)) for n in ("a", "p", "phi", "b")), lam0, eta0)
+    l2, e2 = scan_fwd(*(part(gd[n], slice(k, None)) for n in ("a", "p", "phi", "b")),
+                      l1[:, :, -1].contiguous(), e1[:, :, -1].contiguous())
+    torch.cuda.synchronize(DEV)
+    lam_s = torch.cat([l1, l2], dim=2)
+    eta_s = torch.cat([e1, e2], dim=2)
+    assert torch.allclose(lam_s, lam, rtol=2e-6, atol=0)
+    assert torch.allclose(eta_s, eta, rtol=2e-6, atol=2e-6 * float(eta.abs().max()))
+
+
+def test_repeated_calls_reuse_workspace():
+    """The workspace resets itself: many calls in a row, and a call with a
+    different shape in between, all stay exact and healthy."""
+    g = make_gates((4, 4, 2048, 64), "std", "f32", seed=13)
+    g["lam0"], g["eta0"] = make_initial_state(4, 4, 64, random=True, seed=13)
+    first = run_gpu(g)
+    small = make_gates((1, 1, 300, 5), "std", "f32", seed=14)
+    run_gpu(small, use_state=False)
+    for _ in range(5):
+        again = run_gpu(g)
+    assert health() == 0
+    ref = oracle_scan(g["a"], g["p"], g["phi"], g["b"], g["lam0"], g["eta0"])
+    assert_parity(compare(again[0].cpu(), again[1].cpu(), *ref), TOL_F32, "repeat")
+    assert torch.allclose(first[0], again[0], rtol=1e-6)
+
+
+def test_side_stream():
+    """The call runs on the caller's current stream."""
+    g = make_gates((2, 2, 700, 64), "std", "f32", seed=17)
+    g["lam0"], g["eta0"] = make_initial_state(2, 2, 64, random=True, seed=17)
+    s = torch.cuda.Stream(DEV)
+    with torch.cuda.stream(s):
+        gd = {k: v.to(DEV) for k, v in g.items()}
+        from linear_attention_sequence_kla_amd import scan_fwd
+        lam, eta = scan_fwd(gd["a"], gd["p"], gd["phi"], gd["b"], gd["lam0"], gd["eta0"])
+    s.synchronize()
+    ref = oracle_scan(g["a"], g["p"], g["phi"], g["b"], g["lam0"], g["eta0"])
+    assert_parity(compare(lam.cpu(), eta.cpu(), *ref), TOL_F32, "side stream")
+
+
+def test_argument_errors_on_device():
+    """Host-side validation with real device buffers: nothing is launched."""
+    from linear_attention_sequence_kla_amd import KlaError, scan_fwd
+    g = make_gates((1, 2, 100, 8), "std", "f32", seed=3)
+    gd = {k: v.to(DEV) for k, v in g.items()}
+    small_ws = torch.zeros(64, dtype=torch.uint8, device=DEV)
+    with pytest.raises(KlaError) as e:
+        scan_fwd(gd["a"], gd["p"], gd["phi"], gd["b"], workspace=small_ws)
+    assert e.value.name == "KLA_ERR_WORKSPACE"
+    with pytest.raises(KlaError) as e:
+        scan_fwd(gd["a"], gd["p"], gd["phi"], gd["b"], out=(gd["a"], torch.empty_like(gd["a"])))
+    assert e.value.name == "KLA_ERR_INVALID_ARG"
+    with pytest.raises(ValueError):
+        scan_fwd(gd["a"], gd["p"].double(), gd["phi"], gd["b"])

@@ -23,9 +23,9 @@
 // "Single-pass Parallel Prefix Scan with Decoupled Look-back", 2016):
 //   * a workgroup of W waves owns one tile: 64 channels (one per lane, so a
 //     time row is one coalesced load per wave) by W*L time steps; wave w owns
-//     the L rows starting at w*L.  Tiles are handed out by an atomic ticket in
-//     (chunk, column-group) order, so every tile a workgroup waits for belongs
-//     to a workgroup that is already running.
+//     the L rows starting at w*L.  Tiles are numbered (chunk, column group)
+//     in workgroup-id order; workgroups are dispatched in increasing id, so
+//     every tile a workgroup waits for belongs to one that is already running.
 //   * each wave loads its L rows of a, p, phi, b into registers, where they
 //     stay until the outputs are written (inputs are read from HBM once);
 //   * it folds them into its chunk matrix (float64, renormalised);
@@ -42,13 +42,15 @@
 // same rate as an unpacked float32 FMA.  Inputs and outputs stay 32-bit.
 //
 // Workspace (caller-owned, zero-filled before first use, self-resetting):
-//   [0, 256)         header: u32 ticket, u32 done, u32 epoch, u32 health
+//   [0, 256)         header: u32 reserved[2], u32 epoch, u32 health
 //   flags            u64 per tile: (tag << 32) | status, tag = epoch + 1
 //   matrix records   per tile: 7 x 64 float64 (A B C D E F G per channel)
 //   state records    per tile: 2 x 64 float64 (lam, eta per channel)
 // Flags carry the call's tag, so stale flags of earlier calls read as empty
-// and nothing needs clearing between calls; the last workgroup to finish
-// resets the counters and advances the epoch.
+// and nothing needs clearing between calls; the last workgroup advances the
+// epoch once every workgroup has read it.  Records and flags are accessed
+// only as agent-scope atomics, which stay coherent across XCDs without the
+// L2 write-back/invalidate that a release/acquire fence costs.
 
 #include <hip/hip_runtime.h>
 
@@ -64,6 +66,7 @@ namespace {
 constexpr int kWave = 64;
 constexpr uint32_t kStatusAggregate = 1;  // the tile's own matrix is published
 constexpr uint32_t kStatusInclusive = 2;  // the tile's inclusive state is published
+constexpr uint32_t kStatusFinished = 3;   // a last-chunk tile has its carry-in
 constexpr uint32_t kSpinLimit = 1u << 20; // polls before a look-back gives up
 constexpr int kRenormEvery = 8;           // tokens between renormalisations
 
@@ -205,55 +208,76 @@ struct Args {
     double* state;   // [tile][2][64]
 };
 
-__device__ inline void store_lift(double* rec, int lane, const Lift& n) {
-    rec[0 * kWave + lane] = n.A;
-    rec[1 * kWave + lane] = n.B;
-    rec[2 * kWave + lane] = n.C;
-    rec[3 * kWave + lane] = n.D;
-    rec[4 * kWave + lane] = n.E;
-    rec[5 * kWave + lane] = n.F;
-    rec[6 * kWave + lane] = n.G;
+// Record words are written and read as agent-scope relaxed atomics.  Such
+// accesses are coherent across the L2 caches of all XCDs without any cache
+// write-back or invalidation, so publishing a record only requires its stores
+// to have completed before the flag store is issued.
+__device__ inline void rec_store(double* p, double v) {
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(p), uint64_t(__double_as_longlong(v)),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ inline Lift load_lift(const double* rec, int lane) {
+__device__ inline double rec_load(double* p) {
+    return __longlong_as_double(int64_t(__hip_atomic_load(
+        reinterpret_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
+}
+
+__device__ inline void store_lift(double* rec, int lane, const Lift& n) {
+    rec_store(rec + 0 * kWave + lane, n.A);
+    rec_store(rec + 1 * kWave + lane, n.B);
+    rec_store(rec + 2 * kWave + lane, n.C);
+    rec_store(rec + 3 * kWave + lane, n.D);
+    rec_store(rec + 4 * kWave + lane, n.E);
+    rec_store(rec + 5 * kWave + lane, n.F);
+    rec_store(rec + 6 * kWave + lane, n.G);
+}
+
+__device__ inline Lift load_lift(double* rec, int lane) {
     Lift n;
-    n.A = rec[0 * kWave + lane];
-    n.B = rec[1 * kWave + lane];
-    n.C = rec[2 * kWave + lane];
-    n.D = rec[3 * kWave + lane];
-    n.E = rec[4 * kWave + lane];
-    n.F = rec[5 * kWave + lane];
-    n.G = rec[6 * kWave + lane];
+    n.A = rec_load(rec + 0 * kWave + lane);
+    n.B = rec_load(rec + 1 * kWave + lane);
+    n.C = rec_load(rec + 2 * kWave + lane);
+    n.D = rec_load(rec + 3 * kWave + lane);
+    n.E = rec_load(rec + 4 * kWave + lane);
+    n.F = rec_load(rec + 5 * kWave + lane);
+    n.G = rec_load(rec + 6 * kWave + lane);
     return n;
 }
 
-// Publishes a flag after the record stores of this wave (release, agent scope).
+// Publishes a flag once every record store of this wave has completed.  The
+// records are agent-coherent atomics, so completion (vmcnt reaching zero) is
+// visibility to every other workgroup; no L2 write-back is needed.
 __device__ inline void publish(uint64_t* flag, int lane, uint64_t value) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (lane == 0) __hip_atomic_store(flag, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Records `health` bit 0 and tells whether a wait should give up: after
+// kSpinLimit polls, or as soon as another wait has given up.
+__device__ inline bool give_up(uint32_t spins, uint32_t* header) {
+    if ((spins & 255) != 0) return false;
+    const uint32_t h = __hip_atomic_load(&header[3], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__builtin_amdgcn_readfirstlane(h) != 0 || spins >= kSpinLimit) {
+        __hip_atomic_fetch_or(&header[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return true;
+    }
+    return false;
 }
 
 // Waits until `flag` carries this call's tag with a non-empty status and
 // returns the status (0 if the wait gave up; the health word is then set).
+// The caller's record loads are agent-coherent atomics issued after the flag
+// was seen, so they observe the records published before it.
 __device__ inline uint32_t wait_flag(uint64_t* flag, uint32_t tag, uint32_t* header) {
-    uint32_t spins = 0;
-    while (true) {
+    for (uint32_t spins = 1;; ++spins) {
         const uint64_t v = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
         const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
         if (hi == tag && lo != 0) {
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            asm volatile("" ::: "memory");
             return lo;
         }
-        ++spins;
-        if ((spins & 255) == 0) {
-            const uint32_t h = __hip_atomic_load(&header[3], __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-            if (__builtin_amdgcn_readfirstlane(h) != 0 || spins >= kSpinLimit) {
-                __hip_atomic_fetch_or(&header[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                return 0;
-            }
-        }
+        if (give_up(spins, header)) return 0;
         __builtin_amdgcn_s_sleep(1);
     }
 }
@@ -266,18 +290,18 @@ template <typename In, int L, int W>
 __global__ __launch_bounds__(W * kWave) void kla_scan_kernel(Args g) {
     __shared__ double s_lift[W][7][kWave];
     __shared__ double s_carry[2][kWave];
-    __shared__ uint32_t s_ticket, s_tag;
+    __shared__ uint32_t s_tag;
 
     const int lane = threadIdx.x & (kWave - 1);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
 
-    if (threadIdx.x == 0) {
-        s_ticket = __hip_atomic_fetch_add(&g.header[0], 1u, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
+    // Tiles follow the dispatch order of workgroups, which is increasing
+    // workgroup id: every tile a workgroup waits for has a lower id, so it
+    // was dispatched first and is running or finished.
+    const int64_t ticket = blockIdx.x;
+    if (threadIdx.x == 0)
         s_tag = __hip_atomic_load(&g.header[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-    }
     __syncthreads();
-    const int64_t ticket = __builtin_amdgcn_readfirstlane(s_ticket);
     const uint32_t tag = __builtin_amdgcn_readfirstlane(s_tag);
 
     if (ticket < g.n_tiles) {
@@ -394,8 +418,8 @@ __global__ __launch_bounds__(W * kWave) void kla_scan_kernel(Args g) {
                 while (true) {
                     const uint32_t st = wait_flag(&g.flags[j], tag, g.header);
                     if (st == kStatusInclusive || st == 0) {
-                        double l = g.state[size_t(j) * 2 * kWave + lane];
-                        double e = g.state[size_t(j) * 2 * kWave + kWave + lane];
+                        double l = rec_load(g.state + size_t(j) * 2 * kWave + lane);
+                        double e = rec_load(g.state + size_t(j) * 2 * kWave + kWave + lane);
                         if (st == 0) { l = 1.0; e = 0.0; }  // gave up: outputs wrong, health set
                         apply(acc, l, e);
                         lam_in = l;
@@ -409,9 +433,11 @@ __global__ __launch_bounds__(W * kWave) void kla_scan_kernel(Args g) {
             if (has_next) {
                 double l = lam_in, e = eta_in;
                 apply(tile, l, e);
-                g.state[size_t(ticket) * 2 * kWave + lane] = l;
-                g.state[size_t(ticket) * 2 * kWave + kWave + lane] = e;
+                rec_store(g.state + size_t(ticket) * 2 * kWave + lane, l);
+                rec_store(g.state + size_t(ticket) * 2 * kWave + kWave + lane, e);
                 publish(&g.flags[ticket], lane, flag_word(tag, kStatusInclusive));
+            } else if (g.n_chunks > 1) {
+                publish(&g.flags[ticket], lane, flag_word(tag, kStatusFinished));
             }
             s_carry[0][lane] = lam_in;
             s_carry[1][lane] = eta_in;
@@ -457,16 +483,24 @@ __global__ __launch_bounds__(W * kWave) void kla_scan_kernel(Args g) {
         }
     }
 
-    // ---- the last workgroup to finish resets the header for the next call ----
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t done = __hip_atomic_fetch_add(&g.header[1], 1u, __ATOMIC_RELAXED,
+    // ---- advance the epoch once every workgroup has read it ----
+    // Every tile of a column group has read the epoch once the group's last
+    // tile has its carry-in (the look-back saw each earlier tile publish with
+    // this call's tag).  The last workgroup waits for all last-chunk tiles,
+    // then advances the epoch, so the next call's flags carry a new tag.
+    if (ticket == int64_t(gridDim.x) - 1 && g.n_chunks > 1 && w == 0) {
+        const int64_t first = (g.n_chunks - 1) * g.G;
+        for (int64_t k = first + lane; k < g.n_tiles; k += kWave) {
+            for (uint32_t spins = 1;; ++spins) {
+                const uint64_t v = __hip_atomic_load(&g.flags[k], __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
-        if (done == gridDim.x - 1) {
-            __hip_atomic_store(&g.header[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&g.header[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&g.header[2], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (v == flag_word(tag, kStatusFinished)) break;
+                if (give_up(spins, g.header)) break;
+                __builtin_amdgcn_s_sleep(1);
+            }
         }
+        if (lane == 0)
+            __hip_atomic_store(&g.header[2], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 

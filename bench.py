@@ -52,6 +52,77 @@ def load_traffic(workload_key: int):
     return rec.get("hbm_bytes_per_launch")
 
 
+def _counter_kib(path: str, counter: str, kernel_prefix: str):
+    """Mean per-dispatch value (KiB) of a rocprofv3 --pmc counter for kernels
+    whose name starts with kernel_prefix, and the number of dispatches."""
+    import csv
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+            if r["Counter_Name"] == counter and r["Kernel_Name"].startswith(kernel_prefix)]
+    if not vals:
+        raise SystemExit("no %s rows for %r in %s" % (counter, kernel_prefix, path))
+    return sum(vals) / len(vals), len(vals)
+
+
+def summarize_counters(args):
+    """Writes profiles/traffic_workload<k>.json and a markdown summary from
+    rocprofv3 outputs: the kernel-trace stats of the bench command, its
+    FETCH_SIZE and WRITE_SIZE runs, and the same two counters on a plain
+    device copy of known size (the scale factors)."""
+    import csv
+    from kla_inputs import WORKLOADS
+    w = WORKLOADS[args.workload]
+    scan = "void (anonymous namespace)::kla_scan_kernel"
+    stats = [r for r in csv.DictReader(open(args.trace)) if r["Name"].startswith(scan)]
+    if len(stats) != 1:
+        raise SystemExit("expected one scan kernel row in %s" % args.trace)
+    st = stats[0]
+    fetch, n_f = _counter_kib(args.fetch, "FETCH_SIZE", scan)
+    write, n_w = _counter_kib(args.write, "WRITE_SIZE", scan)
+    copy_bytes = args.copy_mib << 20
+    cf, _ = _counter_kib(args.copy_fetch, "FETCH_SIZE", "__amd_rocclr_copyBuffer")
+    cw, _ = _counter_kib(args.copy_write, "WRITE_SIZE", "__amd_rocclr_copyBuffer")
+    f_fetch = copy_bytes / (cf * 1024.0)
+    f_write = copy_bytes / (cw * 1024.0)
+    traffic = fetch * 1024.0 * f_fetch + write * 1024.0 * f_write
+    algo = w.elements * bytes_per_element(w.dtype)
+    avg_ns = float(st["AverageNs"])
+    rec = {"workload": w.describe(), "kernel": st["Name"], "kernel_sha256_16": kernel_hash(),
+           "hbm_bytes_per_launch": traffic, "algorithmic_bytes_per_launch": algo,
+           "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
+           "dispatches": [n_f, n_w], "copy_fetch_kib": cf, "copy_write_kib": cw,
+           "copy_bytes": copy_bytes, "fetch_scale": f_fetch, "write_scale": f_write,
+           "trace_calls": int(st["Calls"]), "trace_avg_ns": avg_ns,
+           "trace_min_ns": float(st["MinNs"]), "trace_max_ns": float(st["MaxNs"])}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "traffic_workload%d.json" % args.workload), "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    md = os.path.join(ROOT, "profiles", "kla_scan_kernel_%s.md" % w.name)
+    with open(md, "w") as f:
+        f.write("# kla_scan_kernel on %s\n\n" % w.describe())
+        f.write("Kernel: `%s`  (source sha256/16 `%s`)\n\n" % (st["Name"], kernel_hash()))
+        f.write("## Kernel trace (rocprofv3 --kernel-trace --stats)\n\n")
+        f.write("| calls | average ns | min ns | max ns |\n|---|---|---|---|\n")
+        f.write("| %s | %.0f | %s | %s |\n\n" % (st["Calls"], avg_ns, st["MinNs"], st["MaxNs"]))
+        f.write("Algorithmic bytes per launch: %d (%d elements x %d B); at the average "
+                "duration: %.0f GB/s = %.3f of 8 TB/s.\n\n"
+                % (algo, w.elements, bytes_per_element(w.dtype), algo / avg_ns,
+                   algo / avg_ns / HBM_PEAK_GBS))
+        f.write("## HBM counters (rocprofv3 --pmc, one counter per run)\n\n")
+        f.write("| counter | scan KiB/dispatch | plain copy of %d MiB, KiB | scale |\n"
+                "|---|---|---|---|\n" % args.copy_mib)
+        f.write("| FETCH_SIZE | %.0f | %.0f | %.3f |\n" % (fetch, cf, f_fetch))
+        f.write("| WRITE_SIZE | %.0f | %.0f | %.3f |\n\n" % (write, cw, f_write))
+        f.write("HBM traffic per launch = FETCH*scale + WRITE*scale = %.0f bytes = %.3f x "
+                "algorithmic.\n\n" % (traffic, traffic / algo))
+        f.write("## Commands\n\n```\n")
+        for line in args.commands:
+            f.write(line + "\n")
+        f.write("```\n")
+    print(md)
+    return 0
+
+
 def cpu_baseline(w, g_dev, budget_s: float = 12.0):
     """Times the float64 oracle on the host on a bounded sample of the
     workload (whole slabs, full T), scaled to elements per second."""
@@ -92,7 +163,19 @@ def main(argv=None):
                     help="0..4; the headline is 1 (small-LM layer)")
     ap.add_argument("--sets", type=int, default=2, help="input/output sets to rotate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the scan, run torch's plain device copy of MIB MiB "
+                         "(known bytes, to scale rocprofv3 FETCH_SIZE/WRITE_SIZE)")
+    ap.add_argument("--summarize-counters", action="store_true",
+                    help="write profiles/ summaries from rocprofv3 csv files (no GPU)")
+    ap.add_argument("--trace"), ap.add_argument("--fetch"), ap.add_argument("--write")
+    ap.add_argument("--copy-fetch"), ap.add_argument("--copy-write")
+    ap.add_argument("--copy-mib", type=int, default=1024)
+    ap.add_argument("--commands", nargs="*", default=[])
     args = ap.parse_args(argv)
+
+    if args.summarize_counters:
+        return summarize_counters(args)
 
     if args.gpus != 1:
         print("bench.py measures one GPU: the scan's channels are independent, so each "
@@ -101,6 +184,16 @@ def main(argv=None):
         return 2
 
     import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 18  # float32 elements in MIB MiB
+        src = torch.ones(n, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n * 4, "launches": max(1, args.steps)}))
+        return 0
 
     from kla_inputs import WORKLOADS, make_workload
     from linear_attention_sequence_kla_amd import get_workspace, scan_fwd, workspace_health

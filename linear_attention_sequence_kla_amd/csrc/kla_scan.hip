@@ -80,7 +80,7 @@ struct TileShape {
 };
 
 // Rows per wave and waves per workgroup of the launched kernels.
-constexpr TileShape kTile = {32, 4};
+constexpr TileShape kTile = {28, 4};
 
 struct Plan {
     int64_t C;          // channels B*H*D
@@ -133,8 +133,6 @@ struct Lift {
     double A, B, C, D, E, F, G;
 };
 
-__device__ inline Lift lift_identity() { return Lift{1.0, 0.0, 0.0, 1.0, 0.0, 1.0, 0.0}; }
-
 // Scales all entries by the power of two that brings the largest to [0.5, 1).
 __device__ inline void renorm(Lift& n) {
     const double m = fmax(fmax(fmax(fabs(n.A), fabs(n.B)), fmax(fabs(n.C), fabs(n.D))),
@@ -163,16 +161,38 @@ __device__ inline Lift compose(const Lift& l, const Lift& e) {
     return r;
 }
 
+// 1/z: the hardware float64 reciprocal refined by one Newton step (relative
+// error far below float32 resolution; no IEEE division sequence needed).
+__device__ inline double recip(double z) {
+    const double r = __builtin_amdgcn_rcp(z);
+    return fma(fma(-z, r, 1.0), r, r);
+}
+
 // (lam, eta) <- n(lam, eta).
 __device__ inline void apply(const Lift& n, double& lam, double& eta) {
     const double x = fma(n.A, lam, n.B);
     const double y = fma(n.E, lam, fma(n.F, eta, n.G));
-    const double z = fma(n.C, lam, n.D);
-    lam = x / z;
-    eta = y / z;
+    const double r = recip(fma(n.C, lam, n.D));
+    lam = x * r;
+    eta = y * r;
 }
 
 // Loads one gate from `base + off` (a byte offset) and widens it to float.
+// The chunk matrix of wave j of this workgroup, from LDS.
+__device__ inline Lift lds_lift(const double (*s)[7][kWave], int j, int lane) {
+    return Lift{s[j][0][lane], s[j][1][lane], s[j][2][lane], s[j][3][lane],
+                s[j][4][lane], s[j][5][lane], s[j][6][lane]};
+}
+
+// The workgroup's tile matrix: its W chunk matrices composed in time order.
+template <int W>
+__device__ inline Lift tile_lift(const double (*s)[7][kWave], int lane) {
+    Lift t = lds_lift(s, 0, lane);
+#pragma unroll 1
+    for (int j = 1; j < W; ++j) t = compose(lds_lift(s, j, lane), t);
+    return t;
+}
+
 template <typename In>
 __device__ inline float load_gate(const char* base, uint32_t off);
 
@@ -289,8 +309,7 @@ __device__ inline uint32_t wait_flag(uint64_t* flag, uint32_t tag, uint32_t* hea
 template <typename In, int L, int W>
 __global__ __launch_bounds__(W * kWave) void kla_scan_kernel(Args g) {
     __shared__ double s_lift[W][7][kWave];
-    __shared__ double s_carry[2][kWave];
-    __shared__ uint32_t s_tag;
+    __shared__ double s_carry[W][2][kWave];
 
     const int lane = threadIdx.x & (kWave - 1);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -299,10 +318,9 @@ __global__ __launch_bounds__(W * kWave) void kla_scan_kernel(Args g) {
     // workgroup id: every tile a workgroup waits for has a lower id, so it
     // was dispatched first and is running or finished.
     const int64_t ticket = blockIdx.x;
-    if (threadIdx.x == 0)
-        s_tag = __hip_atomic_load(&g.header[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-    __syncthreads();
-    const uint32_t tag = __builtin_amdgcn_readfirstlane(s_tag);
+    // This call's tag; only wave 0 (the look-back wave) needs it.  Its load
+    // is issued after the tile loads so that it costs no extra latency.
+    uint32_t tag = 0;
 
     if (ticket < g.n_tiles) {
         // ---- tile coordinates (wave-uniform) ----
@@ -350,6 +368,10 @@ __global__ __launch_bounds__(W * kWave) void kla_scan_kernel(Args g) {
             }
         }
 
+        if (w == 0)
+            tag = __builtin_amdgcn_readfirstlane(__hip_atomic_load(
+                      &g.header[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) + 1u;
+
         // ---- chunk matrix: the columns (A, E, C) and (B, G, D), and F ----
         Lift m;
         {
@@ -394,67 +416,55 @@ __global__ __launch_bounds__(W * kWave) void kla_scan_kernel(Args g) {
         // ---- tile carry (wave 0): publish, look back, publish ----
         if (w == 0) {
             const bool has_next = c + 1 < g.n_chunks;
-            Lift tile = m;
-#pragma unroll
-            for (int j = 1; j < W; ++j) {
-                const Lift n{s_lift[j][0][lane], s_lift[j][1][lane], s_lift[j][2][lane],
-                             s_lift[j][3][lane], s_lift[j][4][lane], s_lift[j][5][lane],
-                             s_lift[j][6][lane]};
-                tile = compose(n, tile);
-            }
-
             double lam_in = 1.0, eta_in = 0.0;
             if (c == 0) {
                 if (g.lam0) lam_in = g.lam0[qc];
                 if (g.eta0) eta_in = g.eta0[qc];
             } else {
                 if (has_next) {
-                    store_lift(g.matrix + size_t(ticket) * 7 * kWave, lane, tile);
+                    store_lift(g.matrix + size_t(ticket) * 7 * kWave, lane,
+                               tile_lift<W>(s_lift, lane));
                     publish(&g.flags[ticket], lane, flag_word(tag, kStatusAggregate));
                 }
-                // walk back over the tiles of the same column group
-                Lift acc = lift_identity();
+                // Walk back over the flags of this column group to the nearest
+                // tile with a published state, then apply the chunk matrices
+                // of the tiles after it, oldest first.  (Only one matrix is
+                // held at a time, which keeps the registers of the wait low.)
                 int64_t j = ticket - g.G;
-                while (true) {
-                    const uint32_t st = wait_flag(&g.flags[j], tag, g.header);
-                    if (st == kStatusInclusive || st == 0) {
-                        double l = rec_load(g.state + size_t(j) * 2 * kWave + lane);
-                        double e = rec_load(g.state + size_t(j) * 2 * kWave + kWave + lane);
-                        if (st == 0) { l = 1.0; e = 0.0; }  // gave up: outputs wrong, health set
-                        apply(acc, l, e);
-                        lam_in = l;
-                        eta_in = e;
-                        break;
-                    }
-                    acc = compose(acc, load_lift(g.matrix + size_t(j) * 7 * kWave, lane));
-                    j -= g.G;
-                }
+                uint32_t st;
+                while ((st = wait_flag(&g.flags[j], tag, g.header)) == kStatusAggregate) j -= g.G;
+                if (st == kStatusInclusive) {
+                    lam_in = rec_load(g.state + size_t(j) * 2 * kWave + lane);
+                    eta_in = rec_load(g.state + size_t(j) * 2 * kWave + kWave + lane);
+                    for (int64_t k = j + g.G; k < ticket; k += g.G)
+                        apply(load_lift(g.matrix + size_t(k) * 7 * kWave, lane), lam_in, eta_in);
+                }  // else the wait gave up: the health word is set, outputs are wrong
             }
             if (has_next) {
                 double l = lam_in, e = eta_in;
-                apply(tile, l, e);
+                apply(tile_lift<W>(s_lift, lane), l, e);
                 rec_store(g.state + size_t(ticket) * 2 * kWave + lane, l);
                 rec_store(g.state + size_t(ticket) * 2 * kWave + kWave + lane, e);
                 publish(&g.flags[ticket], lane, flag_word(tag, kStatusInclusive));
             } else if (g.n_chunks > 1) {
                 publish(&g.flags[ticket], lane, flag_word(tag, kStatusFinished));
             }
-            s_carry[0][lane] = lam_in;
-            s_carry[1][lane] = eta_in;
+            // carry-in of every wave: the tile's, then through the earlier
+            // waves' chunk matrices (one matrix live at a time)
+            s_carry[0][0][lane] = lam_in;
+            s_carry[0][1][lane] = eta_in;
+#pragma unroll 1
+            for (int j = 0; j + 1 < W; ++j) {
+                apply(lds_lift(s_lift, j, lane), lam_in, eta_in);
+                s_carry[j + 1][0][lane] = lam_in;
+                s_carry[j + 1][1][lane] = eta_in;
+            }
         }
         __syncthreads();
 
         // ---- replay the wave's rows from its own carry-in ----
         if (nr > 0) {
-            double lam_in = s_carry[0][lane];
-            double eta_in = s_carry[1][lane];
-            for (int j = 0; j < w; ++j) {
-                const Lift n{s_lift[j][0][lane], s_lift[j][1][lane], s_lift[j][2][lane],
-                             s_lift[j][3][lane], s_lift[j][4][lane], s_lift[j][5][lane],
-                             s_lift[j][6][lane]};
-                apply(n, lam_in, eta_in);
-            }
-            double X = lam_in, Y = eta_in, Z = 1.0;
+            double X = s_carry[w][0][lane], Y = s_carry[w][1][lane], Z = 1.0;
             char* olam = reinterpret_cast<char*>(g.lam) + e0 * int64_t(sizeof(float));
             char* oeta = reinterpret_cast<char*>(g.eta) + e0 * int64_t(sizeof(float));
 #pragma unroll
@@ -465,8 +475,7 @@ __global__ __launch_bounds__(W * kWave) void kla_scan_kernel(Args g) {
                 X = fma(ph, zn, X);
                 Y = fma(bb, zn, a * Y);
                 Z = zn;
-                double r = __builtin_amdgcn_rcp(Z);
-                r = fma(fma(-Z, r, 1.0), r, r);
+                const double r = recip(Z);
                 if (valid) {
                     const uint32_t off = lane_el * uint32_t(sizeof(float)) + uint32_t(i) * out_row;
                     __builtin_nontemporal_store(float(X * r), reinterpret_cast<float*>(olam + off));

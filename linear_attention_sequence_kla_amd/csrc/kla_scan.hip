@@ -469,7 +469,7 @@ __global__ __launch_bounds__(W * kWave) void kla_scan_kernel(Args g) {
             char* oeta = reinterpret_cast<char*>(g.eta) + e0 * int64_t(sizeof(float));
 #pragma unroll
             for (int i = 0; i < L; ++i) {
-                if (i >= nr) break;
+                if (i >= nr) continue;  // (uniform; keeps the loop fully unrolled)
                 const double a = ra[i], p = rp[i], ph = rf[i], bb = rb[i];
                 const double zn = fma(p, X, (a * a) * Z);
                 X = fma(ph, zn, X);

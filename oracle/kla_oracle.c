@@ -1,6 +1,7 @@
 /*
  * kla_oracle.c -- CPU float64 oracle for the Kalman Linear Attention (KLA)
- * scan forward pass.  TEST INFRASTRUCTURE ONLY: the tests, the smoke check
+ * scan: the forward pass and its backward pass (gradients, further below).
+ * TEST INFRASTRUCTURE ONLY: the tests, the smoke check
  * and the benchmark's CPU-baseline leg may call it; the product path never
  * does, and this file shares no code with the HIP library.
  *
@@ -41,6 +42,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #ifdef _OPENMP
 #include <omp.h>
@@ -134,4 +136,161 @@ int kla_oracle_threads(int nthreads)
     (void)nthreads;
     return 1;
 #endif
+}
+
+/*
+ * Backward pass (vector-Jacobian product) of the scan, per channel.
+ *
+ * Given upstream gradients g_lam[t], g_eta[t] of a scalar loss with respect
+ * to the outputs lam_t, eta_t, returns the gradients with respect to every
+ * input: a_t, p_t, phi_t, b_t, lam0, eta0.  This is reverse-mode
+ * differentiation of the information-form step of the Pith review
+ * ("Circularity check", Theorems 1 and 2):
+ *
+ *     d_t   = a_t^2 + p_t lam_{t-1}
+ *     lam_t = lam_{t-1} / d_t + phi_t
+ *     eta_t = (a_t / d_t) eta_{t-1} + b_t
+ *
+ * whose partial derivatives are
+ *     dlam_t/dlam_{t-1} = a^2 / d^2        deta_t/dlam_{t-1} = -a p eta_{t-1} / d^2
+ *     deta_t/deta_{t-1} = a / d            dlam_t/dphi_t = 1, deta_t/db_t = 1
+ *     dlam_t/da_t = -2 a lam_{t-1} / d^2   deta_t/da_t = eta_{t-1} (p lam_{t-1} - a^2) / d^2
+ *     dlam_t/dp_t = -lam_{t-1}^2 / d^2     deta_t/dp_t = -a lam_{t-1} eta_{t-1} / d^2
+ * The states lam_t, eta_t come from the same covariance-form filter as the
+ * forward oracle.  Walking t from T down to 1, the total adjoints are
+ *     Lam_t = g_lam[t] + dlam_{t+1}/dlam_t Lam_{t+1} + deta_{t+1}/dlam_t Eta_{t+1}
+ *     Eta_t = g_eta[t] + deta_{t+1}/deta_t Eta_{t+1}
+ * and g_phi = Lam, g_b = Eta, g_a = Lam dlam/da + Eta deta/da, etc.;
+ * g_lam0, g_eta0 are the adjoints carried past the first token.
+ *
+ * m_* are cancellation-free magnitudes of the same sums (every term taken
+ * with its absolute value, |eta| replaced by eta_abs of the forward pass and
+ * p lam - a^2 by p lam + a^2), used by the parity metric.
+ */
+static void kalman_channel_bwd(const double *a, const double *p, const double *phi,
+                               const double *b, double lam0, double eta0,
+                               const double *g_lam, const double *g_eta,
+                               double *g_a, double *g_p, double *g_phi, double *g_b,
+                               double *g_lam0, double *g_eta0,
+                               double *m_a, double *m_p, double *m_phi, double *m_b,
+                               double *m_lam0, double *m_eta0,
+                               int64_t T, int64_t stride, double *work)
+{
+    /* forward states, index 0 = before the first token */
+    double *LAM = work, *ETA = work + (T + 1), *ETA_ABS = work + 2 * (T + 1);
+    double P = 1.0 / lam0;
+    double mu = eta0 / lam0;
+    LAM[0] = lam0;
+    ETA[0] = eta0;
+    ETA_ABS[0] = fabs(eta0);
+    for (int64_t t = 1; t <= T; ++t) {
+        const int64_t i = (t - 1) * stride;
+        const double at = a[i];
+        const double Ppred = at * at * P + p[i];
+        const double mupred = at * mu;
+        const double f = at * P / Ppred;
+        const double S = 1.0 + phi[i] * Ppred;
+        mu = (mupred + Ppred * b[i]) / S;
+        P = Ppred / S;
+        LAM[t] = 1.0 / P;
+        ETA[t] = mu / P;
+        ETA_ABS[t] = f * ETA_ABS[t - 1] + fabs(b[i]);
+    }
+
+    /* reverse sweep; (cl, ce) = adjoint contributions from the tokens after t */
+    double cl = 0.0, ce = 0.0, ml = 0.0, me = 0.0;
+    for (int64_t t = T; t >= 1; --t) {
+        const int64_t i = (t - 1) * stride;
+        const double at = a[i];
+        const double pt = p[i];
+        const double lp = LAM[t - 1];
+        const double ep = ETA[t - 1];
+        const double eap = ETA_ABS[t - 1];
+        const double d = at * at + pt * lp;
+        const double d2 = d * d;
+
+        const double Lam = g_lam[i] + cl;
+        const double Eta = g_eta[i] + ce;
+        const double MLam = fabs(g_lam[i]) + ml;
+        const double MEta = fabs(g_eta[i]) + me;
+
+        const double dl_dlp = at * at / d2;
+        const double de_dlp = -at * pt * ep / d2;
+        const double de_dep = at / d;
+        const double dl_da = -2.0 * at * lp / d2;
+        const double de_da = ep * (pt * lp - at * at) / d2;
+        const double dl_dp = -lp * lp / d2;
+        const double de_dp = -at * lp * ep / d2;
+
+        g_phi[i] = Lam;
+        g_b[i] = Eta;
+        g_a[i] = Lam * dl_da + Eta * de_da;
+        g_p[i] = Lam * dl_dp + Eta * de_dp;
+
+        m_phi[i] = MLam;
+        m_b[i] = MEta;
+        m_a[i] = MLam * fabs(dl_da) + MEta * eap * (pt * lp + at * at) / d2;
+        m_p[i] = MLam * lp * lp / d2 + MEta * at * lp * eap / d2;
+
+        cl = dl_dlp * Lam + de_dlp * Eta;
+        ce = de_dep * Eta;
+        ml = dl_dlp * MLam + at * pt * eap / d2 * MEta;
+        me = de_dep * MEta;
+    }
+    *g_lam0 = cl;
+    *g_eta0 = ce;
+    *m_lam0 = ml;
+    *m_eta0 = me;
+}
+
+/*
+ * Backward oracle over a contiguous [B, H, T, D] problem.  Inputs as for
+ * kla_oracle_scan plus g_lam, g_eta [B,H,T,D].  Outputs g_a, g_p, g_phi, g_b,
+ * m_a, m_p, m_phi, m_b [B,H,T,D] and g_lam0, g_eta0, m_lam0, m_eta0 [B,H,D].
+ * Returns 0, -1 on a bad size, -2 if scratch memory could not be allocated.
+ */
+int kla_oracle_scan_bwd(const double *a, const double *p, const double *phi,
+                        const double *b, const double *lam0, const double *eta0,
+                        const double *g_lam, const double *g_eta,
+                        double *g_a, double *g_p, double *g_phi, double *g_b,
+                        double *g_lam0, double *g_eta0,
+                        double *m_a, double *m_p, double *m_phi, double *m_b,
+                        double *m_lam0, double *m_eta0,
+                        int64_t B, int64_t H, int64_t T, int64_t D, int nthreads)
+{
+    if (B < 0 || H < 0 || T < 0 || D < 0)
+        return -1;
+    const int64_t channels = B * H * D;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+
+#pragma omp parallel
+    {
+        double *work = (double *)malloc(sizeof(double) * 3 * (size_t)(T + 1));
+        if (!work) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t c = 0; c < channels; ++c) {
+            if (!work)
+                continue;
+            const int64_t slab = c / D;
+            const int64_t d = c % D;
+            const int64_t base = slab * T * D + d;
+            kalman_channel_bwd(a + base, p + base, phi + base, b + base, lam0[c], eta0[c],
+                               g_lam + base, g_eta + base,
+                               g_a + base, g_p + base, g_phi + base, g_b + base,
+                               g_lam0 + c, g_eta0 + c,
+                               m_a + base, m_p + base, m_phi + base, m_b + base,
+                               m_lam0 + c, m_eta0 + c, T, D, work);
+        }
+        free(work);
+    }
+    return failed ? -2 : 0;
 }

@@ -42,6 +42,8 @@ class OracleLibrary:
         dp = ctypes.POINTER(ctypes.c_double)
         lib.kla_oracle_scan.argtypes = [dp] * 9 + [ctypes.c_int64] * 4 + [ctypes.c_int]
         lib.kla_oracle_scan.restype = ctypes.c_int
+        lib.kla_oracle_scan_bwd.argtypes = [dp] * 20 + [ctypes.c_int64] * 4 + [ctypes.c_int]
+        lib.kla_oracle_scan_bwd.restype = ctypes.c_int
         lib.kla_oracle_threads.argtypes = [ctypes.c_int]
         lib.kla_oracle_threads.restype = ctypes.c_int
         self._lib = lib
@@ -72,6 +74,39 @@ class OracleLibrary:
         if rc != 0:
             raise ValueError("oracle rejected the sizes")
         return lam, eta, eta_abs
+
+    def scan_bwd(self, a, p, phi, b, lam0, eta0, g_lam, g_eta, nthreads: int | None = None):
+        """Runs the float64 backward pass (vector-Jacobian product).
+
+        Gates and upstream gradients g_lam, g_eta: [B, H, T, D]; lam0, eta0:
+        [B, H, D] (None: 1 and 0).  Returns (grads, mags): two dicts with keys
+        a, p, phi, b ([B, H, T, D]) and lam0, eta0 ([B, H, D]); grads are the
+        gradients of sum(g_lam * lam + g_eta * eta) with respect to each
+        input, mags their cancellation-free magnitudes.
+        """
+        a = _as_f64(a)
+        if a.ndim != 4:
+            raise ValueError("gates must be [B, H, T, D]")
+        B, H, T, D = a.shape
+        shape = (B, H, T, D)
+        p, phi, b, g_lam, g_eta = (_as_f64(x, shape) for x in (p, phi, b, g_lam, g_eta))
+        lam0 = _as_f64(np.ones((B, H, D)) if lam0 is None else lam0, (B, H, D))
+        eta0 = _as_f64(np.zeros((B, H, D)) if eta0 is None else eta0, (B, H, D))
+        names = ("a", "p", "phi", "b")
+        grads = {k: np.empty(shape) for k in names}
+        mags = {k: np.empty(shape) for k in names}
+        for k in ("lam0", "eta0"):
+            grads[k] = np.empty((B, H, D))
+            mags[k] = np.empty((B, H, D))
+        rc = self._lib.kla_oracle_scan_bwd(
+            _ptr(a), _ptr(p), _ptr(phi), _ptr(b), _ptr(lam0), _ptr(eta0),
+            _ptr(g_lam), _ptr(g_eta),
+            *(_ptr(grads[k]) for k in names), _ptr(grads["lam0"]), _ptr(grads["eta0"]),
+            *(_ptr(mags[k]) for k in names), _ptr(mags["lam0"]), _ptr(mags["eta0"]),
+            B, H, T, D, int(nthreads or 0))
+        if rc != 0:
+            raise ValueError("backward oracle failed (%d)" % rc)
+        return grads, mags
 
 
 def _as_f64(x, shape=None):
@@ -111,3 +146,8 @@ def oracle_threads(nthreads: int | None = None) -> int:
 def oracle_scan(a, p, phi, b, lam0=None, eta0=None, nthreads: int | None = None):
     """The float64 oracle; see ``OracleLibrary.scan``."""
     return _library().scan(a, p, phi, b, lam0, eta0, nthreads)
+
+
+def oracle_scan_bwd(a, p, phi, b, lam0, eta0, g_lam, g_eta, nthreads: int | None = None):
+    """The float64 backward oracle; see ``OracleLibrary.scan_bwd``."""
+    return _library().scan_bwd(a, p, phi, b, lam0, eta0, g_lam, g_eta, nthreads)

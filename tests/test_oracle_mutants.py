@@ -48,3 +48,53 @@ def test_mutant_is_caught(name, tmp_path):
         except (AssertionError, FloatingPointError, ValueError, ZeroDivisionError) as e:
             caught.append((pin.__name__, str(e)[:80]))
     assert caught, "no pin caught mutant %s" % name
+
+
+import oracle_bwd_pins  # noqa: E402
+
+BWD_MUTANTS = {
+    "bwd-dropped-square-in-lambda-chain": ("const double dl_dlp = at * at / d2;",
+                                           "const double dl_dlp = at / d2;"),
+    "bwd-wrong-sign-of-coupling": ("const double de_dlp = -at * pt * ep / d2;",
+                                   "const double de_dlp = at * pt * ep / d2;"),
+    "bwd-state-one-token-late": ("const double lp = LAM[t - 1];", "const double lp = LAM[t];"),
+    "bwd-eta-carry-without-gate": ("ce = de_dep * Eta;", "ce = Eta;"),
+    "bwd-decay-grad-missing-eta-term": ("g_a[i] = Lam * dl_da + Eta * de_da;",
+                                        "g_a[i] = Lam * dl_da;"),
+    "bwd-lambda-carry-missing-coupling": ("cl = dl_dlp * Lam + de_dlp * Eta;",
+                                          "cl = dl_dlp * Lam;"),
+    "bwd-wrong-sign-in-decay-derivative": ("ep * (pt * lp - at * at) / d2",
+                                           "ep * (pt * lp + at * at) / d2"),
+    "bwd-noise-derivative-missing-square": ("const double dl_dp = -lp * lp / d2;",
+                                            "const double dl_dp = -lp / d2;"),
+    "bwd-upstream-ignored-in-total": ("const double Lam = g_lam[i] + cl;",
+                                      "const double Lam = cl;"),
+    "bwd-magnitude-missing-term": (
+        "m_a[i] = MLam * fabs(dl_da) + MEta * eap * (pt * lp + at * at) / d2;",
+        "m_a[i] = MLam * fabs(dl_da);"),
+    "bwd-initial-gradient-from-magnitude": ("*g_lam0 = cl;", "*g_lam0 = ml;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_bwd_mutant_is_caught(name, tmp_path):
+    old, new = BWD_MUTANTS[name]
+    src = open(SOURCE).read()
+    assert src.count(old) == 1, "mutation site not unique: %r" % old
+    mutant_src = tmp_path / "mutant.c"
+    mutant_src.write_text(src.replace(old, new, 1))
+    lib = OracleLibrary(build_oracle(str(tmp_path / "libmutant.so"), str(mutant_src)))
+
+    def scan(a, p, phi, b, lam0, eta0):
+        return lib.scan(a, p, phi, b, lam0, eta0)
+
+    def scan_bwd(a, p, phi, b, lam0, eta0, g_lam, g_eta):
+        return lib.scan_bwd(a, p, phi, b, lam0, eta0, g_lam, g_eta)
+
+    caught = []
+    for pin in oracle_bwd_pins.ALL_BWD_PINS:
+        try:
+            pin(scan_bwd, scan)
+        except (AssertionError, FloatingPointError, ValueError, ZeroDivisionError) as e:
+            caught.append((pin.__name__, str(e)[:80]))
+    assert caught, "no pin caught mutant %s" % name

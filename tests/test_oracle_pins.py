@@ -56,3 +56,12 @@ def test_regression_fixture():
     lam_i, eta_i = oracle_pins.info_form(*g, lam0, eta0)
     np.testing.assert_allclose(lam_i.reshape(T, D), fx["lam"], rtol=1e-13)
     np.testing.assert_allclose(eta_i.reshape(T, D), fx["eta"], rtol=1e-13, atol=1e-12)
+
+
+import oracle_bwd_pins  # noqa: E402
+from oracle import oracle_scan_bwd  # noqa: E402
+
+
+@pytest.mark.parametrize("pin", oracle_bwd_pins.ALL_BWD_PINS, ids=lambda f: f.__name__)
+def test_bwd_pin(pin):
+    pin(oracle_scan_bwd, scan)

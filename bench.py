@@ -26,28 +26,44 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
-KERNEL_SOURCE = os.path.join(ROOT, "linear_attention_sequence_kla_amd", "csrc", "kla_scan.hip")
+CSRC = os.path.join(ROOT, "linear_attention_sequence_kla_amd", "csrc")
+KERNEL_SOURCES = {"fwd": ("kla_scan_fwd.hip", "kla_lookback.h", "kla_internal.h"),
+                  "bwd": ("kla_scan_bwd.hip", "kla_lookback.h", "kla_internal.h")}
+KERNEL_NAMES = {"fwd": "kla_scan_kernel", "bwd": "kla_scan_bwd_kernel"}
 
 
-def kernel_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_hash(direction: str = "fwd") -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[direction]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def bytes_per_element(dtype: str) -> int:
-    return 4 * (4 if dtype == "f32" else 2) + 2 * 4
+def bytes_per_element(dtype: str, direction: str = "fwd") -> int:
+    """Algorithmic HBM bytes per scanned element.  Forward: 4 gate reads and
+    2 float32 writes.  Backward: reads a, p, the saved lam, eta and the
+    upstream g_lam, g_eta; writes 4 float32 gradients."""
+    gate = 4 if dtype == "f32" else 2
+    if direction == "fwd":
+        return 4 * gate + 2 * 4
+    return 2 * gate + 4 * 4 + 4 * 4
 
 
-def load_traffic(workload_key: int):
+def traffic_path(workload_key: int, direction: str) -> str:
+    suffix = "" if direction == "fwd" else "_bwd"
+    return os.path.join(ROOT, "profiles", "traffic_workload%d%s.json" % (workload_key, suffix))
+
+
+def load_traffic(workload_key: int, direction: str = "fwd"):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when the kernel source changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "traffic_workload%d.json" % workload_key)
     try:
-        with open(path) as f:
+        with open(traffic_path(workload_key, direction)) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_sha256_16") != kernel_hash():
+    if rec.get("kernel_sha256_16") != kernel_hash(direction):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -71,7 +87,8 @@ def summarize_counters(args):
     import csv
     from kla_inputs import WORKLOADS
     w = WORKLOADS[args.workload]
-    scan = "void (anonymous namespace)::kla_scan_kernel"
+    d = args.direction
+    scan = "void kla::(anonymous namespace)::%s<" % KERNEL_NAMES[d]
     stats = [r for r in csv.DictReader(open(args.trace)) if r["Name"].startswith(scan)]
     if len(stats) != 1:
         raise SystemExit("expected one scan kernel row in %s" % args.trace)
@@ -84,9 +101,9 @@ def summarize_counters(args):
     f_fetch = copy_bytes / (cf * 1024.0)
     f_write = copy_bytes / (cw * 1024.0)
     traffic = fetch * 1024.0 * f_fetch + write * 1024.0 * f_write
-    algo = w.elements * bytes_per_element(w.dtype)
+    algo = w.elements * bytes_per_element(w.dtype, d)
     avg_ns = float(st["AverageNs"])
-    rec = {"workload": w.describe(), "kernel": st["Name"], "kernel_sha256_16": kernel_hash(),
+    rec = {"workload": w.describe(), "kernel": st["Name"], "kernel_sha256_16": kernel_hash(d),
            "hbm_bytes_per_launch": traffic, "algorithmic_bytes_per_launch": algo,
            "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
            "dispatches": [n_f, n_w], "copy_fetch_kib": cf, "copy_write_kib": cw,
@@ -94,19 +111,19 @@ def summarize_counters(args):
            "trace_calls": int(st["Calls"]), "trace_avg_ns": avg_ns,
            "trace_min_ns": float(st["MinNs"]), "trace_max_ns": float(st["MaxNs"])}
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    with open(os.path.join(ROOT, "profiles", "traffic_workload%d.json" % args.workload), "w") as f:
+    with open(traffic_path(args.workload, d), "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
-    md = os.path.join(ROOT, "profiles", "kla_scan_kernel_%s.md" % w.name)
+    md = os.path.join(ROOT, "profiles", "%s_%s.md" % (KERNEL_NAMES[d], w.name))
     with open(md, "w") as f:
-        f.write("# kla_scan_kernel on %s\n\n" % w.describe())
-        f.write("Kernel: `%s`  (source sha256/16 `%s`)\n\n" % (st["Name"], kernel_hash()))
+        f.write("# %s on %s\n\n" % (KERNEL_NAMES[d], w.describe()))
+        f.write("Kernel: `%s`  (source sha256/16 `%s`)\n\n" % (st["Name"], kernel_hash(d)))
         f.write("## Kernel trace (rocprofv3 --kernel-trace --stats)\n\n")
         f.write("| calls | average ns | min ns | max ns |\n|---|---|---|---|\n")
         f.write("| %s | %.0f | %s | %s |\n\n" % (st["Calls"], avg_ns, st["MinNs"], st["MaxNs"]))
         f.write("Algorithmic bytes per launch: %d (%d elements x %d B); at the average "
                 "duration: %.0f GB/s = %.3f of 8 TB/s.\n\n"
-                % (algo, w.elements, bytes_per_element(w.dtype), algo / avg_ns,
+                % (algo, w.elements, bytes_per_element(w.dtype, d), algo / avg_ns,
                    algo / avg_ns / HBM_PEAK_GBS))
         f.write("## HBM counters (rocprofv3 --pmc, one counter per run)\n\n")
         f.write("| counter | scan KiB/dispatch | plain copy of %d MiB, KiB | scale |\n"
@@ -162,6 +179,8 @@ def main(argv=None):
     ap.add_argument("--workload", type=int, default=1,
                     help="0..4; the headline is 1 (small-LM layer)")
     ap.add_argument("--sets", type=int, default=2, help="input/output sets to rotate")
+    ap.add_argument("--direction", choices=("fwd", "bwd"), default="fwd",
+                    help="fwd: kla_scan_fwd (the headline); bwd: kla_scan_bwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the scan, run torch's plain device copy of MIB MiB "
@@ -185,6 +204,7 @@ def main(argv=None):
 
     import torch
 
+    TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
     if args.copy_calibration:
         n = args.copy_calibration << 18  # float32 elements in MIB MiB
         src = torch.ones(n, device="cuda:0")
@@ -196,23 +216,38 @@ def main(argv=None):
         return 0
 
     from kla_inputs import WORKLOADS, make_workload
-    from linear_attention_sequence_kla_amd import get_workspace, scan_fwd, workspace_health
+    from linear_attention_sequence_kla_amd import (
+        bwd_workspace_size, get_workspace, scan_bwd, scan_fwd, workspace_health, workspace_size)
 
     w = WORKLOADS[args.workload]
+    d = args.direction
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    get_workspace(max(workspace_size(*w.shape, TORCH_DTYPE[w.dtype]),
+                      bwd_workspace_size(*w.shape, TORCH_DTYPE[w.dtype])), dev, stream)
     sets = []
     for k in range(args.sets):
         g = make_workload(args.workload, device=dev, seed=w.seed + 1000 * k)
         lam = torch.empty(w.shape, dtype=torch.float32, device=dev)
         eta = torch.empty(w.shape, dtype=torch.float32, device=dev)
+        if d == "bwd":
+            # the forward outputs are the saved states; upstream gradients ~ N(0, 1)
+            scan_fwd(g["a"], g["p"], g["phi"], g["b"], g["lam0"], g["eta0"], out=(lam, eta))
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(w.seed + 77 + k)
+            g["g_lam"] = torch.randn(w.shape, generator=gen, device=dev)
+            g["g_eta"] = torch.randn(w.shape, generator=gen, device=dev)
         sets.append((g, (lam, eta)))
     torch.cuda.synchronize(dev)
-    stream = torch.cuda.current_stream(dev)
 
     def step(i):
         g, out = sets[i % len(sets)]
-        scan_fwd(g["a"], g["p"], g["phi"], g["b"], g["lam0"], g["eta0"], out=out)
+        if d == "fwd":
+            scan_fwd(g["a"], g["p"], g["phi"], g["b"], g["lam0"], g["eta0"], out=out)
+        else:
+            scan_bwd(g["a"], g["p"], out[0], out[1], g["g_lam"], g["g_eta"], g["lam0"],
+                     g["eta0"])
 
     for i in range(args.warmup):
         step(i)
@@ -236,9 +271,9 @@ def main(argv=None):
     n = w.elements
     ms_step = wall * 1e3 / args.steps
     k_avg = sum(kernel_ms) / len(kernel_ms)
-    bpe = bytes_per_element(w.dtype)
+    bpe = bytes_per_element(w.dtype, d)
     achieved = n * bpe / (k_avg * 1e-3) / 1e9
-    traffic = load_traffic(args.workload)
+    traffic = load_traffic(args.workload, d)
     rec = {
         "metric": "KLA scan elements (B*H*T*D)/s and achieved HBM GB/s vs peak, 1 MI355X",
         "value": n / (ms_step * 1e-3),
@@ -253,14 +288,17 @@ def main(argv=None):
         "dtype": "f64",
         "data": "synthetic",
         "config": {"workload": w.describe(), "B": w.B, "H": w.H, "T": w.T, "D": w.D,
-                   "io_dtype": w.dtype, "elements": n, "parallelism": "single GPU"},
+                   "io_dtype": w.dtype, "elements": n, "parallelism": "single GPU",
+                   "direction": d},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "kla_scan_kernel", "kernel_ms_avg": k_avg,
+                     "kernel": KERNEL_NAMES[d], "kernel_ms_avg": k_avg,
                      "kernel_ms_min": min(kernel_ms), "bytes_per_element": bpe},
         "health": health,
     }
-    if not args.no_cpu_baseline:
+    if d == "bwd":
+        rec["metric"] = "KLA backward scan elements (B*H*T*D)/s and achieved HBM GB/s vs peak"
+    if not args.no_cpu_baseline and d == "fwd":
         rec["cpu_baseline"] = cpu_baseline(w, sets[0][0])
     print(json.dumps(rec), flush=True)
     return 0

@@ -103,6 +103,53 @@ KLA_API kla_status kla_scan_fwd(const void *a, const void *p, const void *phi,
                         void *stream);
 
 /*
+ * Bytes of device workspace kla_scan_bwd needs (0 for invalid sizes or an
+ * empty problem).  A workspace large enough for both directions may serve
+ * forward and backward calls alternately.
+ */
+KLA_API size_t kla_scan_bwd_workspace_size(int64_t B, int64_t H, int64_t T, int64_t D,
+                                           kla_dtype in_dtype);
+
+/*
+ * Backward KLA scan: the vector-Jacobian product of kla_scan_fwd.
+ *
+ * Reverse-mode differentiation of the forward step (Pith review of arXiv
+ * 2602.10743, "Circularity check", Theorems 1 and 2).  With
+ * d_t = a_t^2 + p_t lam_{t-1} and upstream gradients g_lam, g_eta of a scalar
+ * loss with respect to the outputs lam, eta, it returns the loss gradients
+ * with respect to every input:
+ *     g_phi[t] = Lam_t,  g_b[t] = Eta_t   (total adjoints of lam_t, eta_t)
+ *     g_a[t] = Lam_t (-2 a lam_{t-1}) / d^2 + Eta_t eta_{t-1} (p lam_{t-1} - a^2) / d^2
+ *     g_p[t] = -lam_{t-1} (Lam_t lam_{t-1} + Eta_t a eta_{t-1}) / d^2
+ *     Lam_{t-1} = g_lam[t-1] + (a/d)^2 Lam_t - p (a/d) eta_{t-1} / d Eta_t,
+ *     Eta_{t-1} = g_eta[t-1] + (a/d) Eta_t,
+ * and g_lam0, g_eta0 are the adjoints carried past the first token.  It runs
+ * as the same single-pass scan as the forward call, from the end of the
+ * sequence.
+ *
+ *   a, p          the forward call's gates, [B,H,T,D] of in_dtype (phi and b
+ *                 are not needed).
+ *   lam0, eta0    the forward call's initial state ([B,H,D] float32 or NULL).
+ *   lam, eta      the forward call's outputs, [B,H,T,D] float32: they are the
+ *                 states lam_{t-1}, eta_{t-1} of the derivatives, so they must
+ *                 be finite (where the forward outputs overflowed float32 the
+ *                 gradients are unspecified).
+ *   g_lam, g_eta  upstream gradients, [B,H,T,D] float32; NULL means zero.
+ *   g_a, g_p, g_phi, g_b   outputs, [B,H,T,D] float32 (also for bf16 gates).
+ *   g_lam0, g_eta0         outputs, [B,H,D] float32; either may be NULL.
+ *   workspace, stream      as for kla_scan_fwd (same zero-once contract).
+ * Outputs must not overlap any other argument.  Errors as for kla_scan_fwd.
+ */
+KLA_API kla_status kla_scan_bwd(const void *a, const void *p, kla_dtype in_dtype,
+                                const float *lam0, const float *eta0,
+                                const float *lam, const float *eta,
+                                const float *g_lam, const float *g_eta,
+                                float *g_a, float *g_p, float *g_phi, float *g_b,
+                                float *g_lam0, float *g_eta0,
+                                int64_t B, int64_t H, int64_t T, int64_t D,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Reads the workspace's health word after the calls that used it have
  * completed (it synchronizes `stream`).  *flags_out is 0 when every call so
  * far ran normally; bit 0 is set if a chunk gave up waiting for the carry of

@@ -1,0 +1,303 @@
+// kla_api.cpp -- the C ABI of libkla (include/kla.h): argument validation,
+// tiling plans, workspace sizing and kernel dispatch.  Every argument error is
+// reported before anything is enqueued.
+
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "kla.h"
+#include "kla_internal.h"
+
+namespace kla {
+
+namespace {
+
+bool mul_ok(int64_t x, int64_t y, int64_t* out) {
+    if (x < 0 || y < 0) return false;
+    if (x != 0 && y > INT64_MAX / x) return false;
+    *out = x * y;
+    return true;
+}
+
+}  // namespace
+
+bool make_plan(int64_t B, int64_t H, int64_t T, int64_t D, int rows_per_wave, int waves,
+               int matrix_words, int state_words, Plan* pl) {
+    int64_t BH, C, N;
+    if (!mul_ok(B, H, &BH) || !mul_ok(BH, D, &C) || !mul_ok(C, T, &N)) return false;
+    if (N > INT64_MAX / 16) return false;  // byte offsets of every tensor fit
+    const int64_t R = int64_t(rows_per_wave) * waves;
+    pl->C = C;
+    pl->N = N;
+    pl->G = (C + kWave - 1) / kWave;
+    pl->n_chunks = (T + R - 1) / R;
+    if (!mul_ok(pl->G, pl->n_chunks, &pl->n_tiles)) return false;
+    if (pl->n_tiles > int64_t(INT32_MAX)) return false;
+    // Each wave addresses its rows with 32-bit byte offsets from one base: the
+    // 64 channels of a column group span at most ceil((D + 62) / D) slabs of
+    // T*D elements, plus one row before and the wave's own rows.
+    int64_t span_el = 0;
+    if (D > 0) span_el = ((D + 62) / D) * T * D + 2 * D + int64_t(rows_per_wave) * D;
+    pl->offsets_fit = span_el < (int64_t(1) << 30);
+    pl->ws = workspace_layout(size_t(pl->n_tiles), matrix_words, state_words);
+    return true;
+}
+
+}  // namespace kla
+
+namespace {
+
+using kla::Plan;
+
+thread_local char t_detail[512];
+
+kla_status fail(kla_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+kla_status fail(kla_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(t_detail, sizeof(t_detail), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+bool overlaps(const void* x, size_t nx, const void* y, size_t ny) {
+    if (!x || !y || nx == 0 || ny == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(x), b0 = reinterpret_cast<uintptr_t>(y);
+    return a0 < b0 + ny && b0 < a0 + nx;
+}
+
+bool misaligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a != 0; }
+
+struct Buffer {
+    const void* p;
+    size_t bytes;
+    const char* name;
+    bool written;
+};
+
+// No written buffer may overlap any other buffer.
+kla_status check_overlaps(const Buffer* bufs, int n) {
+    for (int i = 0; i < n; ++i) {
+        if (!bufs[i].written) continue;
+        for (int j = 0; j < n; ++j)
+            if (j != i && overlaps(bufs[i].p, bufs[i].bytes, bufs[j].p, bufs[j].bytes))
+                return fail(KLA_ERR_INVALID_ARG, "%s overlaps %s", bufs[i].name, bufs[j].name);
+    }
+    return KLA_OK;
+}
+
+// Sizes, dtype and the plan shared by both directions.  Sets *empty when some
+// size is 0 (nothing to do).
+kla_status common_checks(int64_t B, int64_t H, int64_t T, int64_t D, kla_dtype dt, int rows,
+                         int waves, int mw, int sw, Plan* pl, bool* empty) {
+    t_detail[0] = '\0';
+    if (B < 0 || H < 0 || T < 0 || D < 0)
+        return fail(KLA_ERR_INVALID_ARG, "negative size B=%lld H=%lld T=%lld D=%lld",
+                    (long long)B, (long long)H, (long long)T, (long long)D);
+    if (dt != KLA_DTYPE_F32 && dt != KLA_DTYPE_BF16)
+        return fail(KLA_ERR_UNSUPPORTED, "unknown input dtype %d", int(dt));
+    if (!kla::make_plan(B, H, T, D, rows, waves, mw, sw, pl))
+        return fail(KLA_ERR_INVALID_ARG, "sizes overflow: B=%lld H=%lld T=%lld D=%lld",
+                    (long long)B, (long long)H, (long long)T, (long long)D);
+    *empty = pl->N == 0;
+    if (*empty) return KLA_OK;
+    if (!pl->offsets_fit)
+        return fail(KLA_ERR_UNSUPPORTED,
+                    "one [T, D] slab is too large (T*D = %lld elements; the limit is about 2^30 "
+                    "elements per 64 channels)", (long long)(T * D));
+    return KLA_OK;
+}
+
+kla_status check_workspace(void* workspace, size_t bytes, const Plan& pl) {
+    if (!workspace) return fail(KLA_ERR_WORKSPACE, "workspace is NULL");
+    if (misaligned(workspace, 256)) return fail(KLA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    if (bytes < pl.ws.bytes)
+        return fail(KLA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", bytes, pl.ws.bytes);
+    return KLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kla_scan_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int64_t D,
+                                   kla_dtype in_dtype) {
+    if (in_dtype != KLA_DTYPE_F32 && in_dtype != KLA_DTYPE_BF16) return 0;
+    Plan pl;
+    if (!kla::make_plan(B, H, T, D, kla::kFwdRows, kla::kFwdWaves, kla::kFwdMatrixWords,
+                        kla::kFwdStateWords, &pl) || pl.N == 0)
+        return 0;
+    return pl.ws.bytes;
+}
+
+size_t kla_scan_bwd_workspace_size(int64_t B, int64_t H, int64_t T, int64_t D,
+                                   kla_dtype in_dtype) {
+    if (in_dtype != KLA_DTYPE_F32 && in_dtype != KLA_DTYPE_BF16) return 0;
+    Plan pl;
+    if (!kla::make_plan(B, H, T, D, kla::kBwdRows, kla::kBwdWaves, kla::kBwdMatrixWords,
+                        kla::kBwdStateWords, &pl) || pl.N == 0)
+        return 0;
+    return pl.ws.bytes;
+}
+
+kla_status kla_scan_fwd(const void* a, const void* p, const void* phi, const void* b,
+                        kla_dtype in_dtype, const float* lam0, const float* eta0,
+                        float* lam, float* eta, int64_t B, int64_t H, int64_t T, int64_t D,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    Plan pl;
+    bool empty = false;
+    kla_status st = common_checks(B, H, T, D, in_dtype, kla::kFwdRows, kla::kFwdWaves,
+                                  kla::kFwdMatrixWords, kla::kFwdStateWords, &pl, &empty);
+    if (st != KLA_OK || empty) return st;
+
+    const void* ins[4] = {a, p, phi, b};
+    const char* names[4] = {"a", "p", "phi", "b"};
+    const size_t esz = in_dtype == KLA_DTYPE_F32 ? 4 : 2;
+    for (int i = 0; i < 4; ++i) {
+        if (!ins[i]) return fail(KLA_ERR_INVALID_ARG, "%s is NULL", names[i]);
+        if (misaligned(ins[i], esz))
+            return fail(KLA_ERR_UNSUPPORTED, "%s is not %zu-byte aligned", names[i], esz);
+    }
+    if (!lam || !eta) return fail(KLA_ERR_INVALID_ARG, "%s is NULL", lam ? "eta" : "lam");
+    if (misaligned(lam, 4) || misaligned(eta, 4))
+        return fail(KLA_ERR_UNSUPPORTED, "outputs must be 4-byte aligned");
+    if ((lam0 && misaligned(lam0, 4)) || (eta0 && misaligned(eta0, 4)))
+        return fail(KLA_ERR_UNSUPPORTED, "lam0/eta0 must be 4-byte aligned");
+    if ((st = check_workspace(workspace, workspace_bytes, pl)) != KLA_OK) return st;
+
+    const size_t in_bytes = size_t(pl.N) * esz, out_bytes = size_t(pl.N) * 4;
+    const size_t st_bytes = size_t(pl.C) * 4;
+    const Buffer bufs[9] = {{a, in_bytes, "a", false},           {p, in_bytes, "p", false},
+                            {phi, in_bytes, "phi", false},       {b, in_bytes, "b", false},
+                            {lam0, st_bytes, "lam0", false},     {eta0, st_bytes, "eta0", false},
+                            {lam, out_bytes, "lam", true},       {eta, out_bytes, "eta", true},
+                            {workspace, pl.ws.bytes, "workspace", true}};
+    if ((st = check_overlaps(bufs, 9)) != KLA_OK) return st;
+
+    kla::FwdArgs args;
+    args.a = a;
+    args.p = p;
+    args.phi = phi;
+    args.b = b;
+    args.lam0 = lam0;
+    args.eta0 = eta0;
+    args.lam = lam;
+    args.eta = eta;
+    args.T = T;
+    args.D = D;
+    args.C = pl.C;
+    args.G = pl.G;
+    args.n_chunks = pl.n_chunks;
+    args.n_tiles = pl.n_tiles;
+    args.ws = kla::workspace_view(workspace, pl.ws);
+    const hipError_t err =
+        kla::launch_scan_fwd(args, in_dtype, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(KLA_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
+    return KLA_OK;
+}
+
+kla_status kla_scan_bwd(const void* a, const void* p, kla_dtype in_dtype,
+                        const float* lam0, const float* eta0, const float* lam,
+                        const float* eta, const float* g_lam, const float* g_eta,
+                        float* g_a, float* g_p, float* g_phi, float* g_b, float* g_lam0,
+                        float* g_eta0, int64_t B, int64_t H, int64_t T, int64_t D,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    Plan pl;
+    bool empty = false;
+    kla_status st = common_checks(B, H, T, D, in_dtype, kla::kBwdRows, kla::kBwdWaves,
+                                  kla::kBwdMatrixWords, kla::kBwdStateWords, &pl, &empty);
+    if (st != KLA_OK || empty) return st;
+
+    const size_t esz = in_dtype == KLA_DTYPE_F32 ? 4 : 2;
+    if (!a || !p) return fail(KLA_ERR_INVALID_ARG, "%s is NULL", a ? "p" : "a");
+    if (misaligned(a, esz) || misaligned(p, esz))
+        return fail(KLA_ERR_UNSUPPORTED, "gates must be %zu-byte aligned", esz);
+    if (!lam || !eta) return fail(KLA_ERR_INVALID_ARG, "saved %s is NULL", lam ? "eta" : "lam");
+    float* outs[4] = {g_a, g_p, g_phi, g_b};
+    const char* onames[4] = {"g_a", "g_p", "g_phi", "g_b"};
+    for (int i = 0; i < 4; ++i)
+        if (!outs[i]) return fail(KLA_ERR_INVALID_ARG, "%s is NULL", onames[i]);
+    const void* f32s[12] = {lam0, eta0, lam, eta, g_lam, g_eta, g_a, g_p, g_phi, g_b, g_lam0, g_eta0};
+    for (int i = 0; i < 12; ++i)
+        if (f32s[i] && misaligned(f32s[i], 4))
+            return fail(KLA_ERR_UNSUPPORTED, "float32 arguments must be 4-byte aligned");
+    if ((st = check_workspace(workspace, workspace_bytes, pl)) != KLA_OK) return st;
+
+    const size_t in_bytes = size_t(pl.N) * esz, f_bytes = size_t(pl.N) * 4;
+    const size_t st_bytes = size_t(pl.C) * 4;
+    const Buffer bufs[15] = {
+        {a, in_bytes, "a", false},           {p, in_bytes, "p", false},
+        {lam0, st_bytes, "lam0", false},     {eta0, st_bytes, "eta0", false},
+        {lam, f_bytes, "lam", false},        {eta, f_bytes, "eta", false},
+        {g_lam, f_bytes, "g_lam", false},    {g_eta, f_bytes, "g_eta", false},
+        {g_a, f_bytes, "g_a", true},         {g_p, f_bytes, "g_p", true},
+        {g_phi, f_bytes, "g_phi", true},     {g_b, f_bytes, "g_b", true},
+        {g_lam0, st_bytes, "g_lam0", true},  {g_eta0, st_bytes, "g_eta0", true},
+        {workspace, pl.ws.bytes, "workspace", true}};
+    if ((st = check_overlaps(bufs, 15)) != KLA_OK) return st;
+
+    kla::BwdArgs args;
+    args.a = a;
+    args.p = p;
+    args.lam0 = lam0;
+    args.eta0 = eta0;
+    args.lam = lam;
+    args.eta = eta;
+    args.g_lam = g_lam;
+    args.g_eta = g_eta;
+    args.g_a = g_a;
+    args.g_p = g_p;
+    args.g_phi = g_phi;
+    args.g_b = g_b;
+    args.g_lam0 = g_lam0;
+    args.g_eta0 = g_eta0;
+    args.T = T;
+    args.D = D;
+    args.C = pl.C;
+    args.G = pl.G;
+    args.n_chunks = pl.n_chunks;
+    args.n_tiles = pl.n_tiles;
+    args.ws = kla::workspace_view(workspace, pl.ws);
+    const hipError_t err =
+        kla::launch_scan_bwd(args, in_dtype, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(KLA_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
+    return KLA_OK;
+}
+
+kla_status kla_workspace_health(void* workspace, uint32_t* flags_out, void* stream) {
+    t_detail[0] = '\0';
+    if (!workspace) return fail(KLA_ERR_WORKSPACE, "workspace is NULL");
+    if (!flags_out) return fail(KLA_ERR_INVALID_ARG, "flags_out is NULL");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint32_t* word = static_cast<uint32_t*>(workspace) + 3;
+    uint32_t host = 0;
+    hipError_t err = hipMemcpyAsync(&host, word, sizeof(host), hipMemcpyDeviceToHost, s);
+    if (err == hipSuccess) err = hipStreamSynchronize(s);
+    if (err == hipSuccess && host != 0) {
+        const uint32_t zero = 0;
+        err = hipMemcpyAsync(word, &zero, sizeof(zero), hipMemcpyHostToDevice, s);
+        if (err == hipSuccess) err = hipStreamSynchronize(s);
+    }
+    if (err != hipSuccess) return fail(KLA_ERR_HIP, "health read: %s", hipGetErrorString(err));
+    *flags_out = host;
+    return KLA_OK;
+}
+
+const char* kla_status_string(kla_status s) {
+    switch (s) {
+        case KLA_OK: return "KLA_OK";
+        case KLA_ERR_INVALID_ARG: return "KLA_ERR_INVALID_ARG";
+        case KLA_ERR_UNSUPPORTED: return "KLA_ERR_UNSUPPORTED";
+        case KLA_ERR_WORKSPACE: return "KLA_ERR_WORKSPACE";
+        case KLA_ERR_HIP: return "KLA_ERR_HIP";
+    }
+    return "KLA_ERR_UNKNOWN";
+}
+
+const char* kla_last_error_detail(void) { return t_detail; }
+
+}  // extern "C"

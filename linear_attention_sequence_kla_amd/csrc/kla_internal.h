@@ -1,0 +1,71 @@
+// kla_internal.h -- host-side plumbing shared by the libkla sources (not part
+// of the public ABI): tiling plans and the kernel launchers.
+
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kla.h"
+#include "kla_lookback.h"
+
+namespace kla {
+
+// Tiling of a [B, H, T, D] problem into tiles of 64 channels by `rows` time
+// steps, and the workspace those tiles need.
+struct Plan {
+    int64_t C;         // channels B*H*D
+    int64_t N;         // elements B*H*T*D
+    int64_t G;         // 64-channel column groups
+    int64_t n_chunks;  // tiles along T
+    int64_t n_tiles;
+    bool offsets_fit;  // per-wave 32-bit byte offsets cannot overflow
+    WorkspaceLayout ws;
+};
+
+// Returns false on negative or overflowing sizes.
+bool make_plan(int64_t B, int64_t H, int64_t T, int64_t D, int rows_per_wave,
+               int waves, int matrix_words, int state_words, Plan* pl);
+
+struct FwdArgs {
+    const void* a;
+    const void* p;
+    const void* phi;
+    const void* b;
+    const float* lam0;  // may be NULL (1)
+    const float* eta0;  // may be NULL (0)
+    float* lam;
+    float* eta;
+    int64_t T, D, C, G, n_chunks, n_tiles;
+    Workspace ws;
+};
+
+struct BwdArgs {
+    const void* a;
+    const void* p;
+    const float* lam0;   // may be NULL (1)
+    const float* eta0;   // may be NULL (0)
+    const float* lam;    // forward outputs
+    const float* eta;
+    const float* g_lam;  // may be NULL (0)
+    const float* g_eta;  // may be NULL (0)
+    float* g_a;
+    float* g_p;
+    float* g_phi;
+    float* g_b;
+    float* g_lam0;  // may be NULL (not written)
+    float* g_eta0;  // may be NULL (not written)
+    int64_t T, D, C, G, n_chunks, n_tiles;
+    Workspace ws;
+};
+
+// Tile shapes (rows per wave, waves per workgroup) and record sizes.
+constexpr int kFwdRows = 28, kFwdWaves = 4, kFwdMatrixWords = 7, kFwdStateWords = 2;
+constexpr int kBwdRows = 20, kBwdWaves = 4, kBwdMatrixWords = 6, kBwdStateWords = 2;
+
+hipError_t launch_scan_fwd(const FwdArgs& args, kla_dtype dtype, hipStream_t stream);
+hipError_t launch_scan_bwd(const BwdArgs& args, kla_dtype dtype, hipStream_t stream);
+
+}  // namespace kla

@@ -1,0 +1,309 @@
+// kla_scan_bwd.hip -- backward KLA scan kernel (vector-Jacobian product) for
+// gfx950 (MI355X).
+//
+// The forward step (Pith review of arXiv 2602.10743, "Circularity check",
+// Theorems 1 and 2), with d_t = a_t^2 + p_t lam_{t-1}:
+//     lam_t = lam_{t-1} / d_t + phi_t,     eta_t = (a_t / d_t) eta_{t-1} + b_t.
+// Given upstream gradients g_lam[t], g_eta[t] of a loss with respect to the
+// outputs, reverse-mode differentiation runs backwards in t.  With
+// f = a/d, alpha = f^2 = dlam_t/dlam_{t-1}, beta = -p f eta_{t-1} / d =
+// deta_t/dlam_{t-1}, and (cl, ce) the adjoint carried into token t from the
+// tokens after it:
+//     Lam_t = g_lam[t] + cl,  Eta_t = g_eta[t] + ce        (total adjoints)
+//     g_phi[t] = Lam_t,       g_b[t] = Eta_t
+//     g_a[t] = Lam_t (-2 a lam_{t-1} / d^2) + Eta_t eta_{t-1} (p lam_{t-1} - a^2) / d^2
+//     g_p[t] = Lam_t (-lam_{t-1}^2 / d^2)   + Eta_t (-a lam_{t-1} eta_{t-1} / d^2)
+//     carry to t-1: (alpha Lam_t + beta Eta_t, f Eta_t)
+// and the carry past the first token is (g_lam0, g_eta0).  The states
+// lam_{t-1}, eta_{t-1} are the forward outputs (saved by the caller).
+//
+// The carry recursion is affine in (cl, ce), so per token it is the 3x3 map
+//     [[alpha, beta, alpha g_lam + beta g_eta], [0, f, f g_eta], [0, 0, 1]],
+// and a chunk of tokens composes to one map [[u, v, x], [0, w, y], [0, 0, s]]
+// (homogeneous: any positive scale of all six entries is the same map, which
+// the kernel uses to renormalise by powers of two).  That makes the backward
+// pass the same single-pass scan as the forward one, run from the end of the
+// sequence: tiles are numbered from the last chunk, each looks back over the
+// tiles *after* it in time (kla_lookback.h), and each wave replays its rows
+// last to first from its carry, writing the four gradients.
+
+#include "kla_internal.h"
+
+namespace kla {
+namespace {
+
+constexpr int kRenormEvery = 8;  // tokens between renormalisations
+
+// Homogeneous affine map on the adjoint carry:
+//   (cl, ce) -> ((u cl + v ce + x) / s, (w ce + y) / s).
+struct Adj {
+    double u, v, x, w, y, s;
+};
+
+__device__ inline void renorm(Adj& m) {
+    const double mx = fmax(fmax(fmax(fabs(m.u), fabs(m.v)), fmax(fabs(m.x), fabs(m.w))),
+                           fmax(fabs(m.y), fabs(m.s)));
+    const int e = renorm_exponent(mx);
+    m.u = pow2_scale(m.u, e);
+    m.v = pow2_scale(m.v, e);
+    m.x = pow2_scale(m.x, e);
+    m.w = pow2_scale(m.w, e);
+    m.y = pow2_scale(m.y, e);
+    m.s = pow2_scale(m.s, e);
+}
+
+// A.B: the map that applies B first, then A.
+__device__ inline Adj mul(const Adj& A, const Adj& B) {
+    Adj r;
+    r.u = A.u * B.u;
+    r.v = fma(A.u, B.v, A.v * B.w);
+    r.x = fma(A.u, B.x, fma(A.v, B.y, A.x * B.s));
+    r.w = A.w * B.w;
+    r.y = fma(A.w, B.y, A.y * B.s);
+    r.s = A.s * B.s;
+    renorm(r);
+    return r;
+}
+
+__device__ inline void apply(const Adj& m, double& cl, double& ce) {
+    const double r = recip(m.s);
+    const double ncl = fma(m.u, cl, fma(m.v, ce, m.x)) * r;
+    ce = fma(m.w, ce, m.y) * r;
+    cl = ncl;
+}
+
+__device__ inline Adj lds_adj(const double (*s)[6][kWave], int j, int lane) {
+    return Adj{s[j][0][lane], s[j][1][lane], s[j][2][lane],
+               s[j][3][lane], s[j][4][lane], s[j][5][lane]};
+}
+
+// The tile's map: wave 0's map applied last (waves cover increasing times).
+template <int W>
+__device__ inline Adj tile_adj(const double (*s)[6][kWave], int lane) {
+    Adj t = lds_adj(s, W - 1, lane);
+#pragma unroll 1
+    for (int j = W - 2; j >= 0; --j) t = mul(lds_adj(s, j, lane), t);
+    return t;
+}
+
+__device__ inline void store_adj(double* rec, int lane, const Adj& m) {
+    rec_store(rec + 0 * kWave + lane, m.u);
+    rec_store(rec + 1 * kWave + lane, m.v);
+    rec_store(rec + 2 * kWave + lane, m.x);
+    rec_store(rec + 3 * kWave + lane, m.w);
+    rec_store(rec + 4 * kWave + lane, m.y);
+    rec_store(rec + 5 * kWave + lane, m.s);
+}
+
+__device__ inline Adj load_adj(double* rec, int lane) {
+    Adj m;
+    m.u = rec_load(rec + 0 * kWave + lane);
+    m.v = rec_load(rec + 1 * kWave + lane);
+    m.x = rec_load(rec + 2 * kWave + lane);
+    m.w = rec_load(rec + 3 * kWave + lane);
+    m.y = rec_load(rec + 4 * kWave + lane);
+    m.s = rec_load(rec + 5 * kWave + lane);
+    return m;
+}
+
+__device__ inline float load_f32(const char* base, uint32_t off) {
+    return __builtin_nontemporal_load(reinterpret_cast<const float*>(base + off));
+}
+
+template <typename In, int L, int W>
+__global__ __launch_bounds__(W * kWave) void kla_scan_bwd_kernel(BwdArgs g) {
+    __shared__ double s_adj[W][6][kWave];
+    __shared__ double s_carry[W][2][kWave];
+    static_assert(kBwdMatrixWords == 6 && kBwdStateWords == 2, "record layout");
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t ticket = blockIdx.x;
+    uint32_t tag = 0;
+
+    if (ticket < g.n_tiles) {
+        // ---- tile and lane coordinates; tiles run from the sequence's end ----
+        const int64_t cc = ticket / g.G;
+        const int64_t grp = ticket - cc * g.G;
+        const int64_t c = g.n_chunks - 1 - cc;  // chunk along T
+        const int64_t t0 = (c * W + w) * L;     // first row of this wave
+        const int nr = int(min(int64_t(L), g.T - t0));
+        const LaneMap lm = lane_map(grp, t0, lane, g.T, g.D, g.C);
+        const uint32_t in_row = uint32_t(g.D * sizeof(In));
+        const uint32_t f_row = uint32_t(g.D * sizeof(float));
+        const uint32_t in_off = lm.lane_el * uint32_t(sizeof(In));
+        const uint32_t f_off = lm.lane_el * uint32_t(sizeof(float));
+        const char* pa = static_cast<const char*>(g.a) + lm.e0 * int64_t(sizeof(In));
+        const char* pp = static_cast<const char*>(g.p) + lm.e0 * int64_t(sizeof(In));
+        const char* pgl = reinterpret_cast<const char*>(g.g_lam) + lm.e0 * 4;
+        const char* pge = reinterpret_cast<const char*>(g.g_eta) + lm.e0 * 4;
+        // saved states lam_{t-1}, eta_{t-1}: row t0 + i - 1; sh = 1 when the
+        // wave starts the sequence (its row 0 takes lam0, eta0 instead)
+        const int sh = t0 > 0 ? 0 : 1;
+        const int64_t sb = lm.e0 - (t0 > 0 ? g.D : 0);
+        const char* pl = reinterpret_cast<const char*>(g.lam) + sb * 4;
+        const char* pe = reinterpret_cast<const char*>(g.eta) + sb * 4;
+
+        // ---- load the wave's rows (rows past T repeat the last one) ----
+        float ra[L], rp[L], rl[L], re[L], rgl[L], rge[L];
+        if (nr > 0) {
+#pragma unroll
+            for (int i = 0; i < L; ++i) {
+                const int ri = min(i, nr - 1);
+                ra[i] = load_gate<In>(pa, in_off + uint32_t(ri) * in_row);
+                rp[i] = load_gate<In>(pp, in_off + uint32_t(ri) * in_row);
+                if (ri - sh >= 0) {
+                    rl[i] = load_f32(pl, f_off + uint32_t(ri - sh) * f_row);
+                    re[i] = load_f32(pe, f_off + uint32_t(ri - sh) * f_row);
+                } else {
+                    rl[i] = g.lam0 ? g.lam0[lm.qc] : 1.0f;
+                    re[i] = g.eta0 ? g.eta0[lm.qc] : 0.0f;
+                }
+                rgl[i] = g.g_lam ? load_f32(pgl, f_off + uint32_t(ri) * f_row) : 0.0f;
+                rge[i] = g.g_eta ? load_f32(pge, f_off + uint32_t(ri) * f_row) : 0.0f;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < L; ++i) {
+                ra[i] = 1.0f;
+                rp[i] = 0.0f;
+                rl[i] = 1.0f;
+                re[i] = 0.0f;
+                rgl[i] = 0.0f;
+                rge[i] = 0.0f;
+            }
+        }
+        if (w == 0) tag = read_tag(g.ws);
+
+        // ---- the wave's map: per-token maps multiplied in time order ----
+        Adj m{1.0, 0.0, 0.0, 1.0, 0.0, 1.0};
+#pragma unroll
+        for (int i = 0; i < L; ++i) {
+            if (i < nr) {  // rows past T are the identity
+                const double a = ra[i], p = rp[i], lp = rl[i], ep = re[i];
+                const double rd = recip(fma(p, lp, a * a));
+                const double f = a * rd;
+                const double al = f * f;
+                const double be = -p * f * ep * rd;
+                const double ge = rge[i];
+                const double o1 = fma(al, double(rgl[i]), be * ge);
+                const double o2 = f * ge;
+                const double nx = fma(m.u, o1, fma(m.v, o2, m.x));
+                m.v = fma(m.u, be, m.v * f);
+                m.u = m.u * al;
+                m.y = fma(m.w, o2, m.y);
+                m.w = m.w * f;
+                m.x = nx;
+            }
+            if ((i % kRenormEvery) == kRenormEvery - 1 || i == L - 1) renorm(m);
+        }
+#pragma unroll
+        for (int i = 0; i < L; ++i)
+            asm volatile("" : "+v"(ra[i]), "+v"(rp[i]), "+v"(rl[i]), "+v"(re[i]), "+v"(rgl[i]),
+                         "+v"(rge[i]));
+        s_adj[w][0][lane] = m.u;
+        s_adj[w][1][lane] = m.v;
+        s_adj[w][2][lane] = m.x;
+        s_adj[w][3][lane] = m.w;
+        s_adj[w][4][lane] = m.y;
+        s_adj[w][5][lane] = m.s;
+        __syncthreads();
+
+        // ---- tile carry (wave 0): publish, look back over later tiles ----
+        if (w == 0) {
+            const bool has_next = c > 0;  // earlier chunks follow in tile order
+            double* const matrix = g.ws.matrix;
+            double* const state = g.ws.state;
+            double cl = 0.0, ce = 0.0;  // nothing flows in past the sequence end
+            if (c + 1 < g.n_chunks) {
+                if (has_next) {
+                    store_adj(matrix + size_t(ticket) * 6 * kWave, lane, tile_adj<W>(s_adj, lane));
+                    publish(&g.ws.flags[ticket], lane, flag_word(tag, kStatusAggregate));
+                }
+                int64_t j = ticket - g.G;
+                uint32_t st;
+                while ((st = wait_flag(&g.ws.flags[j], tag, g.ws.header)) == kStatusAggregate)
+                    j -= g.G;
+                if (st == kStatusInclusive) {
+                    cl = rec_load(state + size_t(j) * 2 * kWave + lane);
+                    ce = rec_load(state + size_t(j) * 2 * kWave + kWave + lane);
+                    for (int64_t k = j + g.G; k < ticket; k += g.G)
+                        apply(load_adj(matrix + size_t(k) * 6 * kWave, lane), cl, ce);
+                }  // else the wait gave up: the health word is set, outputs are wrong
+            }
+            if (has_next) {
+                double l = cl, e = ce;
+                apply(tile_adj<W>(s_adj, lane), l, e);
+                rec_store(state + size_t(ticket) * 2 * kWave + lane, l);
+                rec_store(state + size_t(ticket) * 2 * kWave + kWave + lane, e);
+                publish(&g.ws.flags[ticket], lane, flag_word(tag, kStatusInclusive));
+            } else if (g.n_chunks > 1) {
+                publish(&g.ws.flags[ticket], lane, flag_word(tag, kStatusFinished));
+            }
+            // carry into every wave: the last wave gets the tile's, each
+            // earlier one the carry through the maps of the waves after it
+            s_carry[W - 1][0][lane] = cl;
+            s_carry[W - 1][1][lane] = ce;
+#pragma unroll 1
+            for (int j = W - 1; j > 0; --j) {
+                apply(lds_adj(s_adj, j, lane), cl, ce);
+                s_carry[j - 1][0][lane] = cl;
+                s_carry[j - 1][1][lane] = ce;
+            }
+        }
+        __syncthreads();
+
+        // ---- replay the wave's rows last to first, writing the gradients ----
+        if (nr > 0) {
+            double cl = s_carry[w][0][lane], ce = s_carry[w][1][lane];
+            char* oa = reinterpret_cast<char*>(g.g_a) + lm.e0 * 4;
+            char* op = reinterpret_cast<char*>(g.g_p) + lm.e0 * 4;
+            char* of = reinterpret_cast<char*>(g.g_phi) + lm.e0 * 4;
+            char* ob = reinterpret_cast<char*>(g.g_b) + lm.e0 * 4;
+#pragma unroll
+            for (int i = L - 1; i >= 0; --i) {
+                if (i >= nr) continue;  // (uniform; keeps the loop fully unrolled)
+                const double a = ra[i], p = rp[i], lp = rl[i], ep = re[i];
+                const double rd = recip(fma(p, lp, a * a));
+                const double rd2 = rd * rd;
+                const double f = a * rd;
+                const double Lam = double(rgl[i]) + cl;
+                const double Eta = double(rge[i]) + ce;
+                const double ga = (Lam * (-2.0 * a * lp) + Eta * ep * fma(p, lp, -a * a)) * rd2;
+                const double gp = -lp * (Lam * lp + Eta * a * ep) * rd2;
+                if (lm.valid) {
+                    const uint32_t off = f_off + uint32_t(i) * f_row;
+                    __builtin_nontemporal_store(float(ga), reinterpret_cast<float*>(oa + off));
+                    __builtin_nontemporal_store(float(gp), reinterpret_cast<float*>(op + off));
+                    __builtin_nontemporal_store(float(Lam), reinterpret_cast<float*>(of + off));
+                    __builtin_nontemporal_store(float(Eta), reinterpret_cast<float*>(ob + off));
+                }
+                cl = fma(f * f, Lam, -p * f * ep * rd * Eta);
+                ce = f * Eta;
+            }
+            if (t0 == 0 && lm.valid) {
+                if (g.g_lam0) g.g_lam0[lm.q] = float(cl);
+                if (g.g_eta0) g.g_eta0[lm.q] = float(ce);
+            }
+        }
+    }
+
+    // ---- the last workgroup advances the epoch once every tile read it ----
+    if (ticket == int64_t(gridDim.x) - 1 && g.n_chunks > 1 && w == 0)
+        advance_epoch(g.ws, tag, (g.n_chunks - 1) * g.G, g.n_tiles, lane);
+}
+
+}  // namespace
+
+hipError_t launch_scan_bwd(const BwdArgs& args, kla_dtype dtype, hipStream_t stream) {
+    const dim3 grid(unsigned(args.n_tiles)), block(kBwdWaves * kWave);
+    if (dtype == KLA_DTYPE_F32)
+        hipLaunchKernelGGL((kla_scan_bwd_kernel<float, kBwdRows, kBwdWaves>), grid, block, 0,
+                           stream, args);
+    else
+        hipLaunchKernelGGL((kla_scan_bwd_kernel<uint16_t, kBwdRows, kBwdWaves>), grid, block, 0,
+                           stream, args);
+    return hipGetLastError();
+}
+
+}  // namespace kla

@@ -52,6 +52,10 @@ def library() -> ctypes.CDLL:
         lib.kla_scan_fwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, vp,
                                      i64, i64, i64, i64, vp, sz, vp]
         lib.kla_scan_fwd.restype = ctypes.c_int
+        lib.kla_scan_bwd_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+        lib.kla_scan_bwd_workspace_size.restype = sz
+        lib.kla_scan_bwd.argtypes = [vp, vp, ctypes.c_int] + [vp] * 12 + [i64] * 4 + [vp, sz, vp]
+        lib.kla_scan_bwd.restype = ctypes.c_int
         lib.kla_workspace_health.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), vp]
         lib.kla_workspace_health.restype = ctypes.c_int
         lib.kla_status_string.argtypes = [ctypes.c_int]
@@ -72,6 +76,11 @@ def _check(status: int):
 def workspace_size(B: int, H: int, T: int, D: int, dtype=torch.float32) -> int:
     """Bytes of workspace kla_scan_fwd needs (0 for an empty problem)."""
     return int(library().kla_scan_fwd_workspace_size(B, H, T, D, _DTYPES[dtype]))
+
+
+def bwd_workspace_size(B: int, H: int, T: int, D: int, dtype=torch.float32) -> int:
+    """Bytes of workspace kla_scan_bwd needs (0 for an empty problem)."""
+    return int(library().kla_scan_bwd_workspace_size(B, H, T, D, _DTYPES[dtype]))
 
 
 # Workspaces are zero-filled once and then reused: libkla leaves them ready
@@ -135,14 +144,97 @@ def scan_fwd(a: torch.Tensor, p: torch.Tensor, phi: torch.Tensor, b: torch.Tenso
                     or not t.is_contiguous()):
                 raise ValueError("outputs must be contiguous float32 [B, H, T, D] on a's device")
     stream = torch.cuda.current_stream(a.device)
-    nbytes = workspace_size(B, H, T, D, a.dtype)
     if workspace is None:
-        workspace = get_workspace(nbytes, a.device, stream)
+        workspace = get_workspace(workspace_size(B, H, T, D, a.dtype), a.device, stream)
     _check(library().kla_scan_fwd(
         _ptr(a), _ptr(p), _ptr(phi), _ptr(b), _DTYPES[a.dtype], _ptr(lam0), _ptr(eta0),
         _ptr(lam), _ptr(eta), B, H, T, D, _ptr(workspace), workspace.numel(),
         ctypes.c_void_p(stream.cuda_stream)))
     return lam, eta
+
+
+def _check_f32(name, t, shape, device):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype != torch.float32 or t.device != device:
+        raise ValueError("%s must be float32 %s on %s" % (name, tuple(shape), device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def scan_bwd(a: torch.Tensor, p: torch.Tensor, lam: torch.Tensor, eta: torch.Tensor,
+             g_lam: torch.Tensor | None, g_eta: torch.Tensor | None,
+             lam0: torch.Tensor | None = None, eta0: torch.Tensor | None = None,
+             need_state_grads: bool = True, workspace: torch.Tensor | None = None):
+    """Backward KLA scan on the current stream (kla_scan_bwd).
+
+    a, p: the forward gates; lam, eta: the forward outputs; g_lam, g_eta:
+    upstream gradients (None: zero); lam0, eta0: the forward initial state.
+    Returns (g_a, g_p, g_phi, g_b, g_lam0, g_eta0), float32; the last two are
+    None unless need_state_grads.
+    """
+    if a.dim() != 4 or p.shape != a.shape or p.dtype != a.dtype:
+        raise ValueError("a and p must be [B, H, T, D] tensors of one dtype")
+    if a.dtype not in _DTYPES:
+        raise ValueError("gate dtype must be float32 or bfloat16, got %s" % a.dtype)
+    for name, t in (("a", a), ("p", p)):
+        if not t.is_cuda or t.device != a.device or not t.is_contiguous():
+            raise ValueError("%s must be contiguous on a's GPU" % name)
+    B, H, T, D = a.shape
+    dev = a.device
+    for name, t in (("lam", lam), ("eta", eta), ("g_lam", g_lam), ("g_eta", g_eta)):
+        _check_f32(name, t, a.shape, dev)
+    if lam is None or eta is None:
+        raise ValueError("the forward outputs lam and eta are required")
+    for name, t in (("lam0", lam0), ("eta0", eta0)):
+        _check_f32(name, t, (B, H, D), dev)
+    g_a, g_p, g_phi, g_b = (torch.empty(a.shape, dtype=torch.float32, device=dev)
+                            for _ in range(4))
+    g_lam0 = g_eta0 = None
+    if need_state_grads:
+        g_lam0 = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+        g_eta0 = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    if workspace is None:
+        workspace = get_workspace(max(bwd_workspace_size(B, H, T, D, a.dtype),
+                                      workspace_size(B, H, T, D, a.dtype)), dev, stream)
+    _check(library().kla_scan_bwd(
+        _ptr(a), _ptr(p), _DTYPES[a.dtype], _ptr(lam0), _ptr(eta0), _ptr(lam), _ptr(eta),
+        _ptr(g_lam), _ptr(g_eta), _ptr(g_a), _ptr(g_p), _ptr(g_phi), _ptr(g_b),
+        _ptr(g_lam0), _ptr(g_eta0), B, H, T, D, _ptr(workspace), workspace.numel(),
+        ctypes.c_void_p(stream.cuda_stream)))
+    return g_a, g_p, g_phi, g_b, g_lam0, g_eta0
+
+
+class KLAScan(torch.autograd.Function):
+    """Differentiable forward scan: kla_scan_fwd forward, kla_scan_bwd backward.
+
+    Gradients are float32 and are cast to each input's dtype.
+    """
+
+    @staticmethod
+    def forward(ctx, a, p, phi, b, lam0, eta0):
+        lam, eta = scan_fwd(a, p, phi, b, lam0, eta0)
+        ctx.save_for_backward(a, p, lam0, eta0, lam, eta)
+        ctx.has_state = (lam0 is not None, eta0 is not None)
+        return lam, eta
+
+    @staticmethod
+    def backward(ctx, g_lam, g_eta):
+        a, p, lam0, eta0, lam, eta = ctx.saved_tensors
+        g_lam = None if g_lam is None else g_lam.contiguous().float()
+        g_eta = None if g_eta is None else g_eta.contiguous().float()
+        need = ctx.needs_input_grad
+        g_a, g_p, g_phi, g_b, g_lam0, g_eta0 = scan_bwd(
+            a, p, lam, eta, g_lam, g_eta, lam0, eta0, need_state_grads=need[4] or need[5])
+        cast = (lambda g, x: g.to(x.dtype))  # noqa: E731
+        return (cast(g_a, a), cast(g_p, p), cast(g_phi, a), cast(g_b, a),
+                g_lam0 if need[4] else None, g_eta0 if need[5] else None)
+
+
+def kla_scan(a, p, phi, b, lam0=None, eta0=None):
+    """Differentiable KLA scan: returns (lam, eta); see KLAScan."""
+    return KLAScan.apply(a, p, phi, b, lam0, eta0)
 
 
 def workspace_health(workspace: torch.Tensor) -> int:

@@ -77,3 +77,38 @@ def assert_parity(rep: dict, tol: float, what: str = ""):
     assert rep["range_violations"] == 0, msg
     assert rep["lam_max_rel"] <= tol, msg
     assert rep["eta_max_scaled"] <= tol, msg
+
+
+GRAD_FLOOR = 2.0 ** -100
+
+
+def compare_grads(got: dict, grads: dict, mags: dict) -> dict:
+    """Per-input error of fp32 gradients against the float64 backward oracle:
+    max |g_hat - g| / max(m, 2^-100), m the cancellation-free magnitude of the
+    same sum (a gradient is a signed sum that can cancel), with the fp32
+    overflow rule and no NaN, as for the forward outputs."""
+    rep = {"nan": 0, "range_violations": 0}
+    with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+        for k, ref in grads.items():
+            if k not in got or got[k] is None:
+                continue
+            g = _np(got[k]).astype(np.float64)
+            ref = np.asarray(ref, dtype=np.float64)
+            m = np.asarray(mags[k], dtype=np.float64)
+            over = np.isinf(ref.astype(np.float32))
+            rep["nan"] += int(np.isnan(g).sum())
+            rep["range_violations"] += int((over & (g != np.sign(ref) * np.inf)).sum())
+            rep["range_violations"] += int((~over & ~np.isfinite(g)).sum())
+            ok = ~over & np.isfinite(g)
+            err = np.abs(g - ref) / np.maximum(m, GRAD_FLOOR)
+            rep[k] = float(err[ok].max()) if ok.any() else 0.0
+    return rep
+
+
+def assert_grad_parity(rep: dict, tol: float, what: str = ""):
+    msg = "%s %r" % (what, rep)
+    assert rep["nan"] == 0, msg
+    assert rep["range_violations"] == 0, msg
+    for k, v in rep.items():
+        if k not in ("nan", "range_violations"):
+            assert v <= tol, msg

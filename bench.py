@@ -28,8 +28,10 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
 CSRC = os.path.join(ROOT, "linear_attention_sequence_kla_amd", "csrc")
 KERNEL_SOURCES = {"fwd": ("kla_scan_fwd.hip", "kla_lookback.h", "kla_internal.h"),
-                  "bwd": ("kla_scan_bwd.hip", "kla_lookback.h", "kla_internal.h")}
-KERNEL_NAMES = {"fwd": "kla_scan_kernel", "bwd": "kla_scan_bwd_kernel"}
+                  "bwd": ("kla_scan_bwd.hip", "kla_lookback.h", "kla_internal.h"),
+                  "decode": ("kla_decode.hip", "kla_lookback.h", "kla_internal.h")}
+KERNEL_NAMES = {"fwd": "kla_scan_kernel", "bwd": "kla_scan_bwd_kernel",
+                "decode": "kla_decode_kernel"}
 
 
 def kernel_hash(direction: str = "fwd") -> str:
@@ -47,6 +49,8 @@ def bytes_per_element(dtype: str, direction: str = "fwd") -> int:
     gate = 4 if dtype == "f32" else 2
     if direction == "fwd":
         return 4 * gate + 2 * 4
+    if direction == "decode":  # 4 gates, state read and written in place
+        return 4 * gate + 2 * 4 + 2 * 4
     return 2 * gate + 4 * 4 + 4 * 4
 
 
@@ -179,8 +183,9 @@ def main(argv=None):
     ap.add_argument("--workload", type=int, default=1,
                     help="0..4; the headline is 1 (small-LM layer)")
     ap.add_argument("--sets", type=int, default=2, help="input/output sets to rotate")
-    ap.add_argument("--direction", choices=("fwd", "bwd"), default="fwd",
-                    help="fwd: kla_scan_fwd (the headline); bwd: kla_scan_bwd")
+    ap.add_argument("--direction", choices=("fwd", "bwd", "decode"), default="fwd",
+                    help="fwd: kla_scan_fwd (the headline); bwd: kla_scan_bwd; decode: "
+                         "kla_decode_step on one token of every channel of the workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the scan, run torch's plain device copy of MIB MiB "
@@ -217,7 +222,8 @@ def main(argv=None):
 
     from kla_inputs import WORKLOADS, make_workload
     from linear_attention_sequence_kla_amd import (
-        bwd_workspace_size, get_workspace, scan_bwd, scan_fwd, workspace_health, workspace_size)
+        bwd_workspace_size, decode_step, get_workspace, scan_bwd, scan_fwd, workspace_health,
+        workspace_size)
 
     w = WORKLOADS[args.workload]
     d = args.direction
@@ -227,7 +233,7 @@ def main(argv=None):
     get_workspace(max(workspace_size(*w.shape, TORCH_DTYPE[w.dtype]),
                       bwd_workspace_size(*w.shape, TORCH_DTYPE[w.dtype])), dev, stream)
     sets = []
-    for k in range(args.sets):
+    for k in range(args.sets if d != "decode" else 0):
         g = make_workload(args.workload, device=dev, seed=w.seed + 1000 * k)
         lam = torch.empty(w.shape, dtype=torch.float32, device=dev)
         eta = torch.empty(w.shape, dtype=torch.float32, device=dev)
@@ -239,11 +245,21 @@ def main(argv=None):
             g["g_lam"] = torch.randn(w.shape, generator=gen, device=dev)
             g["g_eta"] = torch.randn(w.shape, generator=gen, device=dev)
         sets.append((g, (lam, eta)))
+    if d == "decode":
+        # one token per channel; the state is updated in place each step
+        from kla_inputs import make_gates, make_initial_state
+        for k in range(args.sets):
+            g = make_gates((w.B, w.H, 1, w.D), w.gates, w.dtype, w.seed + 1000 * k, dev)
+            g = {n: v[:, :, 0].contiguous() for n, v in g.items()}
+            sets.append((g, tuple(x.clone() for x in make_initial_state(
+                w.B, w.H, w.D, random=True, seed=k, device=dev))))
     torch.cuda.synchronize(dev)
 
     def step(i):
         g, out = sets[i % len(sets)]
-        if d == "fwd":
+        if d == "decode":
+            decode_step(g["a"], g["p"], g["phi"], g["b"], out[0], out[1])
+        elif d == "fwd":
             scan_fwd(g["a"], g["p"], g["phi"], g["b"], g["lam0"], g["eta0"], out=out)
         else:
             scan_bwd(g["a"], g["p"], out[0], out[1], g["g_lam"], g["g_eta"], g["lam0"],
@@ -268,7 +284,7 @@ def main(argv=None):
     if health != 0:
         print("warning: workspace health word %#x" % health, file=sys.stderr)
 
-    n = w.elements
+    n = w.elements if d != "decode" else w.channels
     ms_step = wall * 1e3 / args.steps
     k_avg = sum(kernel_ms) / len(kernel_ms)
     bpe = bytes_per_element(w.dtype, d)
@@ -298,6 +314,9 @@ def main(argv=None):
     }
     if d == "bwd":
         rec["metric"] = "KLA backward scan elements (B*H*T*D)/s and achieved HBM GB/s vs peak"
+    if d == "decode":
+        rec["metric"] = "KLA decode step channel updates (B*H*D)/s, one token per step"
+        rec["config"]["elements"] = n
     if not args.no_cpu_baseline and d == "fwd":
         rec["cpu_baseline"] = cpu_baseline(w, sets[0][0])
     print(json.dumps(rec), flush=True)

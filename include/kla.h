@@ -150,6 +150,26 @@ KLA_API kla_status kla_scan_bwd(const void *a, const void *p, kla_dtype in_dtype
                                 void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * One decode step: advances a running filter state by one token, in place.
+ *
+ * For every channel i < n_channels (any layout; B*H*D channels of one token):
+ *     d = a^2 + p lam,  lam <- lam / d + phi,  eta <- (a / d) eta + b,
+ * the step of kla_scan_fwd (computed in float64, stored as float32), so that
+ * repeated decode steps continue a sequence whose prefix went through
+ * kla_scan_fwd (pass its last output row as the state).  This is the
+ * linear-time inference of the "KLA Part 1" primer: constant work and memory
+ * per token.
+ *
+ *   a, p, phi, b  device pointers, [n_channels] of in_dtype (same domain as
+ *                 kla_scan_fwd).
+ *   lam, eta      device pointers, [n_channels] float32, read and written.
+ * No workspace; asynchronous on `stream`; errors as for kla_scan_fwd.
+ */
+KLA_API kla_status kla_decode_step(const void *a, const void *p, const void *phi,
+                                   const void *b, kla_dtype in_dtype,
+                                   float *lam, float *eta, int64_t n_channels, void *stream);
+
+/*
  * Reads the workspace's health word after the calls that used it have
  * completed (it synchronizes `stream`).  *flags_out is 0 when every call so
  * far ran normally; bit 0 is set if a chunk gave up waiting for the carry of

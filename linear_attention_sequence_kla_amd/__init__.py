@@ -5,5 +5,5 @@ The work happens in ``libkla.so`` (HIP kernels behind a C ABI declared in
 """
 
 from .kla import (  # noqa: F401
-    KLAScan, KlaError, LIBRARY, bwd_workspace_size, get_workspace, kla_scan, library, scan_bwd,
-    scan_fwd, workspace_health, workspace_size)
+    KLAScan, KlaError, LIBRARY, bwd_workspace_size, decode_step, get_workspace, kla_scan, library,
+    scan_bwd, scan_fwd, workspace_health, workspace_size)

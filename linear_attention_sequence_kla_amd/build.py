@@ -12,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = [os.path.join(HERE, "csrc", f)
-           for f in ("kla_api.cpp", "kla_scan_fwd.hip", "kla_scan_bwd.hip")]
+           for f in ("kla_api.cpp", "kla_scan_fwd.hip", "kla_scan_bwd.hip", "kla_decode.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "libkla.so")
 ARCH = "gfx950"

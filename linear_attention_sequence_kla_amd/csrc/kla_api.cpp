@@ -268,6 +268,40 @@ kla_status kla_scan_bwd(const void* a, const void* p, kla_dtype in_dtype,
     return KLA_OK;
 }
 
+kla_status kla_decode_step(const void* a, const void* p, const void* phi, const void* b,
+                           kla_dtype in_dtype, float* lam, float* eta, int64_t n_channels,
+                           void* stream) {
+    t_detail[0] = '\0';
+    if (n_channels < 0)
+        return fail(KLA_ERR_INVALID_ARG, "negative channel count %lld", (long long)n_channels);
+    if (in_dtype != KLA_DTYPE_F32 && in_dtype != KLA_DTYPE_BF16)
+        return fail(KLA_ERR_UNSUPPORTED, "unknown input dtype %d", int(in_dtype));
+    if (n_channels == 0) return KLA_OK;
+    if (n_channels > INT64_MAX / 8)
+        return fail(KLA_ERR_INVALID_ARG, "channel count overflows");
+    const void* ins[4] = {a, p, phi, b};
+    const char* names[4] = {"a", "p", "phi", "b"};
+    const size_t esz = in_dtype == KLA_DTYPE_F32 ? 4 : 2;
+    for (int i = 0; i < 4; ++i) {
+        if (!ins[i]) return fail(KLA_ERR_INVALID_ARG, "%s is NULL", names[i]);
+        if (misaligned(ins[i], esz))
+            return fail(KLA_ERR_UNSUPPORTED, "%s is not %zu-byte aligned", names[i], esz);
+    }
+    if (!lam || !eta) return fail(KLA_ERR_INVALID_ARG, "%s is NULL", lam ? "eta" : "lam");
+    if (misaligned(lam, 4) || misaligned(eta, 4))
+        return fail(KLA_ERR_UNSUPPORTED, "lam/eta must be 4-byte aligned");
+    const size_t in_bytes = size_t(n_channels) * esz, st_bytes = size_t(n_channels) * 4;
+    const Buffer bufs[6] = {{a, in_bytes, "a", false},     {p, in_bytes, "p", false},
+                            {phi, in_bytes, "phi", false}, {b, in_bytes, "b", false},
+                            {lam, st_bytes, "lam", true},  {eta, st_bytes, "eta", true}};
+    kla_status st = check_overlaps(bufs, 6);
+    if (st != KLA_OK) return st;
+    const hipError_t err = kla::launch_decode(a, p, phi, b, in_dtype, lam, eta, n_channels,
+                                              static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(KLA_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
+    return KLA_OK;
+}
+
 kla_status kla_workspace_health(void* workspace, uint32_t* flags_out, void* stream) {
     t_detail[0] = '\0';
     if (!workspace) return fail(KLA_ERR_WORKSPACE, "workspace is NULL");

@@ -67,5 +67,7 @@ constexpr int kBwdRows = 20, kBwdWaves = 4, kBwdMatrixWords = 6, kBwdStateWords 
 
 hipError_t launch_scan_fwd(const FwdArgs& args, kla_dtype dtype, hipStream_t stream);
 hipError_t launch_scan_bwd(const BwdArgs& args, kla_dtype dtype, hipStream_t stream);
+hipError_t launch_decode(const void* a, const void* p, const void* phi, const void* b,
+                         kla_dtype dtype, float* lam, float* eta, int64_t n, hipStream_t stream);
 
 }  // namespace kla

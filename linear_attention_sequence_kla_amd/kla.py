@@ -56,6 +56,8 @@ def library() -> ctypes.CDLL:
         lib.kla_scan_bwd_workspace_size.restype = sz
         lib.kla_scan_bwd.argtypes = [vp, vp, ctypes.c_int] + [vp] * 12 + [i64] * 4 + [vp, sz, vp]
         lib.kla_scan_bwd.restype = ctypes.c_int
+        lib.kla_decode_step.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, vp, i64, vp]
+        lib.kla_decode_step.restype = ctypes.c_int
         lib.kla_workspace_health.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), vp]
         lib.kla_workspace_health.restype = ctypes.c_int
         lib.kla_status_string.argtypes = [ctypes.c_int]
@@ -235,6 +237,30 @@ class KLAScan(torch.autograd.Function):
 def kla_scan(a, p, phi, b, lam0=None, eta0=None):
     """Differentiable KLA scan: returns (lam, eta); see KLAScan."""
     return KLAScan.apply(a, p, phi, b, lam0, eta0)
+
+
+def decode_step(a: torch.Tensor, p: torch.Tensor, phi: torch.Tensor, b: torch.Tensor,
+                lam: torch.Tensor, eta: torch.Tensor):
+    """One-token update of the running state (lam, eta), in place, on the
+    current stream (kla_decode_step).  Gates: one token, any shape, all of one
+    dtype (float32 or bfloat16); lam, eta: float32 of the same shape.
+    Returns (lam, eta)."""
+    for name, t in (("a", a), ("p", p), ("phi", phi), ("b", b)):
+        if t.shape != a.shape or t.dtype != a.dtype or t.device != a.device:
+            raise ValueError("%s must match a in shape, dtype and device" % name)
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous GPU tensor" % name)
+    if a.dtype not in _DTYPES:
+        raise ValueError("gate dtype must be float32 or bfloat16, got %s" % a.dtype)
+    for name, t in (("lam", lam), ("eta", eta)):
+        _check_f32(name, t, a.shape, a.device)
+        if t is None:
+            raise ValueError("%s is required" % name)
+    stream = torch.cuda.current_stream(a.device)
+    _check(library().kla_decode_step(_ptr(a), _ptr(p), _ptr(phi), _ptr(b), _DTYPES[a.dtype],
+                                     _ptr(lam), _ptr(eta), a.numel(),
+                                     ctypes.c_void_p(stream.cuda_stream)))
+    return lam, eta
 
 
 def workspace_health(workspace: torch.Tensor) -> int:

@@ -2,7 +2,8 @@
 
 A step is one kla_scan_fwd call over one batch of synthetic gates: the whole
 scan (chunk matrices, carry look-back, replay and output writes) in a single
-kernel launch.  Inputs are generated on the GPU and are resident in HBM
+kernel launch.  The K timed steps are captured once into a HIP graph and
+replayed (--no-graph launches them one by one).  Inputs are generated on the GPU and are resident in HBM
 before timing; two input/output sets alternate so that the 256 MB Infinity
 Cache cannot serve one step from the previous one.
 
@@ -187,6 +188,9 @@ def main(argv=None):
                     help="fwd: kla_scan_fwd (the headline); bwd: kla_scan_bwd; decode: "
                          "kla_decode_step on one token of every channel of the workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", dest="graph", action="store_false",
+                    help="launch the timed steps one by one instead of replaying them "
+                         "from a captured HIP graph")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the scan, run torch's plain device copy of MIB MiB "
                          "(known bytes, to scale rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -230,8 +234,8 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
-    get_workspace(max(workspace_size(*w.shape, TORCH_DTYPE[w.dtype]),
-                      bwd_workspace_size(*w.shape, TORCH_DTYPE[w.dtype])), dev, stream)
+    ws = get_workspace(max(workspace_size(*w.shape, TORCH_DTYPE[w.dtype]),
+                           bwd_workspace_size(*w.shape, TORCH_DTYPE[w.dtype])), dev, stream)
     sets = []
     for k in range(args.sets if d != "decode" else 0):
         g = make_workload(args.workload, device=dev, seed=w.seed + 1000 * k)
@@ -253,6 +257,9 @@ def main(argv=None):
             g = {n: v[:, :, 0].contiguous() for n, v in g.items()}
             sets.append((g, tuple(x.clone() for x in make_initial_state(
                 w.B, w.H, w.D, random=True, seed=k, device=dev))))
+    grads = None
+    if d == "bwd":
+        grads = tuple(torch.empty(w.shape, dtype=torch.float32, device=dev) for _ in range(4))
     torch.cuda.synchronize(dev)
 
     def step(i):
@@ -260,27 +267,47 @@ def main(argv=None):
         if d == "decode":
             decode_step(g["a"], g["p"], g["phi"], g["b"], out[0], out[1])
         elif d == "fwd":
-            scan_fwd(g["a"], g["p"], g["phi"], g["b"], g["lam0"], g["eta0"], out=out)
+            scan_fwd(g["a"], g["p"], g["phi"], g["b"], g["lam0"], g["eta0"], out=out,
+                     workspace=ws)
         else:
             scan_bwd(g["a"], g["p"], out[0], out[1], g["g_lam"], g["g_eta"], g["lam0"],
-                     g["eta0"])
+                     g["eta0"], workspace=ws, out=grads)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize(dev)
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize(dev)
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step(i)
-        ends[i].record(stream)
-    torch.cuda.synchronize(dev)
-    wall = time.perf_counter() - t0
-    kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    health = workspace_health(get_workspace(0, dev, stream))
+    if args.graph:
+        # The K timed launches are captured once into a HIP graph and replayed:
+        # the kernels read their epoch from the workspace, so replays need no
+        # host work (and the graph holds no memset).
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(args.steps):
+                step(i)
+        torch.cuda.synchronize(dev)
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        start.record(stream)
+        graph.replay()
+        end.record(stream)
+        torch.cuda.synchronize(dev)
+        wall = time.perf_counter() - t0
+        kernel_ms = [start.elapsed_time(end) / args.steps] * args.steps
+    else:
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        torch.cuda.synchronize(dev)
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            starts[i].record(stream)
+            step(i)
+            ends[i].record(stream)
+        torch.cuda.synchronize(dev)
+        wall = time.perf_counter() - t0
+        kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    health = workspace_health(ws)
     if health != 0:
         print("warning: workspace health word %#x" % health, file=sys.stderr)
 
@@ -311,6 +338,7 @@ def main(argv=None):
                      "kernel": KERNEL_NAMES[d], "kernel_ms_avg": k_avg,
                      "kernel_ms_min": min(kernel_ms), "bytes_per_element": bpe},
         "health": health,
+        "launch": "hip graph of %d launches" % args.steps if args.graph else "eager",
     }
     if d == "bwd":
         rec["metric"] = "KLA backward scan elements (B*H*T*D)/s and achieved HBM GB/s vs peak"

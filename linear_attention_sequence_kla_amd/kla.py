@@ -167,13 +167,15 @@ def _check_f32(name, t, shape, device):
 def scan_bwd(a: torch.Tensor, p: torch.Tensor, lam: torch.Tensor, eta: torch.Tensor,
              g_lam: torch.Tensor | None, g_eta: torch.Tensor | None,
              lam0: torch.Tensor | None = None, eta0: torch.Tensor | None = None,
-             need_state_grads: bool = True, workspace: torch.Tensor | None = None):
+             need_state_grads: bool = True, workspace: torch.Tensor | None = None,
+             out: tuple | None = None):
     """Backward KLA scan on the current stream (kla_scan_bwd).
 
     a, p: the forward gates; lam, eta: the forward outputs; g_lam, g_eta:
     upstream gradients (None: zero); lam0, eta0: the forward initial state.
     Returns (g_a, g_p, g_phi, g_b, g_lam0, g_eta0), float32; the last two are
-    None unless need_state_grads.
+    None unless need_state_grads.  ``out`` may supply the four [B, H, T, D]
+    gate-gradient tensors.
     """
     if a.dim() != 4 or p.shape != a.shape or p.dtype != a.dtype:
         raise ValueError("a and p must be [B, H, T, D] tensors of one dtype")
@@ -190,8 +192,15 @@ def scan_bwd(a: torch.Tensor, p: torch.Tensor, lam: torch.Tensor, eta: torch.Ten
         raise ValueError("the forward outputs lam and eta are required")
     for name, t in (("lam0", lam0), ("eta0", eta0)):
         _check_f32(name, t, (B, H, D), dev)
-    g_a, g_p, g_phi, g_b = (torch.empty(a.shape, dtype=torch.float32, device=dev)
-                            for _ in range(4))
+    if out is None:
+        g_a, g_p, g_phi, g_b = (torch.empty(a.shape, dtype=torch.float32, device=dev)
+                                for _ in range(4))
+    else:
+        g_a, g_p, g_phi, g_b = out
+        for name, t in zip(("g_a", "g_p", "g_phi", "g_b"), out):
+            if t is None:
+                raise ValueError("%s output is required" % name)
+            _check_f32(name, t, a.shape, dev)
     g_lam0 = g_eta0 = None
     if need_state_grads:
         g_lam0 = torch.empty((B, H, D), dtype=torch.float32, device=dev)

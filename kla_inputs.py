@@ -164,3 +164,60 @@ def make_workload(key: int, device="cpu", seed: int | None = None):
     g = make_gates(w.shape, w.gates, w.dtype, w.seed if seed is None else seed, device)
     g["lam0"], g["eta0"] = make_initial_state(w.B, w.H, w.D, device=device)
     return g
+
+
+# ---------------------------------------------------------------------------
+# Fused-mixer inputs.
+#
+# Recipe: one seeded torch.Generator draws, in order, four float64 standard
+# normal tensors [B, H, T, D] (z_k, z_v, z_lv, z_q) and then, per (h, d)
+# channel, u_A, u_dt (uniform [0, 1)) and z_p (standard normal):
+#   k = z_k, v = z_v, lam_v = softplus(z_lv), q = z_q         (token inputs)
+#   A = 1 + 15 u_A, delta = exp(ln 1e-3 + u_dt (ln 0.1 - ln 1e-3)),
+#   a = exp(-A delta)                                          (OU decay)
+#   p = 0.01 exp(0.5 z_p)                                      (process noise)
+# Token inputs are rounded once to the input dtype (as the gates above); a
+# and p are float32.  The ranges follow the free-parameter ledger of the Pith
+# review of arXiv 2602.10743 (delta learned in [0.001, 0.1], process-noise
+# scale initialised at 0.01, value precision from the input); the decay rates
+# A in [1, 16] span one state expansion of 16.
+
+MIXER_WORKLOADS = {
+    0: Workload(0, "mixer-tiny", 1, 1, 256, 16, "f32", "mixer", 10),
+    1: Workload(1, "mixer-small-lm-layer", 8, 16, 2048, 64, "f32", "mixer", 11),
+    2: Workload(2, "mixer-1b-scale-layer", 4, 32, 8192, 128, "bf16", "mixer", 12),
+    3: Workload(3, "mixer-long-context", 1, 32, 131072, 128, "f32", "mixer", 13),
+}
+
+
+def make_mixer_inputs(shape, dtype: str = "f32", seed: int = 0, device="cpu"):
+    """Returns dict(k, v, lam_v, q, a, p): token tensors of `shape`
+    ([B, H, T, D]) and float32 [H, D] channel gates."""
+    device = torch.device(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    shape = tuple(int(s) for s in shape)
+    out = {}
+    for name in ("k", "v", "lam_v", "q"):
+        z = torch.randn(shape, generator=gen, device=device, dtype=torch.float64)
+        out[name] = _round(_softplus(z) if name == "lam_v" else z, dtype)
+        del z
+    H, D = shape[1], shape[3]
+    u_A = torch.rand((H, D), generator=gen, device=device, dtype=torch.float64)
+    u_dt = torch.rand((H, D), generator=gen, device=device, dtype=torch.float64)
+    z_p = torch.randn((H, D), generator=gen, device=device, dtype=torch.float64)
+    A = 1.0 + 15.0 * u_A
+    lo, hi = torch.log(torch.tensor(1e-3, dtype=torch.float64)), torch.log(
+        torch.tensor(0.1, dtype=torch.float64))
+    delta = torch.exp(lo.to(device) + u_dt * (hi - lo).to(device))
+    out["a"] = torch.exp(-A * delta).to(torch.float32)
+    out["p"] = (0.01 * torch.exp(0.5 * z_p)).to(torch.float32)
+    return out
+
+
+def make_mixer_workload(key: int, device="cpu", seed: int | None = None):
+    """Inputs and initial state of a named mixer workload (0..3)."""
+    w = MIXER_WORKLOADS[key]
+    g = make_mixer_inputs(w.shape, w.dtype, w.seed if seed is None else seed, device)
+    g["lam0"], g["eta0"] = make_initial_state(w.B, w.H, w.D, device=device)
+    return g

@@ -1,6 +1,7 @@
 /*
  * kla_oracle.c -- CPU float64 oracle for the Kalman Linear Attention (KLA)
- * scan: the forward pass and its backward pass (gradients, further below).
+ * scan: the forward pass, its backward pass (gradients, further below) and
+ * the fused mixer (gate production, filter, readout; at the end).
  * TEST INFRASTRUCTURE ONLY: the tests, the smoke check
  * and the benchmark's CPU-baseline leg may call it; the product path never
  * does, and this file shares no code with the HIP library.
@@ -293,4 +294,93 @@ int kla_oracle_scan_bwd(const double *a, const double *p, const double *phi,
         free(work);
     }
     return failed ? -2 : 0;
+}
+
+/*
+ * ---------------------------------------------------------------------------
+ * Fused mixer: gate production, filter and readout.
+ *
+ * A mixer channel observes its token value through an observation operator:
+ * the same scalar model as above, with time-invariant dynamics (the OU decay
+ * a and the process-noise scale p of the Pith review's free-parameter ledger,
+ * one value per (h, d)) and a token observation
+ *
+ *     v_t = k_t x_t + e_t,    precision of e_t = lam_v_t   (lam_v = 0: none)
+ *
+ * whose operator k_t and value precision lam_v_t come from the input.  The
+ * update is the textbook measurement update with operator k (innovation
+ * v - k mupred, gain K = Ppred k / (k^2 Ppred + 1/lam_v), written without
+ * dividing by lam_v).  The information-form update of the review
+ * ("Circularity check") adds k^2 lam_v to the precision, which this update
+ * reproduces.  Readout: q_t times the posterior mean, and the posterior
+ * variance itself.
+ *
+ * Outputs per token: out = q mu, var = P, mu_abs = eta_abs * P (eta_abs the
+ * cancellation-free magnitude of the information mean, with increments
+ * |k lam_v v| and the forget gate f = a P_{t-1} / Ppred; |mu| <= mu_abs), and
+ * per channel the final state lam_T = 1 / P_T, eta_T = mu_T / P_T.
+ */
+static void mixer_channel(const double *k, const double *v, const double *lv,
+                          const double *q, double a, double p, double lam0,
+                          double eta0, double *out, double *var, double *mu_abs,
+                          double *lamT, double *etaT, int64_t T, int64_t stride)
+{
+    double P = 1.0 / lam0;
+    double mu = eta0 / lam0;
+    double mag = fabs(eta0);
+
+    for (int64_t t = 0; t < T; ++t) {
+        const int64_t i = t * stride;
+        const double kt = k[i];
+        const double Ppred = a * a * P + p;
+        const double mupred = a * mu;
+        const double f = a * P / Ppred;
+
+        /* S = (k^2 Ppred + 1/lam_v) * lam_v, so K = Ppred k lam_v / S */
+        const double S = 1.0 + kt * kt * lv[i] * Ppred;
+        const double K = Ppred * kt * lv[i] / S;
+        mu = mupred + K * (v[i] - kt * mupred);
+        P = Ppred / S;
+
+        mag = f * mag + fabs(kt * lv[i] * v[i]);
+
+        out[i] = q[i] * mu;
+        var[i] = P;
+        mu_abs[i] = mag * P;
+    }
+    *lamT = 1.0 / P;
+    *etaT = mu / P;
+}
+
+/*
+ * k, v, lv, q: [B,H,T,D]; a, p: [H,D]; lam0, eta0: [B,H,D];
+ * out, var, mu_abs: [B,H,T,D]; lamT, etaT: [B,H,D].  Returns 0 or -1.
+ */
+int kla_oracle_mixer(const double *k, const double *v, const double *lv,
+                     const double *q, const double *a, const double *p,
+                     const double *lam0, const double *eta0, double *out,
+                     double *var, double *mu_abs, double *lamT, double *etaT,
+                     int64_t B, int64_t H, int64_t T, int64_t D, int nthreads)
+{
+    if (B < 0 || H < 0 || T < 0 || D < 0)
+        return -1;
+    const int64_t channels = B * H * D;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t c = 0; c < channels; ++c) {
+        const int64_t slab = c / D;
+        const int64_t d = c % D;
+        const int64_t hd = (slab % H) * D + d;
+        const int64_t base = slab * T * D + d;
+        mixer_channel(k + base, v + base, lv + base, q + base, a[hd], p[hd],
+                      lam0[c], eta0[c], out + base, var + base, mu_abs + base,
+                      lamT + c, etaT + c, T, D);
+    }
+    return 0;
 }

@@ -44,6 +44,8 @@ class OracleLibrary:
         lib.kla_oracle_scan.restype = ctypes.c_int
         lib.kla_oracle_scan_bwd.argtypes = [dp] * 20 + [ctypes.c_int64] * 4 + [ctypes.c_int]
         lib.kla_oracle_scan_bwd.restype = ctypes.c_int
+        lib.kla_oracle_mixer.argtypes = [dp] * 13 + [ctypes.c_int64] * 4 + [ctypes.c_int]
+        lib.kla_oracle_mixer.restype = ctypes.c_int
         lib.kla_oracle_threads.argtypes = [ctypes.c_int]
         lib.kla_oracle_threads.restype = ctypes.c_int
         self._lib = lib
@@ -109,6 +111,34 @@ class OracleLibrary:
         return grads, mags
 
 
+    def mixer(self, k, v, lam_v, q, a, p, lam0=None, eta0=None, nthreads: int | None = None):
+        """Runs the float64 fused-mixer filter.
+
+        k, v, lam_v, q: [B, H, T, D]; a, p: [H, D]; lam0, eta0: [B, H, D]
+        (None: 1 and 0).  Returns a dict: out (q times the posterior mean),
+        var (posterior variance), mu_abs (a bound on |mean|), [B, H, T, D];
+        lam_T, eta_T (final precision and information mean), [B, H, D].
+        """
+        k = _as_f64(k)
+        if k.ndim != 4:
+            raise ValueError("token inputs must be [B, H, T, D]")
+        B, H, T, D = k.shape
+        shape = (B, H, T, D)
+        v, lam_v, q = (_as_f64(x, shape) for x in (v, lam_v, q))
+        a, p = (_as_f64(x, (H, D)) for x in (a, p))
+        lam0 = _as_f64(np.ones((B, H, D)) if lam0 is None else lam0, (B, H, D))
+        eta0 = _as_f64(np.zeros((B, H, D)) if eta0 is None else eta0, (B, H, D))
+        res = {n: np.empty(shape) for n in ("out", "var", "mu_abs")}
+        res["lam_T"], res["eta_T"] = np.empty((B, H, D)), np.empty((B, H, D))
+        rc = self._lib.kla_oracle_mixer(
+            _ptr(k), _ptr(v), _ptr(lam_v), _ptr(q), _ptr(a), _ptr(p), _ptr(lam0), _ptr(eta0),
+            _ptr(res["out"]), _ptr(res["var"]), _ptr(res["mu_abs"]), _ptr(res["lam_T"]),
+            _ptr(res["eta_T"]), B, H, T, D, int(nthreads or 0))
+        if rc != 0:
+            raise ValueError("oracle rejected the sizes")
+        return res
+
+
 def _as_f64(x, shape=None):
     if hasattr(x, "detach"):  # a torch tensor: copy to host, upcast exactly
         x = x.detach().to("cpu")
@@ -146,6 +176,11 @@ def oracle_threads(nthreads: int | None = None) -> int:
 def oracle_scan(a, p, phi, b, lam0=None, eta0=None, nthreads: int | None = None):
     """The float64 oracle; see ``OracleLibrary.scan``."""
     return _library().scan(a, p, phi, b, lam0, eta0, nthreads)
+
+
+def oracle_mixer(k, v, lam_v, q, a, p, lam0=None, eta0=None, nthreads: int | None = None):
+    """The float64 fused-mixer oracle; see ``OracleLibrary.mixer``."""
+    return _library().mixer(k, v, lam_v, q, a, p, lam0, eta0, nthreads)
 
 
 def oracle_scan_bwd(a, p, phi, b, lam0, eta0, g_lam, g_eta, nthreads: int | None = None):

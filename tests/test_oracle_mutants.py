@@ -98,3 +98,48 @@ def test_bwd_mutant_is_caught(name, tmp_path):
         except (AssertionError, FloatingPointError, ValueError, ZeroDivisionError) as e:
             caught.append((pin.__name__, str(e)[:80]))
     assert caught, "no pin caught mutant %s" % name
+
+
+import oracle_mixer_pins  # noqa: E402
+
+MIXER_MUTANTS = {
+    "mixer-gain-without-operator": ("const double K = Ppred * kt * lv[i] / S;",
+                                    "const double K = Ppred * lv[i] / S;"),
+    "mixer-innovation-ignores-operator": ("(v[i] - kt * mupred)", "(v[i] - mupred)"),
+    "mixer-precision-linear-in-operator": ("1.0 + kt * kt * lv[i] * Ppred",
+                                           "1.0 + kt * lv[i] * Ppred"),
+    "mixer-readout-without-q": ("out[i] = q[i] * mu;", "out[i] = mu;"),
+    "mixer-variance-not-updated": ("mu = mupred + K * (v[i] - kt * mupred);\n        P = Ppred / S;",
+                                   "mu = mupred + K * (v[i] - kt * mupred);\n        P = Ppred;"),
+    "mixer-decay-not-squared": ("const double Ppred = a * a * P + p;",
+                                "const double Ppred = a * P + p;"),
+    "mixer-noise-dropped": ("const double Ppred = a * a * P + p;",
+                            "const double Ppred = a * a * P;"),
+    "mixer-final-precision-as-variance": ("*lamT = 1.0 / P;", "*lamT = P;"),
+    "mixer-signed-magnitude": ("fabs(kt * lv[i] * v[i])", "(kt * lv[i] * v[i])"),
+    "mixer-wrong-channel-gates": ("(slab % H) * D + d", "(slab / H) * D + d"),
+    "mixer-variance-before-update": ("var[i] = P;", "var[i] = Ppred;"),
+    "mixer-prior-mean-ignored": ("    double mu = eta0 / lam0;\n    double mag = fabs(eta0);\n\n    for (int64_t t = 0; t < T; ++t) {\n        const int64_t i = t * stride;\n        const double kt",
+                                 "    double mu = 0.0;\n    double mag = fabs(eta0);\n\n    for (int64_t t = 0; t < T; ++t) {\n        const int64_t i = t * stride;\n        const double kt"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MIXER_MUTANTS))
+def test_mixer_mutant_is_caught(name, tmp_path):
+    old, new = MIXER_MUTANTS[name]
+    src = open(SOURCE).read()
+    assert src.count(old) == 1, "mutation site not unique: %r" % old
+    mutant_src = tmp_path / "mutant.c"
+    mutant_src.write_text(src.replace(old, new, 1))
+    lib = OracleLibrary(build_oracle(str(tmp_path / "libmutant.so"), str(mutant_src)))
+
+    def mixer(k, v, lam_v, q, a, p, lam0, eta0):
+        return lib.mixer(k, v, lam_v, q, a, p, lam0, eta0)
+
+    caught = []
+    for pin in oracle_mixer_pins.ALL_MIXER_PINS:
+        try:
+            pin(mixer)
+        except (AssertionError, FloatingPointError, ValueError, ZeroDivisionError) as e:
+            caught.append((pin.__name__, str(e)[:80]))
+    assert caught, "no pin caught mutant %s" % name

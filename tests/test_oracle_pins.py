@@ -65,3 +65,12 @@ from oracle import oracle_scan_bwd  # noqa: E402
 @pytest.mark.parametrize("pin", oracle_bwd_pins.ALL_BWD_PINS, ids=lambda f: f.__name__)
 def test_bwd_pin(pin):
     pin(oracle_scan_bwd, scan)
+
+
+import oracle_mixer_pins  # noqa: E402
+
+
+@pytest.mark.parametrize("pin", oracle_mixer_pins.ALL_MIXER_PINS, ids=lambda f: f.__name__)
+def test_mixer_pin(pin):
+    from oracle import oracle_mixer
+    pin(oracle_mixer)

@@ -30,16 +30,37 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
 CSRC = os.path.join(ROOT, "linear_attention_sequence_kla_amd", "csrc")
 KERNEL_SOURCES = {"fwd": ("kla_scan_fwd.hip", "kla_lookback.h", "kla_internal.h"),
                   "bwd": ("kla_scan_bwd.hip", "kla_lookback.h", "kla_internal.h"),
-                  "decode": ("kla_decode.hip", "kla_lookback.h", "kla_internal.h")}
+                  "decode": ("kla_decode.hip", "kla_lookback.h", "kla_internal.h"),
+                  "mixer": ("kla_scan_fwd.hip", "kla_lookback.h", "kla_internal.h")}
 KERNEL_NAMES = {"fwd": "kla_scan_kernel", "bwd": "kla_scan_bwd_kernel",
-                "decode": "kla_decode_kernel"}
+                "decode": "kla_decode_kernel", "mixer": "kla_scan_kernel"}
+# the forward kernel template's last parameter selects the fused-mixer mode
+KERNEL_SUFFIX = {"fwd": ", false>", "mixer": ", true>"}
+PROFILE_NAMES = {"fwd": "kla_scan_kernel", "bwd": "kla_scan_bwd_kernel",
+                 "decode": "kla_decode_kernel", "mixer": "kla_scan_kernel_mixer"}
+
+
+def is_kernel(name: str, direction: str) -> bool:
+    """Whether a rocprofv3 kernel name is the kernel a direction times."""
+    return (name.startswith("void kla::(anonymous namespace)::%s<" % KERNEL_NAMES[direction])
+            and KERNEL_SUFFIX.get(direction, ">") in name)
+
+
+def _code_only(text: str) -> str:
+    """Source text without comments and blank lines (what the compiler sees)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
 
 
 def kernel_hash(direction: str = "fwd") -> str:
+    """Hash of the code (comments excluded) of the sources a direction's kernel
+    is built from; counter records taken from other code do not apply."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[direction]:
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(CSRC, name)) as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
@@ -52,11 +73,13 @@ def bytes_per_element(dtype: str, direction: str = "fwd") -> int:
         return 4 * gate + 2 * 4
     if direction == "decode":  # 4 gates, state read and written in place
         return 4 * gate + 2 * 4 + 2 * 4
+    if direction == "mixer":  # k, v, lam_v, q read; readout and variance written
+        return 4 * gate + 2 * 4
     return 2 * gate + 4 * 4 + 4 * 4
 
 
 def traffic_path(workload_key: int, direction: str) -> str:
-    suffix = "" if direction == "fwd" else "_bwd"
+    suffix = {"fwd": "", "bwd": "_bwd", "mixer": "_mixer"}.get(direction, "_" + direction)
     return os.path.join(ROOT, "profiles", "traffic_workload%d%s.json" % (workload_key, suffix))
 
 
@@ -73,14 +96,14 @@ def load_traffic(workload_key: int, direction: str = "fwd"):
     return rec.get("hbm_bytes_per_launch")
 
 
-def _counter_kib(path: str, counter: str, kernel_prefix: str):
+def _counter_kib(path: str, counter: str, match):
     """Mean per-dispatch value (KiB) of a rocprofv3 --pmc counter for kernels
-    whose name starts with kernel_prefix, and the number of dispatches."""
+    whose name satisfies match(name), and the number of dispatches."""
     import csv
     vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
-            if r["Counter_Name"] == counter and r["Kernel_Name"].startswith(kernel_prefix)]
+            if r["Counter_Name"] == counter and match(r["Kernel_Name"])]
     if not vals:
-        raise SystemExit("no %s rows for %r in %s" % (counter, kernel_prefix, path))
+        raise SystemExit("no %s rows in %s" % (counter, path))
     return sum(vals) / len(vals), len(vals)
 
 
@@ -90,19 +113,24 @@ def summarize_counters(args):
     FETCH_SIZE and WRITE_SIZE runs, and the same two counters on a plain
     device copy of known size (the scale factors)."""
     import csv
-    from kla_inputs import WORKLOADS
-    w = WORKLOADS[args.workload]
     d = args.direction
-    scan = "void kla::(anonymous namespace)::%s<" % KERNEL_NAMES[d]
-    stats = [r for r in csv.DictReader(open(args.trace)) if r["Name"].startswith(scan)]
+    w = workloads_for(d)[args.workload]
+
+    def scan(name):
+        return is_kernel(name, d)
+
+    def copy(name):
+        return name.startswith("__amd_rocclr_copyBuffer")
+
+    stats = [r for r in csv.DictReader(open(args.trace)) if scan(r["Name"])]
     if len(stats) != 1:
         raise SystemExit("expected one scan kernel row in %s" % args.trace)
     st = stats[0]
     fetch, n_f = _counter_kib(args.fetch, "FETCH_SIZE", scan)
     write, n_w = _counter_kib(args.write, "WRITE_SIZE", scan)
     copy_bytes = args.copy_mib << 20
-    cf, _ = _counter_kib(args.copy_fetch, "FETCH_SIZE", "__amd_rocclr_copyBuffer")
-    cw, _ = _counter_kib(args.copy_write, "WRITE_SIZE", "__amd_rocclr_copyBuffer")
+    cf, _ = _counter_kib(args.copy_fetch, "FETCH_SIZE", copy)
+    cw, _ = _counter_kib(args.copy_write, "WRITE_SIZE", copy)
     f_fetch = copy_bytes / (cf * 1024.0)
     f_write = copy_bytes / (cw * 1024.0)
     traffic = fetch * 1024.0 * f_fetch + write * 1024.0 * f_write
@@ -119,9 +147,9 @@ def summarize_counters(args):
     with open(traffic_path(args.workload, d), "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
-    md = os.path.join(ROOT, "profiles", "%s_%s.md" % (KERNEL_NAMES[d], w.name))
+    md = os.path.join(ROOT, "profiles", "%s_%s.md" % (PROFILE_NAMES[d], w.name))
     with open(md, "w") as f:
-        f.write("# %s on %s\n\n" % (KERNEL_NAMES[d], w.describe()))
+        f.write("# %s on %s\n\n" % (PROFILE_NAMES[d], w.describe()))
         f.write("Kernel: `%s`  (source sha256/16 `%s`)\n\n" % (st["Name"], kernel_hash(d)))
         f.write("## Kernel trace (rocprofv3 --kernel-trace --stats)\n\n")
         f.write("| calls | average ns | min ns | max ns |\n|---|---|---|---|\n")
@@ -143,6 +171,11 @@ def summarize_counters(args):
         f.write("```\n")
     print(md)
     return 0
+
+
+def workloads_for(direction: str):
+    from kla_inputs import MIXER_WORKLOADS, WORKLOADS
+    return MIXER_WORKLOADS if direction == "mixer" else WORKLOADS
 
 
 def cpu_baseline(w, g_dev, budget_s: float = 10.0):
@@ -184,9 +217,10 @@ def main(argv=None):
     ap.add_argument("--workload", type=int, default=1,
                     help="0..4; the headline is 1 (small-LM layer)")
     ap.add_argument("--sets", type=int, default=2, help="input/output sets to rotate")
-    ap.add_argument("--direction", choices=("fwd", "bwd", "decode"), default="fwd",
+    ap.add_argument("--direction", choices=("fwd", "bwd", "decode", "mixer"), default="fwd",
                     help="fwd: kla_scan_fwd (the headline); bwd: kla_scan_bwd; decode: "
-                         "kla_decode_step on one token of every channel of the workload")
+                         "kla_decode_step on one token of every channel of the workload; "
+                         "mixer: kla_mixer_fwd on the mixer workload of the same key")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="launch the timed steps one by one instead of replaying them "
@@ -224,13 +258,13 @@ def main(argv=None):
         print(json.dumps({"copy_calibration_bytes": n * 4, "launches": max(1, args.steps)}))
         return 0
 
-    from kla_inputs import WORKLOADS, make_workload
+    from kla_inputs import make_mixer_workload, make_workload
     from linear_attention_sequence_kla_amd import (
-        bwd_workspace_size, decode_step, get_workspace, scan_bwd, scan_fwd, workspace_health,
-        workspace_size)
+        bwd_workspace_size, decode_step, get_workspace, mixer_fwd, scan_bwd, scan_fwd,
+        workspace_health, workspace_size)
 
-    w = WORKLOADS[args.workload]
     d = args.direction
+    w = workloads_for(d)[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
@@ -238,7 +272,8 @@ def main(argv=None):
                            bwd_workspace_size(*w.shape, TORCH_DTYPE[w.dtype])), dev, stream)
     sets = []
     for k in range(args.sets if d != "decode" else 0):
-        g = make_workload(args.workload, device=dev, seed=w.seed + 1000 * k)
+        make = make_mixer_workload if d == "mixer" else make_workload
+        g = make(args.workload, device=dev, seed=w.seed + 1000 * k)
         lam = torch.empty(w.shape, dtype=torch.float32, device=dev)
         eta = torch.empty(w.shape, dtype=torch.float32, device=dev)
         if d == "bwd":
@@ -269,6 +304,9 @@ def main(argv=None):
         elif d == "fwd":
             scan_fwd(g["a"], g["p"], g["phi"], g["b"], g["lam0"], g["eta0"], out=out,
                      workspace=ws)
+        elif d == "mixer":
+            mixer_fwd(g["k"], g["v"], g["lam_v"], g["q"], g["a"], g["p"], g["lam0"], g["eta0"],
+                      out=out[0], var=out[1], workspace=ws)
         else:
             scan_bwd(g["a"], g["p"], out[0], out[1], g["g_lam"], g["g_eta"], g["lam0"],
                      g["eta0"], workspace=ws, out=grads)
@@ -342,6 +380,9 @@ def main(argv=None):
     }
     if d == "bwd":
         rec["metric"] = "KLA backward scan elements (B*H*T*D)/s and achieved HBM GB/s vs peak"
+    if d == "mixer":
+        rec["metric"] = ("KLA fused mixer elements (B*H*T*D)/s and achieved HBM GB/s vs peak "
+                         "(gates, scan, readout and variance in one pass)")
     if d == "decode":
         rec["metric"] = "KLA decode step channel updates (B*H*D)/s, one token per step"
         rec["config"]["elements"] = n

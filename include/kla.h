@@ -170,6 +170,50 @@ KLA_API kla_status kla_decode_step(const void *a, const void *p, const void *phi
                                    float *lam, float *eta, int64_t n_channels, void *stream);
 
 /*
+ * Fused KLA mixer forward: gate production, scan and readout in one pass.
+ *
+ * A KLA mixer channel observes its token value through an observation
+ * operator k with a token-dependent value precision lam_v, under a state decay
+ * a and process noise p that do not depend on the token (Pith review of arXiv
+ * 2602.10743, "Circularity check": the update adds k^2 lam_v to the
+ * precision; "Axiom & Free-Parameter Ledger": OU decay a learned and
+ * time-invariant, process-noise scale p learned, value precision and the
+ * observation/readout operators k, q produced from the input).  Per channel
+ * (b, h, d) and token t:
+ *
+ *     phi_t = k_t^2 lam_v_t,   b_t = k_t lam_v_t v_t           (gates)
+ *     (lam_t, eta_t) = the kla_scan_fwd step with a_t = a[h, d], p_t = p[h, d]
+ *     out_t = q_t eta_t / lam_t   (readout of the posterior mean)
+ *     var_t = 1 / lam_t           (posterior variance)
+ *
+ * i.e. the Kalman filter of x_t = a x_{t-1} + w_t (Var w_t = p),
+ * v_t = k_t x_t + e_t (precision of e_t = lam_v_t), read out as q_t times the
+ * posterior mean.  The gate tensors never exist in memory.  The discretised
+ * OU decay (a = exp(-A delta)) is the caller's.
+ *
+ *   k, v, lam_v, q  device pointers, [B, H, T, D] of in_dtype; lam_v >= 0.
+ *   a, p            device pointers, [H, D] float32; a > 0, p >= 0.
+ *   lam0, eta0      as for kla_scan_fwd (NULL: 1 and 0).
+ *   out             device pointer, [B, H, T, D] float32, written.
+ *   var             device pointer, [B, H, T, D] float32, written; may be NULL.
+ *   lam_T, eta_T    device pointers, [B, H, D] float32: the state after the
+ *                   last token (pass it as lam0/eta0 of a following call);
+ *                   both NULL or both given.
+ *   workspace       kla_mixer_fwd_workspace_size bytes, same contract as for
+ *                   kla_scan_fwd (one workspace serves both entry points).
+ * Errors, stream semantics and the overflow rule as for kla_scan_fwd.
+ */
+KLA_API size_t kla_mixer_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int64_t D,
+                                            kla_dtype in_dtype);
+KLA_API kla_status kla_mixer_fwd(const void *k, const void *v, const void *lam_v,
+                                 const void *q, kla_dtype in_dtype,
+                                 const float *a, const float *p,
+                                 const float *lam0, const float *eta0,
+                                 float *out, float *var, float *lam_T, float *eta_T,
+                                 int64_t B, int64_t H, int64_t T, int64_t D,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Reads the workspace's health word after the calls that used it have
  * completed (it synchronizes `stream`).  *flags_out is 0 when every call so
  * far ran normally; bit 0 is set if a chunk gave up waiting for the carry of

@@ -178,11 +178,11 @@ kla_status kla_scan_fwd(const void* a, const void* p, const void* phi, const voi
                             {workspace, pl.ws.bytes, "workspace", true}};
     if ((st = check_overlaps(bufs, 9)) != KLA_OK) return st;
 
-    kla::FwdArgs args;
-    args.a = a;
-    args.p = p;
-    args.phi = phi;
-    args.b = b;
+    kla::FwdArgs args = {};
+    args.in[0] = a;
+    args.in[1] = p;
+    args.in[2] = phi;
+    args.in[3] = b;
     args.lam0 = lam0;
     args.eta0 = eta0;
     args.lam = lam;
@@ -193,9 +193,83 @@ kla_status kla_scan_fwd(const void* a, const void* p, const void* phi, const voi
     args.G = pl.G;
     args.n_chunks = pl.n_chunks;
     args.n_tiles = pl.n_tiles;
+    args.HD = H * D;
     args.ws = kla::workspace_view(workspace, pl.ws);
     const hipError_t err =
-        kla::launch_scan_fwd(args, in_dtype, static_cast<hipStream_t>(stream));
+        kla::launch_scan_fwd(args, in_dtype, false, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(KLA_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
+    return KLA_OK;
+}
+
+size_t kla_mixer_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int64_t D,
+                                    kla_dtype in_dtype) {
+    return kla_scan_fwd_workspace_size(B, H, T, D, in_dtype);
+}
+
+kla_status kla_mixer_fwd(const void* k, const void* v, const void* lam_v, const void* q,
+                         kla_dtype in_dtype, const float* a, const float* p, const float* lam0,
+                         const float* eta0, float* out, float* var, float* lam_T, float* eta_T,
+                         int64_t B, int64_t H, int64_t T, int64_t D, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    Plan pl;
+    bool empty = false;
+    kla_status st = common_checks(B, H, T, D, in_dtype, kla::kFwdRows, kla::kFwdWaves,
+                                  kla::kFwdMatrixWords, kla::kFwdStateWords, &pl, &empty);
+    if (st != KLA_OK || empty) return st;
+
+    const void* ins[4] = {k, v, lam_v, q};
+    const char* names[4] = {"k", "v", "lam_v", "q"};
+    const size_t esz = in_dtype == KLA_DTYPE_F32 ? 4 : 2;
+    for (int i = 0; i < 4; ++i) {
+        if (!ins[i]) return fail(KLA_ERR_INVALID_ARG, "%s is NULL", names[i]);
+        if (misaligned(ins[i], esz))
+            return fail(KLA_ERR_UNSUPPORTED, "%s is not %zu-byte aligned", names[i], esz);
+    }
+    if (!a || !p) return fail(KLA_ERR_INVALID_ARG, "%s is NULL", a ? "p" : "a");
+    if (!out) return fail(KLA_ERR_INVALID_ARG, "out is NULL");
+    if (!lam_T != !eta_T)
+        return fail(KLA_ERR_INVALID_ARG, "lam_T and eta_T must both be given or both be NULL");
+    const void* f32s[9] = {a, p, lam0, eta0, out, var, lam_T, eta_T, nullptr};
+    for (int i = 0; i < 8; ++i)
+        if (f32s[i] && misaligned(f32s[i], 4))
+            return fail(KLA_ERR_UNSUPPORTED, "float32 arguments must be 4-byte aligned");
+    if ((st = check_workspace(workspace, workspace_bytes, pl)) != KLA_OK) return st;
+
+    const size_t in_bytes = size_t(pl.N) * esz, out_bytes = size_t(pl.N) * 4;
+    const size_t st_bytes = size_t(pl.C) * 4, ch_bytes = size_t(H * D) * 4;
+    const Buffer bufs[14] = {{k, in_bytes, "k", false},           {v, in_bytes, "v", false},
+                             {lam_v, in_bytes, "lam_v", false},   {q, in_bytes, "q", false},
+                             {a, ch_bytes, "a", false},           {p, ch_bytes, "p", false},
+                             {lam0, st_bytes, "lam0", false},     {eta0, st_bytes, "eta0", false},
+                             {out, out_bytes, "out", true},       {var, out_bytes, "var", true},
+                             {lam_T, st_bytes, "lam_T", true},    {eta_T, st_bytes, "eta_T", true},
+                             {workspace, pl.ws.bytes, "workspace", true},
+                             {nullptr, 0, "", false}};
+    if ((st = check_overlaps(bufs, 13)) != KLA_OK) return st;
+
+    kla::FwdArgs args = {};
+    args.in[0] = k;
+    args.in[1] = v;
+    args.in[2] = lam_v;
+    args.in[3] = q;
+    args.lam0 = lam0;
+    args.eta0 = eta0;
+    args.lam = out;
+    args.eta = var;
+    args.a_ch = a;
+    args.p_ch = p;
+    args.lam_T = lam_T;
+    args.eta_T = eta_T;
+    args.T = T;
+    args.D = D;
+    args.C = pl.C;
+    args.G = pl.G;
+    args.n_chunks = pl.n_chunks;
+    args.n_tiles = pl.n_tiles;
+    args.HD = H * D;
+    args.ws = kla::workspace_view(workspace, pl.ws);
+    const hipError_t err =
+        kla::launch_scan_fwd(args, in_dtype, true, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return fail(KLA_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
     return KLA_OK;
 }

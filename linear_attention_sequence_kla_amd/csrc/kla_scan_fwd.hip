@@ -33,6 +33,13 @@
 //     matrices of the waves before it, then replays its rows sequentially from
 //     on-chip data, writing lam and eta.
 //
+// Mixer mode (the same kernel with Mixer = true) is the fused KLA mixer: the
+// inputs are the token tensors k, v, lam_v, q and per-channel gates (a, p);
+// phi = k^2 lam_v and b = k lam_v v are formed on the fly (token_gates), and
+// the replay writes the readout q * eta / lam = q * Y / X and the variance
+// 1 / lam = Z / X instead of lam and eta, so no gate or state tensor crosses
+// HBM.
+//
 // Arithmetic is float64 for everything carried (chunk matrices, states): the
 // exact precision can reach 1e88 and the information mean 1e-51 on hard gates,
 // beyond float32's exponent range, and on gfx950 a float64 FMA issues at the
@@ -124,8 +131,32 @@ __device__ inline Lift load_lift(double* rec, int lane) {
     return n;
 }
 
-template <typename In, int L, int W>
-__global__ __launch_bounds__(W * kWave) void kla_scan_kernel(FwdArgs g) {
+// The float64 gates (a, p, phi, b) of one token.  Scan mode reads them from
+// the four input rows.  Mixer mode makes them from the token inputs (k, v,
+// lam_v, q) and the channel's (a, p): the observation v = k x + noise of
+// precision lam_v adds phi = k^2 lam_v to the precision and b = k lam_v v to
+// the information mean (the information-form update of the Pith review,
+// "Circularity check", with the observation operator k of the ledger).  Both
+// passes over a row evaluate the same expressions, so they see equal gates.
+template <bool Mixer>
+__device__ inline void token_gates(float x0, float x1, float x2, float x3, double ac, double pc,
+                                   double& a, double& p, double& ph, double& b) {
+    if constexpr (Mixer) {
+        const double k = x0, lv = x2;
+        a = ac;
+        p = pc;
+        ph = k * k * lv;
+        b = k * lv * double(x1);
+    } else {
+        a = x0;
+        p = x1;
+        ph = x2;
+        b = x3;
+    }
+}
+
+template <typename In, int L, int W, bool Mixer>
+__global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(3))) void kla_scan_kernel(FwdArgs g) {
     __shared__ double s_lift[W][7][kWave];
     __shared__ double s_carry[W][2][kWave];
     static_assert(kFwdMatrixWords == 7 && kFwdStateWords == 2, "record layout");
@@ -146,10 +177,17 @@ __global__ __launch_bounds__(W * kWave) void kla_scan_kernel(FwdArgs g) {
         const LaneMap lm = lane_map(grp, t0, lane, g.T, g.D, g.C);
         const uint32_t in_row = uint32_t(g.D * sizeof(In));
         const uint32_t out_row = uint32_t(g.D * sizeof(float));
-        const char* pa = static_cast<const char*>(g.a) + lm.e0 * int64_t(sizeof(In));
-        const char* pp = static_cast<const char*>(g.p) + lm.e0 * int64_t(sizeof(In));
-        const char* pf = static_cast<const char*>(g.phi) + lm.e0 * int64_t(sizeof(In));
-        const char* pb = static_cast<const char*>(g.b) + lm.e0 * int64_t(sizeof(In));
+        const char* pa = static_cast<const char*>(g.in[0]) + lm.e0 * int64_t(sizeof(In));
+        const char* pp = static_cast<const char*>(g.in[1]) + lm.e0 * int64_t(sizeof(In));
+        const char* pf = static_cast<const char*>(g.in[2]) + lm.e0 * int64_t(sizeof(In));
+        const char* pb = static_cast<const char*>(g.in[3]) + lm.e0 * int64_t(sizeof(In));
+        // mixer mode: the channel's time-invariant gates
+        double ac = 1.0, pc = 0.0;
+        if constexpr (Mixer) {
+            const int64_t hd = lm.qc % g.HD;
+            ac = g.a_ch[hd];
+            pc = g.p_ch[hd];
+        }
 
         // ---- load the wave's rows; rows past T repeat the last row ----
         // (their values only reach chunk matrices that no valid row uses)
@@ -183,7 +221,8 @@ __global__ __launch_bounds__(W * kWave) void kla_scan_kernel(FwdArgs g) {
             double f = 1.0;
 #pragma unroll
             for (int i = 0; i < L; ++i) {
-                const double a = ra[i], p = rp[i], ph = rf[i], bb = rb[i];
+                double a, p, ph, bb;
+                token_gates<Mixer>(ra[i], rp[i], rf[i], rb[i], ac, pc, a, p, ph, bb);
                 const double a2 = a * a;
                 double zn = fma(p, x1, a2 * z1);
                 x1 = fma(ph, zn, x1);
@@ -276,17 +315,34 @@ __global__ __launch_bounds__(W * kWave) void kla_scan_kernel(FwdArgs g) {
 #pragma unroll
             for (int i = 0; i < L; ++i) {
                 if (i >= nr) continue;  // (uniform; keeps the loop fully unrolled)
-                const double a = ra[i], p = rp[i], ph = rf[i], bb = rb[i];
+                double a, p, ph, bb;
+                token_gates<Mixer>(ra[i], rp[i], rf[i], rb[i], ac, pc, a, p, ph, bb);
                 const double zn = fma(p, X, (a * a) * Z);
                 X = fma(ph, zn, X);
                 Y = fma(bb, zn, a * Y);
                 Z = zn;
-                const double r = recip(Z);
-                if (lm.valid) {
-                    const uint32_t off =
-                        lm.lane_el * uint32_t(sizeof(float)) + uint32_t(i) * out_row;
-                    __builtin_nontemporal_store(float(X * r), reinterpret_cast<float*>(olam + off));
-                    __builtin_nontemporal_store(float(Y * r), reinterpret_cast<float*>(oeta + off));
+                const uint32_t off = lm.lane_el * uint32_t(sizeof(float)) + uint32_t(i) * out_row;
+                if constexpr (Mixer) {
+                    // readout: mean eta / lam = Y / X scaled by q, variance 1 / lam = Z / X
+                    const double r = recip(X);
+                    if (lm.valid) {
+                        __builtin_nontemporal_store(float(double(rb[i]) * (Y * r)),
+                                                    reinterpret_cast<float*>(olam + off));
+                        if (g.eta)
+                            __builtin_nontemporal_store(float(Z * r),
+                                                        reinterpret_cast<float*>(oeta + off));
+                    }
+                    if (g.lam_T && t0 + i == g.T - 1 && lm.valid) {
+                        const double rz = recip(Z);
+                        g.lam_T[lm.q] = float(X * rz);
+                        g.eta_T[lm.q] = float(Y * rz);
+                    }
+                } else {
+                    const double r = recip(Z);
+                    if (lm.valid) {
+                        __builtin_nontemporal_store(float(X * r), reinterpret_cast<float*>(olam + off));
+                        __builtin_nontemporal_store(float(Y * r), reinterpret_cast<float*>(oeta + off));
+                    }
                 }
                 if ((i % kRenormEvery) == kRenormEvery - 1) {
                     const int e = renorm_exponent(fmax(fmax(X, fabs(Y)), Z));
@@ -305,14 +361,20 @@ __global__ __launch_bounds__(W * kWave) void kla_scan_kernel(FwdArgs g) {
 
 }  // namespace
 
-hipError_t launch_scan_fwd(const FwdArgs& args, kla_dtype dtype, hipStream_t stream) {
+hipError_t launch_scan_fwd(const FwdArgs& args, kla_dtype dtype, bool mixer, hipStream_t stream) {
     const dim3 grid(unsigned(args.n_tiles)), block(kFwdWaves * kWave);
-    if (dtype == KLA_DTYPE_F32)
-        hipLaunchKernelGGL((kla_scan_kernel<float, kFwdRows, kFwdWaves>), grid, block, 0, stream,
-                           args);
-    else
-        hipLaunchKernelGGL((kla_scan_kernel<uint16_t, kFwdRows, kFwdWaves>), grid, block, 0,
+    if (dtype == KLA_DTYPE_F32 && !mixer)
+        hipLaunchKernelGGL((kla_scan_kernel<float, kFwdRows, kFwdWaves, false>), grid, block, 0,
                            stream, args);
+    else if (!mixer)
+        hipLaunchKernelGGL((kla_scan_kernel<uint16_t, kFwdRows, kFwdWaves, false>), grid, block,
+                           0, stream, args);
+    else if (dtype == KLA_DTYPE_F32)
+        hipLaunchKernelGGL((kla_scan_kernel<float, kFwdRows, kFwdWaves, true>), grid, block, 0,
+                           stream, args);
+    else
+        hipLaunchKernelGGL((kla_scan_kernel<uint16_t, kFwdRows, kFwdWaves, true>), grid, block,
+                           0, stream, args);
     return hipGetLastError();
 }
 

@@ -56,6 +56,11 @@ def library() -> ctypes.CDLL:
         lib.kla_scan_bwd_workspace_size.restype = sz
         lib.kla_scan_bwd.argtypes = [vp, vp, ctypes.c_int] + [vp] * 12 + [i64] * 4 + [vp, sz, vp]
         lib.kla_scan_bwd.restype = ctypes.c_int
+        lib.kla_mixer_fwd_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+        lib.kla_mixer_fwd_workspace_size.restype = sz
+        lib.kla_mixer_fwd.argtypes = [vp, vp, vp, vp, ctypes.c_int] + [vp] * 8 + [i64] * 4 + [
+            vp, sz, vp]
+        lib.kla_mixer_fwd.restype = ctypes.c_int
         lib.kla_decode_step.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, vp, i64, vp]
         lib.kla_decode_step.restype = ctypes.c_int
         lib.kla_workspace_health.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), vp]
@@ -246,6 +251,65 @@ class KLAScan(torch.autograd.Function):
 def kla_scan(a, p, phi, b, lam0=None, eta0=None):
     """Differentiable KLA scan: returns (lam, eta); see KLAScan."""
     return KLAScan.apply(a, p, phi, b, lam0, eta0)
+
+
+def mixer_workspace_size(B: int, H: int, T: int, D: int, dtype=torch.float32) -> int:
+    """Bytes of workspace kla_mixer_fwd needs (0 for an empty problem)."""
+    return int(library().kla_mixer_fwd_workspace_size(B, H, T, D, _DTYPES[dtype]))
+
+
+def mixer_fwd(k: torch.Tensor, v: torch.Tensor, lam_v: torch.Tensor, q: torch.Tensor,
+              a: torch.Tensor, p: torch.Tensor, lam0: torch.Tensor | None = None,
+              eta0: torch.Tensor | None = None, want_var: bool = True,
+              want_state: bool = False, out: torch.Tensor | None = None,
+              var: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Fused KLA mixer forward on the current stream (kla_mixer_fwd).
+
+    k, v, lam_v, q: [B, H, T, D] contiguous, all float32 or all bfloat16 (the
+    observation operator, the value, its precision and the readout operator).
+    a, p: [H, D] float32 state decay and process noise.  lam0, eta0: [B, H, D]
+    float32 (None: 1 and 0).  Returns (out, var, lam_T, eta_T): the readout
+    q * eta / lam, the posterior variance 1 / lam (None unless want_var) and
+    the final state (None unless want_state), float32.
+    """
+    ins = (k, v, lam_v, q)
+    if k.dim() != 4:
+        raise ValueError("token inputs must be [B, H, T, D], got shape %s" % (tuple(k.shape),))
+    for name, t in zip(("k", "v", "lam_v", "q"), ins):
+        if t.shape != k.shape or t.dtype != k.dtype:
+            raise ValueError("%s must match k in shape and dtype" % name)
+        if not t.is_cuda or t.device != k.device or not t.is_contiguous():
+            raise ValueError("%s must be contiguous on k's GPU" % name)
+    if k.dtype not in _DTYPES:
+        raise ValueError("token dtype must be float32 or bfloat16, got %s" % k.dtype)
+    B, H, T, D = k.shape
+    dev = k.device
+    for name, t in (("a", a), ("p", p)):
+        if t is None:
+            raise ValueError("%s is required" % name)
+        _check_f32(name, t, (H, D), dev)
+    for name, t in (("lam0", lam0), ("eta0", eta0)):
+        _check_f32(name, t, (B, H, D), dev)
+    if out is None:
+        out = torch.empty(k.shape, dtype=torch.float32, device=dev)
+    _check_f32("out", out, k.shape, dev)
+    if want_var and var is None:
+        var = torch.empty(k.shape, dtype=torch.float32, device=dev)
+    if not want_var:
+        var = None
+    _check_f32("var", var, k.shape, dev)
+    lam_T = eta_T = None
+    if want_state:
+        lam_T = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+        eta_T = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    if workspace is None:
+        workspace = get_workspace(mixer_workspace_size(B, H, T, D, k.dtype), dev, stream)
+    _check(library().kla_mixer_fwd(
+        _ptr(k), _ptr(v), _ptr(lam_v), _ptr(q), _DTYPES[k.dtype], _ptr(a), _ptr(p), _ptr(lam0),
+        _ptr(eta0), _ptr(out), _ptr(var), _ptr(lam_T), _ptr(eta_T), B, H, T, D, _ptr(workspace),
+        workspace.numel(), ctypes.c_void_p(stream.cuda_stream)))
+    return out, var, lam_T, eta_T
 
 
 def decode_step(a: torch.Tensor, p: torch.Tensor, phi: torch.Tensor, b: torch.Tensor,

@@ -30,7 +30,8 @@ TOL_BF16 = 2e-2  # bf16 gate inputs (oracle runs on the same bf16 values)
 
 def _np(x):
     if hasattr(x, "detach"):
-        return x.detach().to("cpu").numpy()
+        x = x.detach().to("cpu")
+        return (x.double() if x.dtype.is_floating_point else x).numpy()
     return np.asarray(x)
 
 
@@ -112,3 +113,46 @@ def assert_grad_parity(rep: dict, tol: float, what: str = ""):
     for k, v in rep.items():
         if k not in ("nan", "range_violations"):
             assert v <= tol, msg
+
+
+def compare_mixer(out_hat, var_hat, q, out, var, mu_abs) -> dict:
+    """Error report of the fused mixer's fp32 outputs against the float64
+    oracle.  The readout q * mean is a signed quantity that can cancel, so its
+    error is divided by |q| times the cancellation-free magnitude of the mean
+    (floored at 2^-126); where q is 0 the output must be exactly 0.  The
+    variance is positive: plain relative error, floored at 2^-126.  The fp32
+    overflow rule and the NaN rule are those of ``compare``."""
+    out_hat = _np(out_hat).astype(np.float64)
+    q = _np(q).astype(np.float64)
+    out, mu_abs = (np.asarray(x, dtype=np.float64) for x in (out, mu_abs))
+    with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+        out_over = np.isinf(out.astype(np.float32))
+        rep = {"n": int(out.size)}
+        rep["nan"] = int(np.isnan(out_hat).sum())
+        bad = (out_over & (out_hat != np.sign(out) * np.inf)).sum()
+        bad += (~out_over & ~np.isfinite(out_hat)).sum()
+        ok = ~out_over & np.isfinite(out_hat)
+        den = np.abs(q) * np.maximum(mu_abs, TINY)
+        zero_q = den == 0
+        rep["zero_q_nonzero_out"] = int((zero_q & (out_hat != 0)).sum())
+        err = np.abs(out_hat - out) / np.where(zero_q, 1.0, den)
+        rep["out_max_scaled"] = float(err[ok & ~zero_q].max()) if (ok & ~zero_q).any() else 0.0
+        if var_hat is not None:
+            var_hat = _np(var_hat).astype(np.float64)
+            var = np.asarray(var, dtype=np.float64)
+            rep["nan"] += int(np.isnan(var_hat).sum())
+            bad += (~np.isfinite(var_hat)).sum()
+            vok = np.isfinite(var_hat)
+            verr = np.abs(var_hat - var) / np.maximum(var, TINY)
+            rep["var_max_rel"] = float(verr[vok].max()) if vok.any() else 0.0
+        rep["range_violations"] = int(bad)
+    return rep
+
+
+def assert_mixer_parity(rep: dict, tol: float, what: str = ""):
+    msg = "%s %r" % (what, rep)
+    assert rep["nan"] == 0, msg
+    assert rep["range_violations"] == 0, msg
+    assert rep["zero_q_nonzero_out"] == 0, msg
+    assert rep["out_max_scaled"] <= tol, msg
+    assert rep.get("var_max_rel", 0.0) <= tol, msg

@@ -106,3 +106,42 @@ def test_argument_errors_before_launch(lib):
 def test_health_rejects_null(lib):
     out = ctypes.c_uint32(0)
     assert lib.kla_workspace_health(None, ctypes.byref(out), None) == 3
+
+
+def _mixer_call(lib, k=1, a=0x500000, out=0x1000000, var=0x2000000, lam_T=0, eta_T=0,
+                shape=(2, 1, 4, 4), ws=0x4000000, ws_bytes=1 << 20):
+    vp = ctypes.c_void_p
+    B, H, T, D = shape
+    st = lib.kla_mixer_fwd(vp(k * 0x100000), vp(0x200000), vp(0x300000), vp(0x400000), 0,
+                           vp(a), vp(0x600000), None, None, vp(out), vp(var), vp(lam_T),
+                           vp(eta_T), B, H, T, D, vp(ws), ws_bytes, None)
+    return st, lib.kla_last_error_detail().decode()
+
+
+def test_mixer_workspace_matches_scan(lib):
+    for shape in ((1, 1, 256, 16), (8, 16, 2048, 64), (3, 5, 77, 9)):
+        for dt in (0, 1):
+            assert (lib.kla_mixer_fwd_workspace_size(*shape, dt)
+                    == lib.kla_scan_fwd_workspace_size(*shape, dt))
+
+
+def test_mixer_argument_errors_before_launch(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("uses fake device pointers; argument errors are tested on GPUs elsewhere")
+    st, msg = _mixer_call(lib, k=0)
+    assert st == 1 and "k is NULL" in msg
+    st, msg = _mixer_call(lib, a=0)
+    assert st == 1 and "a is NULL" in msg
+    st, msg = _mixer_call(lib, out=0)
+    assert st == 1 and "out is NULL" in msg
+    st, msg = _mixer_call(lib, lam_T=0x3000000)
+    assert st == 1 and "both" in msg
+    st, msg = _mixer_call(lib, var=0x100000)
+    assert st == 1 and "overlaps" in msg
+    st, msg = _mixer_call(lib, lam_T=0x3000000, eta_T=0x3000010)
+    assert st == 1 and "overlaps" in msg
+    st, msg = _mixer_call(lib, ws_bytes=16)
+    assert st == 3 and "needs" in msg
+    st, _ = _mixer_call(lib, k=0, shape=(1, 1, 0, 4))
+    assert st == 0

@@ -1,0 +1,177 @@
+"""GPU parity of the fused KLA mixer (kla_mixer_fwd through the C ABI)
+against the float64 mixer oracle, on the same seeded inputs (kla_inputs'
+mixer recipe).  Bar: kla_metric.compare_mixer within 1e-4 (fp32 inputs) or
+2e-2 (bf16 inputs), no NaN, the overflow rule."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from kla_inputs import (MIXER_WORKLOADS, make_initial_state, make_mixer_inputs,
+                        make_mixer_workload)
+from kla_metric import TOL_BF16, TOL_F32, assert_mixer_parity, compare_mixer
+from oracle import oracle_mixer
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+TOKEN = ("k", "v", "lam_v", "q")
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def run_gpu(g, use_state=True, want_var=True, want_state=False):
+    from linear_attention_sequence_kla_amd import mixer_fwd
+    lam0 = g["lam0"].to(DEV) if use_state else None
+    eta0 = g["eta0"].to(DEV) if use_state else None
+    res = mixer_fwd(*(g[n].to(DEV) for n in TOKEN), g["a"].to(DEV), g["p"].to(DEV), lam0, eta0,
+                    want_var=want_var, want_state=want_state)
+    torch.cuda.synchronize(DEV)
+    return res
+
+
+def health():
+    from linear_attention_sequence_kla_amd import get_workspace, workspace_health
+    return workspace_health(get_workspace(0, DEV, torch.cuda.current_stream(DEV)))
+
+
+def oracle(g, use_state=True):
+    return oracle_mixer(*(g[n] for n in TOKEN), g["a"], g["p"],
+                        g["lam0"] if use_state else None, g["eta0"] if use_state else None)
+
+
+def full_parity(g, tol, what, use_state=True):
+    out, var, _, _ = run_gpu(g, use_state)
+    assert health() == 0, what
+    ref = oracle(g, use_state)
+    rep = compare_mixer(out.cpu(), var.cpu(), g["q"], ref["out"], ref["var"], ref["mu_abs"])
+    _say("%s: %s" % (what, rep))
+    assert_mixer_parity(rep, tol, what)
+    return rep
+
+
+@pytest.mark.parametrize("key", [0, 1])
+def test_mixer_workload_full(key):
+    w = MIXER_WORKLOADS[key]
+    _say("mixer workload %s" % w.describe())
+    full_parity(make_mixer_workload(key), TOL_F32, w.describe())
+
+
+def _sample_channels(C, n, seed):
+    rng = np.random.default_rng(seed)
+    picks = set(rng.choice(C, size=min(n, C), replace=False).tolist())
+    picks.update({0, C - 1, min(63, C - 1), min(64, C - 1)})
+    return np.array(sorted(picks))
+
+
+def _gather(x, D, q):
+    B, H, T, _ = x.shape
+    flat = x.reshape(B * H, T, D)
+    slab = torch.as_tensor(q // D, device=x.device)
+    d = torch.as_tensor(q % D, device=x.device)
+    return flat[slab, :, d].transpose(0, 1).reshape(1, 1, T, len(q)).contiguous()
+
+
+@pytest.mark.parametrize("key", [2, 3])
+def test_mixer_workload_full_size_sampled(key):
+    """The full-size workload in the launch configuration the benchmark
+    times; the oracle checks a sample of channels (whole sequences)."""
+    w = MIXER_WORKLOADS[key]
+    _say("mixer workload %s (full size, sampled channels)" % w.describe())
+    g = make_mixer_inputs(w.shape, w.dtype, w.seed, device=DEV)
+    g["lam0"], g["eta0"] = make_initial_state(w.B, w.H, w.D, random=True, seed=w.seed,
+                                              device=DEV)
+    out, var, lam_T, eta_T = run_gpu(g, want_state=True)
+    assert health() == 0
+    qs = _sample_channels(w.channels, 384, w.seed)
+    sub = {n: _gather(g[n], w.D, qs).cpu() for n in TOKEN}
+    hd = torch.as_tensor(qs % (w.H * w.D))
+    sub["a"] = g["a"].reshape(-1)[hd.to(DEV)].reshape(1, -1).cpu()
+    sub["p"] = g["p"].reshape(-1)[hd.to(DEV)].reshape(1, -1).cpu()
+    qd = torch.as_tensor(qs, device=DEV)
+    sub["lam0"] = g["lam0"].reshape(-1)[qd].reshape(1, 1, -1).cpu()
+    sub["eta0"] = g["eta0"].reshape(-1)[qd].reshape(1, 1, -1).cpu()
+    ref = oracle(sub)
+    rep = compare_mixer(_gather(out, w.D, qs).cpu(), _gather(var, w.D, qs).cpu(), sub["q"],
+                        ref["out"], ref["var"], ref["mu_abs"])
+    _say("%s: %s" % (w.describe(), rep))
+    assert_mixer_parity(rep, TOL_BF16 if w.dtype == "bf16" else TOL_F32, w.describe())
+    lt = lam_T.reshape(-1)[qd].cpu().double().numpy()
+    et = eta_T.reshape(-1)[qd].cpu().double().numpy()
+    assert np.max(np.abs(lt - ref["lam_T"][0, 0]) / ref["lam_T"][0, 0]) < 1e-5
+    assert np.all(np.isfinite(et))
+
+
+SHAPES = [
+    (1, 1, 1, 1), (1, 1, 5, 3), (2, 3, 113, 7), (1, 2, 337, 64), (3, 1, 450, 65),
+    (2, 2, 1000, 33), (1, 1, 2049, 128), (4, 3, 96, 40),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_mixer_shapes(shape):
+    g = make_mixer_inputs(shape, "f32", seed=sum(shape))
+    g["lam0"], g["eta0"] = make_initial_state(shape[0], shape[1], shape[3], random=True,
+                                              seed=sum(shape))
+    full_parity(g, TOL_F32, "shape %s" % (shape,))
+
+
+def test_mixer_bf16_shape():
+    shape = (2, 2, 700, 48)
+    g = make_mixer_inputs(shape, "bf16", seed=5)
+    g["lam0"], g["eta0"] = make_initial_state(2, 2, 48, random=True, seed=5)
+    full_parity(g, TOL_BF16, "bf16 %s" % (shape,))
+
+
+def test_mixer_default_state_and_no_variance():
+    shape = (2, 2, 300, 16)
+    g = make_mixer_inputs(shape, "f32", seed=9)
+    g["lam0"], g["eta0"] = make_initial_state(2, 2, 16)
+    full_parity(g, TOL_F32, "default state", use_state=False)
+    out1, var1, _, _ = run_gpu(g, use_state=False)
+    out2, var2, _, _ = run_gpu(g, use_state=False, want_var=False)
+    assert var2 is None
+    assert torch.equal(out1, out2)
+
+
+def test_mixer_final_state_and_segments():
+    from linear_attention_sequence_kla_amd import mixer_fwd
+    shape = (2, 3, 777, 24)
+    g = make_mixer_inputs(shape, "f32", seed=21)
+    g["lam0"], g["eta0"] = make_initial_state(2, 3, 24, random=True, seed=21)
+    out, var, lam_T, eta_T = run_gpu(g, want_state=True)
+    ref = oracle(g)
+    rel = np.abs(lam_T.cpu().double().numpy() - ref["lam_T"]) / ref["lam_T"]
+    assert rel.max() < TOL_F32
+    mag = ref["mu_abs"][:, :, -1] * ref["lam_T"]
+    err = np.abs(eta_T.cpu().double().numpy() - ref["eta_T"]) / mag
+    assert err.max() < TOL_F32
+    # two calls chained through the final state equal one call
+    s = 300
+    d = {n: g[n].to(DEV) for n in g}
+    o1, v1, l1, e1 = mixer_fwd(*(d[n][:, :, :s].contiguous() for n in TOKEN), d["a"], d["p"],
+                               d["lam0"], d["eta0"], want_state=True)
+    o2, v2, _, _ = mixer_fwd(*(d[n][:, :, s:].contiguous() for n in TOKEN), d["a"], d["p"],
+                             l1, e1)
+    torch.cuda.synchronize(DEV)
+    rep = compare_mixer(torch.cat([o1, o2], 2).cpu(), torch.cat([v1, v2], 2).cpu(), g["q"],
+                        ref["out"], ref["var"], ref["mu_abs"])
+    _say("segments: %s" % rep)
+    assert_mixer_parity(rep, TOL_F32, "segments")
+
+
+def test_mixer_argument_errors_on_device():
+    from linear_attention_sequence_kla_amd import mixer_fwd
+    g = {n: v.to(DEV) for n, v in make_mixer_inputs((1, 2, 8, 4), "f32", seed=1).items()}
+    with pytest.raises(ValueError):
+        mixer_fwd(g["k"], g["v"][:, :, :4].contiguous(), g["lam_v"], g["q"], g["a"], g["p"])
+    with pytest.raises(ValueError):
+        mixer_fwd(g["k"], g["v"], g["lam_v"], g["q"], g["a"][:1].contiguous(), g["p"])
+    with pytest.raises(ValueError):
+        mixer_fwd(g["k"], g["v"], g["lam_v"].double(), g["q"], g["a"], g["p"])
+    with pytest.raises(ValueError):
+        mixer_fwd(g["k"], g["v"], g["lam_v"], g["q"], g["a"], g["p"].double())

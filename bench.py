@@ -31,13 +31,16 @@ CSRC = os.path.join(ROOT, "linear_attention_sequence_kla_amd", "csrc")
 KERNEL_SOURCES = {"fwd": ("kla_scan_fwd.hip", "kla_lookback.h", "kla_internal.h"),
                   "bwd": ("kla_scan_bwd.hip", "kla_lookback.h", "kla_internal.h"),
                   "decode": ("kla_decode.hip", "kla_lookback.h", "kla_internal.h"),
-                  "mixer": ("kla_scan_fwd.hip", "kla_lookback.h", "kla_internal.h")}
+                  "mixer": ("kla_scan_fwd.hip", "kla_lookback.h", "kla_internal.h"),
+                  "lti": ("kla_scan_fwd.hip", "kla_lookback.h", "kla_internal.h")}
 KERNEL_NAMES = {"fwd": "kla_scan_kernel", "bwd": "kla_scan_bwd_kernel",
-                "decode": "kla_decode_kernel", "mixer": "kla_scan_kernel"}
+                "decode": "kla_decode_kernel", "mixer": "kla_scan_kernel",
+                "lti": "kla_scan_kernel"}
 # the forward kernel template's last parameter selects the fused-mixer mode
-KERNEL_SUFFIX = {"fwd": ", false>", "mixer": ", true>"}
+KERNEL_SUFFIX = {"fwd": "Mode)0>", "mixer": "Mode)1>", "lti": "Mode)2>"}
 PROFILE_NAMES = {"fwd": "kla_scan_kernel", "bwd": "kla_scan_bwd_kernel",
-                 "decode": "kla_decode_kernel", "mixer": "kla_scan_kernel_mixer"}
+                 "decode": "kla_decode_kernel", "mixer": "kla_scan_kernel_mixer",
+                 "lti": "kla_scan_kernel_lti"}
 
 
 def is_kernel(name: str, direction: str) -> bool:
@@ -75,11 +78,13 @@ def bytes_per_element(dtype: str, direction: str = "fwd") -> int:
         return 4 * gate + 2 * 4 + 2 * 4
     if direction == "mixer":  # k, v, lam_v, q read; readout and variance written
         return 4 * gate + 2 * 4
+    if direction == "lti":  # b read (gates once per channel); lam, eta written
+        return gate + 2 * 4
     return 2 * gate + 4 * 4 + 4 * 4
 
 
 def traffic_path(workload_key: int, direction: str) -> str:
-    suffix = {"fwd": "", "bwd": "_bwd", "mixer": "_mixer"}.get(direction, "_" + direction)
+    suffix = {"fwd": "", "bwd": "_bwd"}.get(direction, "_" + direction)
     return os.path.join(ROOT, "profiles", "traffic_workload%d%s.json" % (workload_key, suffix))
 
 
@@ -174,8 +179,8 @@ def summarize_counters(args):
 
 
 def workloads_for(direction: str):
-    from kla_inputs import MIXER_WORKLOADS, WORKLOADS
-    return MIXER_WORKLOADS if direction == "mixer" else WORKLOADS
+    from kla_inputs import LTI_WORKLOADS, MIXER_WORKLOADS, WORKLOADS
+    return {"mixer": MIXER_WORKLOADS, "lti": LTI_WORKLOADS}.get(direction, WORKLOADS)
 
 
 def cpu_baseline(w, g_dev, budget_s: float = 10.0):
@@ -217,10 +222,12 @@ def main(argv=None):
     ap.add_argument("--workload", type=int, default=1,
                     help="0..4; the headline is 1 (small-LM layer)")
     ap.add_argument("--sets", type=int, default=2, help="input/output sets to rotate")
-    ap.add_argument("--direction", choices=("fwd", "bwd", "decode", "mixer"), default="fwd",
+    ap.add_argument("--direction", choices=("fwd", "bwd", "decode", "mixer", "lti"),
+                    default="fwd",
                     help="fwd: kla_scan_fwd (the headline); bwd: kla_scan_bwd; decode: "
                          "kla_decode_step on one token of every channel of the workload; "
-                         "mixer: kla_mixer_fwd on the mixer workload of the same key")
+                         "mixer: kla_mixer_fwd on the mixer workload of the same key; "
+                         "lti: kla_scan_lti_fwd on the time-invariant workload of that key")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="launch the timed steps one by one instead of replaying them "
@@ -258,10 +265,10 @@ def main(argv=None):
         print(json.dumps({"copy_calibration_bytes": n * 4, "launches": max(1, args.steps)}))
         return 0
 
-    from kla_inputs import make_mixer_workload, make_workload
+    from kla_inputs import make_lti_workload, make_mixer_workload, make_workload
     from linear_attention_sequence_kla_amd import (
-        bwd_workspace_size, decode_step, get_workspace, mixer_fwd, scan_bwd, scan_fwd,
-        workspace_health, workspace_size)
+        bwd_workspace_size, decode_step, get_workspace, lti_workspace_size, mixer_fwd, scan_bwd,
+        scan_fwd, scan_lti_fwd, workspace_health, workspace_size)
 
     d = args.direction
     w = workloads_for(d)[args.workload]
@@ -269,10 +276,11 @@ def main(argv=None):
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
     ws = get_workspace(max(workspace_size(*w.shape, TORCH_DTYPE[w.dtype]),
-                           bwd_workspace_size(*w.shape, TORCH_DTYPE[w.dtype])), dev, stream)
+                           bwd_workspace_size(*w.shape, TORCH_DTYPE[w.dtype]),
+                           lti_workspace_size(*w.shape, TORCH_DTYPE[w.dtype])), dev, stream)
     sets = []
     for k in range(args.sets if d != "decode" else 0):
-        make = make_mixer_workload if d == "mixer" else make_workload
+        make = {"mixer": make_mixer_workload, "lti": make_lti_workload}.get(d, make_workload)
         g = make(args.workload, device=dev, seed=w.seed + 1000 * k)
         lam = torch.empty(w.shape, dtype=torch.float32, device=dev)
         eta = torch.empty(w.shape, dtype=torch.float32, device=dev)
@@ -304,6 +312,9 @@ def main(argv=None):
         elif d == "fwd":
             scan_fwd(g["a"], g["p"], g["phi"], g["b"], g["lam0"], g["eta0"], out=out,
                      workspace=ws)
+        elif d == "lti":
+            scan_lti_fwd(g["a"], g["p"], g["phi"], g["b"], g["lam0"], g["eta0"], out=out,
+                         workspace=ws)
         elif d == "mixer":
             mixer_fwd(g["k"], g["v"], g["lam_v"], g["q"], g["a"], g["p"], g["lam0"], g["eta0"],
                       out=out[0], var=out[1], workspace=ws)
@@ -380,6 +391,9 @@ def main(argv=None):
     }
     if d == "bwd":
         rec["metric"] = "KLA backward scan elements (B*H*T*D)/s and achieved HBM GB/s vs peak"
+    if d == "lti":
+        rec["metric"] = ("KLA scan with time-invariant gates, elements (B*H*T*D)/s and "
+                         "achieved HBM GB/s vs peak")
     if d == "mixer":
         rec["metric"] = ("KLA fused mixer elements (B*H*T*D)/s and achieved HBM GB/s vs peak "
                          "(gates, scan, readout and variance in one pass)")

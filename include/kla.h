@@ -170,6 +170,36 @@ KLA_API kla_status kla_decode_step(const void *a, const void *p, const void *phi
                                    float *lam, float *eta, int64_t n_channels, void *stream);
 
 /*
+ * Forward KLA scan for time-invariant gates (the linear time-invariant case
+ * of the Pith review of arXiv 2602.10743, minor comment on Theorem 3, whose
+ * convolutional form covers it).
+ *
+ * Same recursion and outputs as kla_scan_fwd, with a_t = a[h, d],
+ * p_t = p[h, d], phi_t = phi[h, d] for every token: only the information b
+ * is per token.  Then lam_t does not depend on the data, and from the
+ * stationary precision lam* (the fixed point of the Moebius map) eta is the
+ * causal convolution of b with the kernel f*^j, f* = a / (a^2 + p lam*).
+ * For a scalar channel that geometric kernel is evaluated exactly by the
+ * first-order recursion, so the library runs the scan with the gates read
+ * once per channel: 12 bytes of HBM traffic per element (f32 b) instead of
+ * 24.  Any initial state is allowed (the transient is exact too).
+ *
+ *   a, p, phi       device pointers, [H, D] float32 (a > 0, p >= 0, phi >= 0).
+ *   b               device pointer, [B, H, T, D] of in_dtype.
+ *   lam0, eta0, lam, eta, workspace, stream: as for kla_scan_fwd, with
+ *   kla_scan_lti_fwd_workspace_size bytes of workspace.
+ * Errors as for kla_scan_fwd.
+ */
+KLA_API size_t kla_scan_lti_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int64_t D,
+                                               kla_dtype in_dtype);
+KLA_API kla_status kla_scan_lti_fwd(const float *a, const float *p, const float *phi,
+                                    const void *b, kla_dtype in_dtype,
+                                    const float *lam0, const float *eta0,
+                                    float *lam, float *eta,
+                                    int64_t B, int64_t H, int64_t T, int64_t D,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Fused KLA mixer forward: gate production, scan and readout in one pass.
  *
  * A KLA mixer channel observes its token value through an observation

@@ -221,3 +221,74 @@ def make_mixer_workload(key: int, device="cpu", seed: int | None = None):
     g = make_mixer_inputs(w.shape, w.dtype, w.seed if seed is None else seed, device)
     g["lam0"], g["eta0"] = make_initial_state(w.B, w.H, w.D, device=device)
     return g
+
+
+# ---------------------------------------------------------------------------
+# Time-invariant-gate (LTI) inputs.
+#
+# Recipe: one seeded torch.Generator draws z_a, z_p, z_phi per (h, d) channel
+# ([H, D]; standard normals, or coin flips for "hard"), maps them with the
+# gate family of make_gates to a, p, phi (float32), then draws y per token
+# ([B, H, T, D]) and sets b = phi[h, d] * y, rounded once to the input dtype.
+
+LTI_WORKLOADS = {
+    0: Workload(0, "lti-tiny", 1, 1, 256, 16, "f32", "std", 20),
+    1: Workload(1, "lti-small-lm-layer", 8, 16, 2048, 64, "f32", "std", 21),
+    2: Workload(2, "lti-1b-scale-layer", 4, 32, 8192, 128, "bf16", "std", 22),
+    3: Workload(3, "lti-long-context", 1, 32, 131072, 128, "f32", "slow", 23),
+}
+
+
+def make_lti_inputs(shape, gates: str = "std", dtype: str = "f32", seed: int = 0,
+                    device="cpu"):
+    """Returns dict(a, p, phi, b): float32 [H, D] channel gates and the
+    token information b of `shape` ([B, H, T, D]) in the input dtype."""
+    device = torch.device(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    shape = tuple(int(s) for s in shape)
+    ch = (shape[1], shape[3])
+    z = _draw(ch, gen, device, gates)
+    if gates == "std":
+        a64 = torch.sigmoid(z + 2.0)
+    elif gates == "slow":
+        a64 = 1.0 - 1e-3 * torch.sigmoid(z)
+    elif gates == "hard":
+        a64 = torch.where(z > 0.5, 1.0, 1e-3)
+    else:
+        raise ValueError("unknown gate family %r" % gates)
+    z = _draw(ch, gen, device, gates)
+    if gates == "std":
+        p64 = _softplus(z)
+    elif gates == "slow":
+        p64 = 1e-4 * _softplus(z)
+    else:
+        p64 = torch.where(z > 0.5, 1.0, 0.0)
+    z = _draw(ch, gen, device, gates)
+    phi64 = _softplus(z) if gates in ("std", "slow") else torch.where(z > 0.5, 1e4, 0.0)
+    out = {"a": a64.to(torch.float32), "p": p64.to(torch.float32),
+           "phi": phi64.to(torch.float32)}
+    z = _draw(shape, gen, device, gates)
+    y = z if gates in ("std", "slow") else torch.where(z > 0.5, 1.0, -1.0)
+    phi_b = out["phi"].to(torch.float64)[None, :, None, :]
+    out["b"] = _round(phi_b * y, dtype)
+    return out
+
+
+def make_lti_workload(key: int, device="cpu", seed: int | None = None):
+    """Inputs and initial state of a named LTI workload (0..3)."""
+    w = LTI_WORKLOADS[key]
+    g = make_lti_inputs(w.shape, w.gates, w.dtype, w.seed if seed is None else seed, device)
+    g["lam0"], g["eta0"] = make_initial_state(w.B, w.H, w.D, device=device)
+    return g
+
+
+def broadcast_lti(g):
+    """The LTI inputs as full [B, H, T, D] gates (a, p, phi, b) on the CPU in
+    float64, for the oracle."""
+    b = g["b"].detach().to("cpu").double()
+    B, H, T, D = b.shape
+    full = {n: g[n].detach().to("cpu").double()[None, :, None, :].expand(B, H, T, D)
+            for n in ("a", "p", "phi")}
+    full["b"] = b
+    return full

@@ -196,7 +196,76 @@ kla_status kla_scan_fwd(const void* a, const void* p, const void* phi, const voi
     args.HD = H * D;
     args.ws = kla::workspace_view(workspace, pl.ws);
     const hipError_t err =
-        kla::launch_scan_fwd(args, in_dtype, false, static_cast<hipStream_t>(stream));
+        kla::launch_scan_fwd(args, in_dtype, kla::FwdMode::kScan, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(KLA_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
+    return KLA_OK;
+}
+
+size_t kla_scan_lti_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int64_t D,
+                                       kla_dtype in_dtype) {
+    if (in_dtype != KLA_DTYPE_F32 && in_dtype != KLA_DTYPE_BF16) return 0;
+    Plan pl;
+    if (!kla::make_plan(B, H, T, D, kla::kLtiRows, kla::kLtiWaves, kla::kFwdMatrixWords,
+                        kla::kFwdStateWords, &pl) || pl.N == 0)
+        return 0;
+    return pl.ws.bytes;
+}
+
+kla_status kla_scan_lti_fwd(const float* a, const float* p, const float* phi, const void* b,
+                            kla_dtype in_dtype, const float* lam0, const float* eta0,
+                            float* lam, float* eta, int64_t B, int64_t H, int64_t T, int64_t D,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    Plan pl;
+    bool empty = false;
+    kla_status st = common_checks(B, H, T, D, in_dtype, kla::kLtiRows, kla::kLtiWaves,
+                                  kla::kFwdMatrixWords, kla::kFwdStateWords, &pl, &empty);
+    if (st != KLA_OK || empty) return st;
+
+    const float* gates[3] = {a, p, phi};
+    const char* names[3] = {"a", "p", "phi"};
+    for (int i = 0; i < 3; ++i) {
+        if (!gates[i]) return fail(KLA_ERR_INVALID_ARG, "%s is NULL", names[i]);
+        if (misaligned(gates[i], 4))
+            return fail(KLA_ERR_UNSUPPORTED, "%s is not 4-byte aligned", names[i]);
+    }
+    const size_t esz = in_dtype == KLA_DTYPE_F32 ? 4 : 2;
+    if (!b) return fail(KLA_ERR_INVALID_ARG, "b is NULL");
+    if (misaligned(b, esz)) return fail(KLA_ERR_UNSUPPORTED, "b is not %zu-byte aligned", esz);
+    if (!lam || !eta) return fail(KLA_ERR_INVALID_ARG, "%s is NULL", lam ? "eta" : "lam");
+    if (misaligned(lam, 4) || misaligned(eta, 4))
+        return fail(KLA_ERR_UNSUPPORTED, "outputs must be 4-byte aligned");
+    if ((lam0 && misaligned(lam0, 4)) || (eta0 && misaligned(eta0, 4)))
+        return fail(KLA_ERR_UNSUPPORTED, "lam0/eta0 must be 4-byte aligned");
+    if ((st = check_workspace(workspace, workspace_bytes, pl)) != KLA_OK) return st;
+
+    const size_t in_bytes = size_t(pl.N) * esz, out_bytes = size_t(pl.N) * 4;
+    const size_t st_bytes = size_t(pl.C) * 4, ch_bytes = size_t(H * D) * 4;
+    const Buffer bufs[9] = {{a, ch_bytes, "a", false},           {p, ch_bytes, "p", false},
+                            {phi, ch_bytes, "phi", false},       {b, in_bytes, "b", false},
+                            {lam0, st_bytes, "lam0", false},     {eta0, st_bytes, "eta0", false},
+                            {lam, out_bytes, "lam", true},       {eta, out_bytes, "eta", true},
+                            {workspace, pl.ws.bytes, "workspace", true}};
+    if ((st = check_overlaps(bufs, 9)) != KLA_OK) return st;
+
+    kla::FwdArgs args = {};
+    args.in[3] = b;
+    args.lam0 = lam0;
+    args.eta0 = eta0;
+    args.lam = lam;
+    args.eta = eta;
+    args.a_ch = a;
+    args.p_ch = p;
+    args.phi_ch = phi;
+    args.T = T;
+    args.D = D;
+    args.C = pl.C;
+    args.G = pl.G;
+    args.n_chunks = pl.n_chunks;
+    args.n_tiles = pl.n_tiles;
+    args.HD = H * D;
+    args.ws = kla::workspace_view(workspace, pl.ws);
+    const hipError_t err = kla::launch_scan_fwd(args, in_dtype, kla::FwdMode::kLti,
+                                                static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return fail(KLA_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
     return KLA_OK;
 }
@@ -269,7 +338,7 @@ kla_status kla_mixer_fwd(const void* k, const void* v, const void* lam_v, const 
     args.HD = H * D;
     args.ws = kla::workspace_view(workspace, pl.ws);
     const hipError_t err =
-        kla::launch_scan_fwd(args, in_dtype, true, static_cast<hipStream_t>(stream));
+        kla::launch_scan_fwd(args, in_dtype, kla::FwdMode::kMixer, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return fail(KLA_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
     return KLA_OK;
 }

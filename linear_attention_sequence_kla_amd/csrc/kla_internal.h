@@ -30,7 +30,8 @@ bool make_plan(int64_t B, int64_t H, int64_t T, int64_t D, int rows_per_wave,
                int waves, int matrix_words, int state_words, Plan* pl);
 
 // Forward scan.  Scan mode: the four [B, H, T, D] inputs are the gates a, p,
-// phi, b and the outputs lam, eta.  Mixer mode: the inputs are the token
+// phi, b and the outputs lam, eta.  LTI mode: only in[3] (b) is a token
+// tensor; a_ch, p_ch, phi_ch hold the time-invariant gates; outputs lam, eta.  Mixer mode: the inputs are the token
 // tensors k, v, lam_v, q, the gates are a_ch, p_ch per (h, d) channel and
 // phi = k^2 lam_v, b = k lam_v v per token, and the outputs are the readout
 // out = q * eta / lam, optionally var = 1 / lam and the final state.
@@ -40,8 +41,9 @@ struct FwdArgs {
     const float* eta0;     // may be NULL (0)
     float* lam;            // scan: lam     | mixer: out
     float* eta;            // scan: eta     | mixer: var (may be NULL)
-    const float* a_ch;     // mixer: [H, D]
-    const float* p_ch;     // mixer: [H, D]
+    const float* a_ch;     // mixer, LTI: [H, D]
+    const float* p_ch;     // mixer, LTI: [H, D]
+    const float* phi_ch;   // LTI: [H, D]
     float* lam_T;          // mixer: final state [B, H, D] (may be NULL)
     float* eta_T;
     int64_t T, D, C, G, n_chunks, n_tiles, HD;
@@ -69,9 +71,11 @@ struct BwdArgs {
 
 // Tile shapes (rows per wave, waves per workgroup) and record sizes.
 constexpr int kFwdRows = 28, kFwdWaves = 4, kFwdMatrixWords = 7, kFwdStateWords = 2;
+constexpr int kLtiRows = 64, kLtiWaves = 4;
 constexpr int kBwdRows = 20, kBwdWaves = 4, kBwdMatrixWords = 6, kBwdStateWords = 2;
 
-hipError_t launch_scan_fwd(const FwdArgs& args, kla_dtype dtype, bool mixer, hipStream_t stream);
+enum class FwdMode { kScan, kMixer, kLti };
+hipError_t launch_scan_fwd(const FwdArgs& args, kla_dtype dtype, FwdMode mode, hipStream_t stream);
 hipError_t launch_scan_bwd(const BwdArgs& args, kla_dtype dtype, hipStream_t stream);
 hipError_t launch_decode(const void* a, const void* p, const void* phi, const void* b,
                          kla_dtype dtype, float* lam, float* eta, int64_t n, hipStream_t stream);

@@ -131,22 +131,36 @@ __device__ inline Lift load_lift(double* rec, int lane) {
     return n;
 }
 
+// What the four token inputs are and what the replay writes.
+enum class Mode {
+    Scan,   // a, p, phi, b per token -> lam, eta
+    Mixer,  // k, v, lam_v, q per token, (a, p) per channel -> q eta / lam, 1 / lam
+    Lti,    // b per token, (a, p, phi) per channel -> lam, eta
+};
+
 // The float64 gates (a, p, phi, b) of one token.  Scan mode reads them from
 // the four input rows.  Mixer mode makes them from the token inputs (k, v,
 // lam_v, q) and the channel's (a, p): the observation v = k x + noise of
 // precision lam_v adds phi = k^2 lam_v to the precision and b = k lam_v v to
 // the information mean (the information-form update of the Pith review,
-// "Circularity check", with the observation operator k of the ledger).  Both
-// passes over a row evaluate the same expressions, so they see equal gates.
-template <bool Mixer>
+// "Circularity check", with the observation operator k of the ledger).  LTI
+// mode takes the channel's time-invariant (a, p, phi) and the token's b.
+// Both passes over a row evaluate the same expressions, so they see equal
+// gates.
+template <Mode M>
 __device__ inline void token_gates(float x0, float x1, float x2, float x3, double ac, double pc,
-                                   double& a, double& p, double& ph, double& b) {
-    if constexpr (Mixer) {
+                                   double fc, double& a, double& p, double& ph, double& b) {
+    if constexpr (M == Mode::Mixer) {
         const double k = x0, lv = x2;
         a = ac;
         p = pc;
         ph = k * k * lv;
         b = k * lv * double(x1);
+    } else if constexpr (M == Mode::Lti) {
+        a = ac;
+        p = pc;
+        ph = fc;
+        b = x3;
     } else {
         a = x0;
         p = x1;
@@ -155,8 +169,10 @@ __device__ inline void token_gates(float x0, float x1, float x2, float x3, doubl
     }
 }
 
-template <typename In, int L, int W, bool Mixer>
+template <typename In, int L, int W, Mode M>
 __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(3))) void kla_scan_kernel(FwdArgs g) {
+    constexpr bool kMixer = M == Mode::Mixer;
+    constexpr bool kAll = M != Mode::Lti;  // all four token inputs are read
     __shared__ double s_lift[W][7][kWave];
     __shared__ double s_carry[W][2][kWave];
     static_assert(kFwdMatrixWords == 7 && kFwdStateWords == 2, "record layout");
@@ -181,12 +197,13 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
         const char* pp = static_cast<const char*>(g.in[1]) + lm.e0 * int64_t(sizeof(In));
         const char* pf = static_cast<const char*>(g.in[2]) + lm.e0 * int64_t(sizeof(In));
         const char* pb = static_cast<const char*>(g.in[3]) + lm.e0 * int64_t(sizeof(In));
-        // mixer mode: the channel's time-invariant gates
-        double ac = 1.0, pc = 0.0;
-        if constexpr (Mixer) {
+        // mixer and LTI modes: the channel's time-invariant gates
+        double ac = 1.0, pc = 0.0, fc = 0.0;
+        if constexpr (M != Mode::Scan) {
             const int64_t hd = lm.qc % g.HD;
             ac = g.a_ch[hd];
             pc = g.p_ch[hd];
+            if constexpr (M == Mode::Lti) fc = g.phi_ch[hd];
         }
 
         // ---- load the wave's rows; rows past T repeat the last row ----
@@ -197,9 +214,13 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
             for (int i = 0; i < L; ++i) {
                 const uint32_t off =
                     lm.lane_el * uint32_t(sizeof(In)) + uint32_t(min(i, nr - 1)) * in_row;
-                ra[i] = load_gate<In>(pa, off);
-                rp[i] = load_gate<In>(pp, off);
-                rf[i] = load_gate<In>(pf, off);
+                if constexpr (kAll) {
+                    ra[i] = load_gate<In>(pa, off);
+                    rp[i] = load_gate<In>(pp, off);
+                    rf[i] = load_gate<In>(pf, off);
+                } else {
+                    ra[i] = rp[i] = rf[i] = 0.0f;
+                }
                 rb[i] = load_gate<In>(pb, off);
             }
         } else {
@@ -222,7 +243,7 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
 #pragma unroll
             for (int i = 0; i < L; ++i) {
                 double a, p, ph, bb;
-                token_gates<Mixer>(ra[i], rp[i], rf[i], rb[i], ac, pc, a, p, ph, bb);
+                token_gates<M>(ra[i], rp[i], rf[i], rb[i], ac, pc, fc, a, p, ph, bb);
                 const double a2 = a * a;
                 double zn = fma(p, x1, a2 * z1);
                 x1 = fma(ph, zn, x1);
@@ -244,8 +265,10 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
         // this barrier the compiler reuses the float64 conversions of the
         // first pass in the second, doubling the registers a tile needs.
 #pragma unroll
-        for (int i = 0; i < L; ++i)
-            asm volatile("" : "+v"(ra[i]), "+v"(rp[i]), "+v"(rf[i]), "+v"(rb[i]));
+        for (int i = 0; i < L; ++i) {
+            if constexpr (kAll) asm volatile("" : "+v"(ra[i]), "+v"(rp[i]), "+v"(rf[i]));
+            asm volatile("" : "+v"(rb[i]));
+        }
         s_lift[w][0][lane] = m.A;
         s_lift[w][1][lane] = m.B;
         s_lift[w][2][lane] = m.C;
@@ -316,13 +339,13 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
             for (int i = 0; i < L; ++i) {
                 if (i >= nr) continue;  // (uniform; keeps the loop fully unrolled)
                 double a, p, ph, bb;
-                token_gates<Mixer>(ra[i], rp[i], rf[i], rb[i], ac, pc, a, p, ph, bb);
+                token_gates<M>(ra[i], rp[i], rf[i], rb[i], ac, pc, fc, a, p, ph, bb);
                 const double zn = fma(p, X, (a * a) * Z);
                 X = fma(ph, zn, X);
                 Y = fma(bb, zn, a * Y);
                 Z = zn;
                 const uint32_t off = lm.lane_el * uint32_t(sizeof(float)) + uint32_t(i) * out_row;
-                if constexpr (Mixer) {
+                if constexpr (kMixer) {
                     // readout: mean eta / lam = Y / X scaled by q, variance 1 / lam = Z / X
                     const double r = recip(X);
                     if (lm.valid) {
@@ -359,22 +382,25 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
         advance_epoch(g.ws, tag, (g.n_chunks - 1) * g.G, g.n_tiles, lane);
 }
 
+template <int L, int W, Mode M>
+void launch(const FwdArgs& args, kla_dtype dtype, hipStream_t stream) {
+    const dim3 grid(unsigned(args.n_tiles)), block(W * kWave);
+    if (dtype == KLA_DTYPE_F32)
+        hipLaunchKernelGGL((kla_scan_kernel<float, L, W, M>), grid, block, 0, stream, args);
+    else
+        hipLaunchKernelGGL((kla_scan_kernel<uint16_t, L, W, M>), grid, block, 0, stream, args);
+}
+
 }  // namespace
 
-hipError_t launch_scan_fwd(const FwdArgs& args, kla_dtype dtype, bool mixer, hipStream_t stream) {
-    const dim3 grid(unsigned(args.n_tiles)), block(kFwdWaves * kWave);
-    if (dtype == KLA_DTYPE_F32 && !mixer)
-        hipLaunchKernelGGL((kla_scan_kernel<float, kFwdRows, kFwdWaves, false>), grid, block, 0,
-                           stream, args);
-    else if (!mixer)
-        hipLaunchKernelGGL((kla_scan_kernel<uint16_t, kFwdRows, kFwdWaves, false>), grid, block,
-                           0, stream, args);
-    else if (dtype == KLA_DTYPE_F32)
-        hipLaunchKernelGGL((kla_scan_kernel<float, kFwdRows, kFwdWaves, true>), grid, block, 0,
-                           stream, args);
+hipError_t launch_scan_fwd(const FwdArgs& args, kla_dtype dtype, FwdMode mode,
+                           hipStream_t stream) {
+    if (mode == FwdMode::kScan)
+        launch<kFwdRows, kFwdWaves, Mode::Scan>(args, dtype, stream);
+    else if (mode == FwdMode::kMixer)
+        launch<kFwdRows, kFwdWaves, Mode::Mixer>(args, dtype, stream);
     else
-        hipLaunchKernelGGL((kla_scan_kernel<uint16_t, kFwdRows, kFwdWaves, true>), grid, block,
-                           0, stream, args);
+        launch<kLtiRows, kLtiWaves, Mode::Lti>(args, dtype, stream);
     return hipGetLastError();
 }
 

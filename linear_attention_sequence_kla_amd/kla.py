@@ -61,6 +61,11 @@ def library() -> ctypes.CDLL:
         lib.kla_mixer_fwd.argtypes = [vp, vp, vp, vp, ctypes.c_int] + [vp] * 8 + [i64] * 4 + [
             vp, sz, vp]
         lib.kla_mixer_fwd.restype = ctypes.c_int
+        lib.kla_scan_lti_fwd_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+        lib.kla_scan_lti_fwd_workspace_size.restype = sz
+        lib.kla_scan_lti_fwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, vp,
+                                         i64, i64, i64, i64, vp, sz, vp]
+        lib.kla_scan_lti_fwd.restype = ctypes.c_int
         lib.kla_decode_step.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, vp, i64, vp]
         lib.kla_decode_step.restype = ctypes.c_int
         lib.kla_workspace_health.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), vp]
@@ -251,6 +256,53 @@ class KLAScan(torch.autograd.Function):
 def kla_scan(a, p, phi, b, lam0=None, eta0=None):
     """Differentiable KLA scan: returns (lam, eta); see KLAScan."""
     return KLAScan.apply(a, p, phi, b, lam0, eta0)
+
+
+def lti_workspace_size(B: int, H: int, T: int, D: int, dtype=torch.float32) -> int:
+    """Bytes of workspace kla_scan_lti_fwd needs (0 for an empty problem)."""
+    return int(library().kla_scan_lti_fwd_workspace_size(B, H, T, D, _DTYPES[dtype]))
+
+
+def scan_lti_fwd(a: torch.Tensor, p: torch.Tensor, phi: torch.Tensor, b: torch.Tensor,
+                 lam0: torch.Tensor | None = None, eta0: torch.Tensor | None = None,
+                 out: tuple | None = None, workspace: torch.Tensor | None = None):
+    """Forward KLA scan with time-invariant gates (kla_scan_lti_fwd).
+
+    a, p, phi: [H, D] float32; b: [B, H, T, D] contiguous float32 or
+    bfloat16; lam0, eta0: [B, H, D] float32 (None: 1 and 0).  Returns
+    (lam, eta), float32 [B, H, T, D].
+    """
+    if b.dim() != 4:
+        raise ValueError("b must be [B, H, T, D], got shape %s" % (tuple(b.shape),))
+    if b.dtype not in _DTYPES:
+        raise ValueError("b must be float32 or bfloat16, got %s" % b.dtype)
+    if not b.is_cuda or not b.is_contiguous():
+        raise ValueError("b must be a contiguous GPU tensor")
+    B, H, T, D = b.shape
+    dev = b.device
+    for name, t in (("a", a), ("p", p), ("phi", phi)):
+        if t is None:
+            raise ValueError("%s is required" % name)
+        _check_f32(name, t, (H, D), dev)
+    for name, t in (("lam0", lam0), ("eta0", eta0)):
+        _check_f32(name, t, (B, H, D), dev)
+    if out is None:
+        lam = torch.empty(b.shape, dtype=torch.float32, device=dev)
+        eta = torch.empty(b.shape, dtype=torch.float32, device=dev)
+    else:
+        lam, eta = out
+        for name, t in (("lam", lam), ("eta", eta)):
+            if t is None:
+                raise ValueError("%s output is required" % name)
+            _check_f32(name, t, b.shape, dev)
+    stream = torch.cuda.current_stream(dev)
+    if workspace is None:
+        workspace = get_workspace(lti_workspace_size(B, H, T, D, b.dtype), dev, stream)
+    _check(library().kla_scan_lti_fwd(
+        _ptr(a), _ptr(p), _ptr(phi), _ptr(b), _DTYPES[b.dtype], _ptr(lam0), _ptr(eta0),
+        _ptr(lam), _ptr(eta), B, H, T, D, _ptr(workspace), workspace.numel(),
+        ctypes.c_void_p(stream.cuda_stream)))
+    return lam, eta
 
 
 def mixer_workspace_size(B: int, H: int, T: int, D: int, dtype=torch.float32) -> int:

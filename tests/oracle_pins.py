@@ -386,6 +386,61 @@ def pin_constant_gates(scan):
         np.testing.assert_allclose(eta[0, 0, -1], bv / (1.0 - f_star), rtol=1e-11)
 
 
+def _causal_convolution_fft(x, kernel):
+    """y[t] = sum_{s <= t} kernel[t - s] x[s] along the last axis, by a
+    zero-padded real FFT (the frequency-domain evaluation of the convolutional
+    form)."""
+    T = x.shape[-1]
+    n = 1 << (2 * T - 1).bit_length()
+    X = np.fft.rfft(x, n=n)
+    K = np.fft.rfft(kernel, n=n)
+    return np.fft.irfft(X * K, n=n)[..., :T]
+
+
+def pin_lti_convolution(scan):
+    """Time-invariant gates (the linear time-invariant case of the review's
+    minor comment on Theorem 3).  Started from the stationary precision
+    lam* (positive root of p l^2 + (a^2 - 1 - p phi) l - a^2 phi = 0) the
+    precision stays lam* and eta is the causal convolution of b with the
+    kernel f*^j (f* = a / (a^2 + p lam*)) plus f*^t eta0, evaluated here by
+    FFT.  With p = 0 (a deterministic state) and a >= 1 the precision is
+    a^-2t lam0 + phi sum_j a^-2j and the kernel of eta is a^-j, from any
+    lam0."""
+    rng = np.random.default_rng(23)
+    T, D = 700, 5
+    av = rng.uniform(0.3, 1.0, D)
+    pv = rng.uniform(0.05, 2.0, D)
+    fv = rng.uniform(0.1, 3.0, D)
+    c = 1.0 + pv * fv - av * av
+    lam_star = (c + np.sqrt(c * c + 4.0 * pv * av * av * fv)) / (2.0 * pv)
+    f_star = av / (av * av + pv * lam_star)
+    b = rng.normal(size=(1, 1, T, D)) * fv
+    eta0 = rng.normal(size=(1, 1, D))
+    full = lambda v: np.broadcast_to(v, (1, 1, T, D)).copy()  # noqa: E731
+    lam, eta, eta_abs = scan(full(av), full(pv), full(fv), b, lam_star[None, None, :], eta0)
+    np.testing.assert_allclose(lam[0, 0], np.broadcast_to(lam_star, (T, D)), rtol=1e-12)
+    j = np.arange(T)
+    for d in range(D):
+        kern = f_star[d] ** j
+        ref = _causal_convolution_fft(b[0, 0, :, d], kern) + f_star[d] ** (j + 1) * eta0[0, 0, d]
+        err = np.abs(eta[0, 0, :, d] - ref) / eta_abs[0, 0, :, d]
+        assert err.max() <= 1e-10, ("stationary LTI convolution", d, err.max())
+    # deterministic state: p = 0, a >= 1
+    av = rng.uniform(1.0, 1.05, D)
+    fv = rng.uniform(0.1, 3.0, D)
+    lam0 = rng.uniform(0.5, 2.0, (1, 1, D))
+    lam, eta, eta_abs = scan(full(av), np.zeros((1, 1, T, D)), full(fv), b, lam0, eta0)
+    for d in range(D):
+        t = j + 1
+        lam_ref = av[d] ** (-2.0 * t) * lam0[0, 0, d] + fv[d] * _causal_convolution_fft(
+            np.ones(T), av[d] ** (-2.0 * j))
+        np.testing.assert_allclose(lam[0, 0, :, d], lam_ref, rtol=1e-11)
+        ref = _causal_convolution_fft(b[0, 0, :, d], av[d] ** (-1.0 * j)) + \
+            av[d] ** (-1.0 * t) * eta0[0, 0, d]
+        err = np.abs(eta[0, 0, :, d] - ref) / eta_abs[0, 0, :, d]
+        assert err.max() <= 1e-10, ("deterministic LTI convolution", d, err.max())
+
+
 # ---------------------------------------------------------------------------
 # Invariants
 # ---------------------------------------------------------------------------
@@ -457,4 +512,4 @@ def pin_segmenting(scan):
 ALL_PINS = [pin_exact_marginal, pin_hand_worked, pin_info_form, pin_eta_abs,
             pin_prefix_products, pin_random_bracketings, pin_static_state,
             pin_no_process_noise, pin_no_observation, pin_constant_gates,
-            pin_invariants, pin_forget_gate_falls, pin_segmenting]
+            pin_lti_convolution, pin_invariants, pin_forget_gate_falls, pin_segmenting]

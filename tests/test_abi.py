@@ -145,3 +145,31 @@ def test_mixer_argument_errors_before_launch(lib):
     assert st == 3 and "needs" in msg
     st, _ = _mixer_call(lib, k=0, shape=(1, 1, 0, 4))
     assert st == 0
+
+
+def test_lti_workspace_size(lib):
+    ws = lib.kla_scan_lti_fwd_workspace_size
+    assert ws(0, 1, 1, 1, 0) == 0
+    assert ws(1, 1, 1, 1, 7) == 0
+    assert 256 < ws(8, 16, 2048, 64, 0) <= lib.kla_scan_fwd_workspace_size(8, 16, 2048, 64, 0)
+
+
+def test_lti_argument_errors_before_launch(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("uses fake device pointers; argument errors are tested on GPUs elsewhere")
+    vp = ctypes.c_void_p
+
+    def call(a=0x100000, b=0x400000, lam=0x1000000, ws_bytes=1 << 20):
+        st = lib.kla_scan_lti_fwd(vp(a), vp(0x200000), vp(0x300000), vp(b), 0, None, None,
+                                  vp(lam), vp(0x2000000), 2, 1, 4, 4, vp(0x4000000), ws_bytes,
+                                  None)
+        return st, lib.kla_last_error_detail().decode()
+    st, msg = call(a=0)
+    assert st == 1 and "a is NULL" in msg
+    st, msg = call(b=0)
+    assert st == 1 and "b is NULL" in msg
+    st, msg = call(lam=0x400000)
+    assert st == 1 and "overlaps" in msg
+    st, msg = call(ws_bytes=16)
+    assert st == 3

@@ -64,3 +64,40 @@ def test_graph_replays_match_eager():
         scan_fwd(dev[1]["a"], dev[1]["p"], dev[1]["phi"], dev[1]["b"], workspace=ws)
         torch.cuda.synchronize(DEV)
     assert workspace_health(ws) == 0
+
+
+def test_graph_replays_mixer_and_lti():
+    """The fused mixer and the time-invariant scan captured together in one
+    graph on one workspace (kla_mixer_fwd and kla_scan_lti_fwd), replayed
+    three times with eager calls in between."""
+    from kla_inputs import make_lti_inputs, make_mixer_inputs
+    from linear_attention_sequence_kla_amd import (lti_workspace_size, mixer_fwd,
+                                                   mixer_workspace_size, scan_lti_fwd,
+                                                   workspace_health)
+    shape = (2, 3, 900, 40)
+    mx = {n: v.to(DEV) for n, v in make_mixer_inputs(shape, "f32", seed=41).items()}
+    lt = {n: v.to(DEV) for n, v in make_lti_inputs(shape, "std", "f32", seed=42).items()}
+    nbytes = max(mixer_workspace_size(*shape), lti_workspace_size(*shape))
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    outs = [torch.empty(shape, device=DEV) for _ in range(4)]
+    e_out, e_var, _, _ = mixer_fwd(mx["k"], mx["v"], mx["lam_v"], mx["q"], mx["a"], mx["p"],
+                                   workspace=ws)
+    e_lam, e_eta = scan_lti_fwd(lt["a"], lt["p"], lt["phi"], lt["b"], workspace=ws)
+    torch.cuda.synchronize(DEV)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        mixer_fwd(mx["k"], mx["v"], mx["lam_v"], mx["q"], mx["a"], mx["p"], out=outs[0],
+                  var=outs[1], workspace=ws)
+        scan_lti_fwd(lt["a"], lt["p"], lt["phi"], lt["b"], out=(outs[2], outs[3]), workspace=ws)
+    torch.cuda.synchronize(DEV)
+    for replay in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize(DEV)
+        # (a tile may take its carry by another look-back path: equal up to rounding)
+        for got, want in zip(outs, (e_out, e_var, e_lam, e_eta)):
+            assert torch.allclose(got, want, rtol=1e-5, atol=1e-5), replay
+        scan_lti_fwd(lt["a"], lt["p"], lt["phi"], lt["b"], workspace=ws)
+        torch.cuda.synchronize(DEV)
+    assert workspace_health(ws) == 0

@@ -1,6 +1,7 @@
 /*
- * kla.h -- C ABI of libkla: the forward pass of the Kalman Linear Attention
- * (KLA) scan on AMD Instinct MI355X (gfx950).
+ * kla.h -- C ABI of libkla: the Kalman Linear Attention (KLA) scan on AMD
+ * Instinct MI355X (gfx950) -- forward pass, its backward pass, the fused
+ * mixer forward, the time-invariant-gate form and the one-token decode step.
  *
  * The operation (Pith review of arXiv 2602.10743, "What carries the
  * argument" and "Circularity check"; "KLA Part 1" primer, sections 2 and

@@ -183,6 +183,48 @@ def test_side_stream():
     assert_parity(compare(lam.cpu(), eta.cpu(), *ref), TOL_F32, "side stream")
 
 
+def test_concurrent_streams():
+    """Four scans in flight at once on four streams (default priority), each
+    with its own workspace: the carry protocols of concurrent launches do not
+    interfere, and every result matches the oracle."""
+    from linear_attention_sequence_kla_amd import scan_fwd, workspace_health, workspace_size
+    shapes = [(2, 2, 3000, 64), (1, 3, 2500, 40), (4, 1, 1800, 96), (3, 2, 2222, 33)]
+    cases = []
+    for k, shape in enumerate(shapes):
+        g = make_gates(shape, "std", "f32", seed=60 + k)
+        g["lam0"], g["eta0"] = make_initial_state(shape[0], shape[1], shape[3], random=True,
+                                                  seed=60 + k)
+        cases.append(g)
+    streams = [torch.cuda.Stream(DEV) for _ in shapes]
+    outs, wss = [], []
+    torch.cuda.synchronize(DEV)
+    for g, s, shape in zip(cases, streams, shapes):
+        with torch.cuda.stream(s):
+            gd = {n: v.to(DEV, non_blocking=False) for n, v in g.items()}
+            ws = torch.zeros(workspace_size(*shape), dtype=torch.uint8, device=DEV)
+            for _ in range(3):  # repeated calls on the same workspace and stream
+                out = scan_fwd(gd["a"], gd["p"], gd["phi"], gd["b"], gd["lam0"], gd["eta0"],
+                               workspace=ws)
+            outs.append(out)
+            wss.append(ws)
+    torch.cuda.synchronize(DEV)
+    for g, (lam, eta), ws, shape in zip(cases, outs, wss, shapes):
+        assert workspace_health(ws) == 0
+        ref = oracle_scan(g["a"], g["p"], g["phi"], g["b"], g["lam0"], g["eta0"])
+        assert_parity(compare(lam.cpu(), eta.cpu(), *ref), TOL_F32, "stream %s" % (shape,))
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 200000, 1), (1, 4096, 1, 512)],
+                         ids=["one-channel-long", "many-channels-one-token"])
+def test_extreme_aspect(shape):
+    """One channel over a long sequence (a chain of ~1800 tiles in one column)
+    and two million channels of one token (one tile per column)."""
+    g = make_gates(shape, "std", "f32", seed=71)
+    g["lam0"], g["eta0"] = make_initial_state(shape[0], shape[1], shape[3], random=True,
+                                              seed=71)
+    full_parity(g, TOL_F32, "shape %s" % (shape,))
+
+
 def test_argument_errors_on_device():
     """Host-side validation with real device buffers: nothing is launched."""
     from linear_attention_sequence_kla_amd import KlaError, scan_fwd

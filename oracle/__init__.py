@@ -7,5 +7,5 @@ it.  Every function here is pinned by ``tests/test_oracle_pins.py``.
 """
 
 from .kla_oracle import (  # noqa: F401
-    LIBRARY, SOURCE, OracleLibrary, build_oracle, oracle_mixer, oracle_scan, oracle_scan_bwd,
-    oracle_threads)
+    LIBRARY, SOURCE, OracleLibrary, build_oracle, oracle_mixer, oracle_mixer_bwd, oracle_scan,
+    oracle_scan_bwd, oracle_threads)

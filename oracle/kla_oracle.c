@@ -384,3 +384,177 @@ int kla_oracle_mixer(const double *k, const double *v, const double *lv,
     }
     return 0;
 }
+
+/*
+ * ---------------------------------------------------------------------------
+ * Fused mixer, backward pass (vector-Jacobian product), per channel.
+ *
+ * Loss = sum_t g_out[t] out_t + g_var[t] var_t with out_t = q_t eta_t / lam_t
+ * and var_t = 1 / lam_t.  The readout contributes, per token, the direct
+ * adjoints
+ *     d/dlam_t = -g_out q eta / lam^2 - g_var / lam^2,   d/deta_t = g_out q / lam,
+ *     g_q[t]   = g_out eta / lam
+ * which enter the reverse sweep of the filter exactly as g_lam, g_eta do in
+ * kalman_channel_bwd (same partial derivatives of Theorems 1 and 2, here
+ * with the channel's a, p).  The gate adjoints (Lam_t for phi_t, Eta_t for
+ * b_t) reach the token inputs through phi = k^2 lam_v and b = k lam_v v:
+ *     g_k = Lam 2 k lam_v + Eta lam_v v,  g_lam_v = Lam k^2 + Eta k v,
+ *     g_v = Eta k lam_v,
+ * and the channel gates collect their per-token adjoints: g_a = sum_t (Lam
+ * dlam/da + Eta deta/da), g_p likewise (summed over the batch by the caller
+ * of this routine).  m_* are the cancellation-free magnitudes of the same
+ * sums (absolute values of every term, |eta| replaced by its magnitude).
+ */
+static void mixer_channel_bwd(const double *k, const double *v, const double *lv,
+                              const double *q, double a, double p, double lam0,
+                              double eta0, const double *g_out, const double *g_var,
+                              double *g_k, double *g_v, double *g_lv, double *g_q,
+                              double *g_a, double *g_p, double *g_lam0, double *g_eta0,
+                              double *m_k, double *m_v, double *m_lv, double *m_q,
+                              double *m_a, double *m_p, double *m_lam0, double *m_eta0,
+                              int64_t T, int64_t stride, double *work)
+{
+    /* forward states (index 0 = before the first token), by the measurement
+     * update of mixer_channel */
+    double *LAM = work, *ETA = work + (T + 1), *EABS = work + 2 * (T + 1);
+    double P = 1.0 / lam0;
+    double mu = eta0 / lam0;
+    LAM[0] = lam0;
+    ETA[0] = eta0;
+    EABS[0] = fabs(eta0);
+    for (int64_t t = 1; t <= T; ++t) {
+        const int64_t i = (t - 1) * stride;
+        const double kt = k[i];
+        const double Ppred = a * a * P + p;
+        const double mupred = a * mu;
+        const double f = a * P / Ppred;
+        const double S = 1.0 + kt * kt * lv[i] * Ppred;
+        const double K = Ppred * kt * lv[i] / S;
+        mu = mupred + K * (v[i] - kt * mupred);
+        P = Ppred / S;
+        LAM[t] = 1.0 / P;
+        ETA[t] = mu / P;
+        EABS[t] = f * EABS[t - 1] + fabs(kt * lv[i] * v[i]);
+    }
+
+    double cl = 0.0, ce = 0.0, ml = 0.0, me = 0.0;
+    double ga = 0.0, gp = 0.0, ma = 0.0, mp = 0.0;
+    for (int64_t t = T; t >= 1; --t) {
+        const int64_t i = (t - 1) * stride;
+        const double kt = k[i], vt = v[i], lvt = lv[i], qt = q[i];
+        const double lam = LAM[t], eta = ETA[t];
+
+        /* readout adjoints of this token */
+        const double gl_dir = -(g_out[i] * qt * eta + g_var[i]) / (lam * lam);
+        const double ge_dir = g_out[i] * qt / lam;
+        g_q[i] = g_out[i] * eta / lam;
+        m_q[i] = fabs(g_out[i]) * EABS[t] / lam;
+        const double ml_dir = (fabs(g_out[i] * qt) * EABS[t] + fabs(g_var[i])) / (lam * lam);
+        const double me_dir = fabs(g_out[i] * qt) / lam;
+
+        /* the filter step t, as in kalman_channel_bwd */
+        const double lp = LAM[t - 1], ep = ETA[t - 1], eap = EABS[t - 1];
+        const double d = a * a + p * lp;
+        const double d2 = d * d;
+        const double Lam = gl_dir + cl;
+        const double Eta = ge_dir + ce;
+        const double MLam = ml_dir + ml;
+        const double MEta = me_dir + me;
+
+        ga += Lam * (-2.0 * a * lp / d2) + Eta * ep * (p * lp - a * a) / d2;
+        gp += Lam * (-lp * lp / d2) + Eta * (-a * lp * ep / d2);
+        ma += MLam * 2.0 * a * lp / d2 + MEta * eap * (p * lp + a * a) / d2;
+        mp += MLam * lp * lp / d2 + MEta * a * lp * eap / d2;
+
+        /* through phi = k^2 lam_v and b = k lam_v v */
+        g_k[i] = Lam * 2.0 * kt * lvt + Eta * lvt * vt;
+        g_lv[i] = Lam * kt * kt + Eta * kt * vt;
+        g_v[i] = Eta * kt * lvt;
+        m_k[i] = MLam * fabs(2.0 * kt * lvt) + MEta * fabs(lvt * vt);
+        m_lv[i] = MLam * kt * kt + MEta * fabs(kt * vt);
+        m_v[i] = MEta * fabs(kt * lvt);
+
+        cl = a * a / d2 * Lam - a * p * ep / d2 * Eta;
+        ce = a / d * Eta;
+        ml = a * a / d2 * MLam + a * p * eap / d2 * MEta;
+        me = a / d * MEta;
+    }
+    *g_a = ga;
+    *g_p = gp;
+    *m_a = ma;
+    *m_p = mp;
+    *g_lam0 = cl;
+    *g_eta0 = ce;
+    *m_lam0 = ml;
+    *m_eta0 = me;
+}
+
+/*
+ * k, v, lv, q, g_out, g_var: [B,H,T,D]; a, p: [H,D]; lam0, eta0: [B,H,D].
+ * Outputs g_k, g_v, g_lv, g_q (+ m_*) [B,H,T,D]; g_a, g_p (+ m_a, m_p)
+ * [H,D], summed over the batch in order b = 0..B-1; g_lam0, g_eta0 (+ m_*)
+ * [B,H,D].  Returns 0, -1 on a bad size, -2 if scratch memory failed.
+ */
+int kla_oracle_mixer_bwd(const double *k, const double *v, const double *lv,
+                         const double *q, const double *a, const double *p,
+                         const double *lam0, const double *eta0,
+                         const double *g_out, const double *g_var,
+                         double *g_k, double *g_v, double *g_lv, double *g_q,
+                         double *g_a, double *g_p, double *g_lam0, double *g_eta0,
+                         double *m_k, double *m_v, double *m_lv, double *m_q,
+                         double *m_a, double *m_p, double *m_lam0, double *m_eta0,
+                         int64_t B, int64_t H, int64_t T, int64_t D, int nthreads)
+{
+    if (B < 0 || H < 0 || T < 0 || D < 0)
+        return -1;
+    const int64_t channels = B * H * D;
+    int failed = 0;
+    /* per (b, h, d) channel sums of the gate adjoints, added over b below */
+    double *part = (double *)malloc(sizeof(double) * 4 * (size_t)(channels > 0 ? channels : 1));
+    if (!part)
+        return -2;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+
+#pragma omp parallel
+    {
+        double *work = (double *)malloc(sizeof(double) * 3 * (size_t)(T + 1));
+        if (!work) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t c = 0; c < channels; ++c) {
+            if (!work)
+                continue;
+            const int64_t slab = c / D;
+            const int64_t d = c % D;
+            const int64_t hd = (slab % H) * D + d;
+            const int64_t base = slab * T * D + d;
+            mixer_channel_bwd(k + base, v + base, lv + base, q + base, a[hd], p[hd],
+                              lam0[c], eta0[c], g_out + base, g_var + base,
+                              g_k + base, g_v + base, g_lv + base, g_q + base,
+                              part + 4 * c, part + 4 * c + 1, g_lam0 + c, g_eta0 + c,
+                              m_k + base, m_v + base, m_lv + base, m_q + base,
+                              part + 4 * c + 2, part + 4 * c + 3, m_lam0 + c, m_eta0 + c,
+                              T, D, work);
+        }
+        free(work);
+    }
+    for (int64_t hd = 0; hd < H * D; ++hd) {
+        g_a[hd] = g_p[hd] = m_a[hd] = m_p[hd] = 0.0;
+    }
+    for (int64_t c = 0; c < channels; ++c) {
+        const int64_t hd = ((c / D) % H) * D + c % D;
+        g_a[hd] += part[4 * c];
+        g_p[hd] += part[4 * c + 1];
+        m_a[hd] += part[4 * c + 2];
+        m_p[hd] += part[4 * c + 3];
+    }
+    free(part);
+    return failed ? -2 : 0;
+}

@@ -46,6 +46,8 @@ class OracleLibrary:
         lib.kla_oracle_scan_bwd.restype = ctypes.c_int
         lib.kla_oracle_mixer.argtypes = [dp] * 13 + [ctypes.c_int64] * 4 + [ctypes.c_int]
         lib.kla_oracle_mixer.restype = ctypes.c_int
+        lib.kla_oracle_mixer_bwd.argtypes = [dp] * 26 + [ctypes.c_int64] * 4 + [ctypes.c_int]
+        lib.kla_oracle_mixer_bwd.restype = ctypes.c_int
         lib.kla_oracle_threads.argtypes = [ctypes.c_int]
         lib.kla_oracle_threads.restype = ctypes.c_int
         self._lib = lib
@@ -139,6 +141,44 @@ class OracleLibrary:
         return res
 
 
+    def mixer_bwd(self, k, v, lam_v, q, a, p, lam0, eta0, g_out, g_var,
+                  nthreads: int | None = None):
+        """Runs the float64 fused-mixer backward pass.
+
+        Inputs as for ``mixer`` plus the upstream gradients g_out, g_var
+        ([B, H, T, D]; g_var None means zero).  Returns (grads, mags): dicts
+        with keys k, v, lam_v, q ([B, H, T, D]), a, p ([H, D], summed over the
+        batch) and lam0, eta0 ([B, H, D]); mags are the cancellation-free
+        magnitudes of the same sums.
+        """
+        k = _as_f64(k)
+        if k.ndim != 4:
+            raise ValueError("token inputs must be [B, H, T, D]")
+        B, H, T, D = k.shape
+        shape = (B, H, T, D)
+        v, lam_v, q, g_out = (_as_f64(x, shape) for x in (v, lam_v, q, g_out))
+        g_var = _as_f64(np.zeros(shape) if g_var is None else g_var, shape)
+        a, p = (_as_f64(x, (H, D)) for x in (a, p))
+        lam0 = _as_f64(np.ones((B, H, D)) if lam0 is None else lam0, (B, H, D))
+        eta0 = _as_f64(np.zeros((B, H, D)) if eta0 is None else eta0, (B, H, D))
+        names = ("k", "v", "lam_v", "q")
+        grads = {n: np.empty(shape) for n in names}
+        mags = {n: np.empty(shape) for n in names}
+        for n, sh in (("a", (H, D)), ("p", (H, D)), ("lam0", (B, H, D)), ("eta0", (B, H, D))):
+            grads[n] = np.empty(sh)
+            mags[n] = np.empty(sh)
+        rc = self._lib.kla_oracle_mixer_bwd(
+            _ptr(k), _ptr(v), _ptr(lam_v), _ptr(q), _ptr(a), _ptr(p), _ptr(lam0), _ptr(eta0),
+            _ptr(g_out), _ptr(g_var),
+            *(_ptr(grads[n]) for n in names), _ptr(grads["a"]), _ptr(grads["p"]),
+            _ptr(grads["lam0"]), _ptr(grads["eta0"]),
+            *(_ptr(mags[n]) for n in names), _ptr(mags["a"]), _ptr(mags["p"]),
+            _ptr(mags["lam0"]), _ptr(mags["eta0"]), B, H, T, D, int(nthreads or 0))
+        if rc != 0:
+            raise ValueError("mixer backward oracle failed (%d)" % rc)
+        return grads, mags
+
+
 def _as_f64(x, shape=None):
     if hasattr(x, "detach"):  # a torch tensor: copy to host, upcast exactly
         x = x.detach().to("cpu")
@@ -181,6 +221,12 @@ def oracle_scan(a, p, phi, b, lam0=None, eta0=None, nthreads: int | None = None)
 def oracle_mixer(k, v, lam_v, q, a, p, lam0=None, eta0=None, nthreads: int | None = None):
     """The float64 fused-mixer oracle; see ``OracleLibrary.mixer``."""
     return _library().mixer(k, v, lam_v, q, a, p, lam0, eta0, nthreads)
+
+
+def oracle_mixer_bwd(k, v, lam_v, q, a, p, lam0, eta0, g_out, g_var,
+                     nthreads: int | None = None):
+    """The float64 fused-mixer backward oracle; see ``OracleLibrary.mixer_bwd``."""
+    return _library().mixer_bwd(k, v, lam_v, q, a, p, lam0, eta0, g_out, g_var, nthreads)
 
 
 def oracle_scan_bwd(a, p, phi, b, lam0, eta0, g_lam, g_eta, nthreads: int | None = None):

@@ -143,3 +143,47 @@ def test_mixer_mutant_is_caught(name, tmp_path):
         except (AssertionError, FloatingPointError, ValueError, ZeroDivisionError) as e:
             caught.append((pin.__name__, str(e)[:80]))
     assert caught, "no pin caught mutant %s" % name
+
+
+import oracle_mixer_bwd_pins  # noqa: E402
+
+MIXER_BWD_MUTANTS = {
+    "mbwd-readout-precision-adjoint-sign": ("const double gl_dir = -(g_out[i] * qt * eta + g_var[i])",
+                                            "const double gl_dir = (g_out[i] * qt * eta + g_var[i])"),
+    "mbwd-variance-adjoint-dropped": ("-(g_out[i] * qt * eta + g_var[i]) / (lam * lam)",
+                                      "-(g_out[i] * qt * eta) / (lam * lam)"),
+    "mbwd-operator-grad-missing-2": ("g_k[i] = Lam * 2.0 * kt * lvt", "g_k[i] = Lam * kt * lvt"),
+    "mbwd-readout-grad-unscaled": ("g_q[i] = g_out[i] * eta / lam;", "g_q[i] = g_out[i] * eta;"),
+    "mbwd-eta-carry-without-gate": ("ce = a / d * Eta;", "ce = Eta;"),
+    "mbwd-batch-sum-overwrites": ("g_a[hd] += part[4 * c];", "g_a[hd] = part[4 * c];"),
+    "mbwd-precision-grad-missing-term": ("g_lv[i] = Lam * kt * kt + Eta * kt * vt;",
+                                         "g_lv[i] = Lam * kt * kt;"),
+    "mbwd-noise-grad-sign": ("gp += Lam * (-lp * lp / d2)", "gp += Lam * (lp * lp / d2)"),
+    "mbwd-value-grad-missing-precision": ("g_v[i] = Eta * kt * lvt;", "g_v[i] = Eta * kt;"),
+    "mbwd-coupling-dropped": ("cl = a * a / d2 * Lam - a * p * ep / d2 * Eta;",
+                              "cl = a * a / d2 * Lam;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MIXER_BWD_MUTANTS))
+def test_mixer_bwd_mutant_is_caught(name, tmp_path):
+    old, new = MIXER_BWD_MUTANTS[name]
+    src = open(SOURCE).read()
+    assert src.count(old) == 1, "mutation site not unique: %r" % old
+    mutant_src = tmp_path / "mutant.c"
+    mutant_src.write_text(src.replace(old, new, 1))
+    lib = OracleLibrary(build_oracle(str(tmp_path / "libmutant.so"), str(mutant_src)))
+
+    def mixer_bwd(**kw):
+        return lib.mixer_bwd(**kw)
+
+    def mixer(*args):
+        return lib.mixer(*args)
+
+    caught = []
+    for pin in oracle_mixer_bwd_pins.ALL_MIXER_BWD_PINS:
+        try:
+            pin(mixer_bwd, mixer)
+        except (AssertionError, FloatingPointError, ValueError, ZeroDivisionError) as e:
+            caught.append((pin.__name__, str(e)[:80]))
+    assert caught, "no pin caught mutant %s" % name

@@ -74,3 +74,13 @@ import oracle_mixer_pins  # noqa: E402
 def test_mixer_pin(pin):
     from oracle import oracle_mixer
     pin(oracle_mixer)
+
+
+import oracle_mixer_bwd_pins  # noqa: E402
+
+
+@pytest.mark.parametrize("pin", oracle_mixer_bwd_pins.ALL_MIXER_BWD_PINS,
+                         ids=lambda f: f.__name__)
+def test_mixer_bwd_pin(pin):
+    from oracle import oracle_mixer, oracle_mixer_bwd
+    pin(oracle_mixer_bwd, oracle_mixer)

@@ -72,7 +72,8 @@ BWD_MUTANTS = {
     "bwd-magnitude-missing-term": (
         "m_a[i] = MLam * fabs(dl_da) + MEta * eap * (pt * lp + at * at) / d2;",
         "m_a[i] = MLam * fabs(dl_da);"),
-    "bwd-initial-gradient-from-magnitude": ("*g_lam0 = cl;", "*g_lam0 = ml;"),
+    "bwd-initial-gradient-from-magnitude": ("me = de_dep * MEta;\n    }\n    *g_lam0 = cl;",
+                                            "me = de_dep * MEta;\n    }\n    *g_lam0 = ml;"),
 }
 
 

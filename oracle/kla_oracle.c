@@ -320,14 +320,17 @@ int kla_oracle_scan_bwd(const double *a, const double *p, const double *phi,
  * |k lam_v v| and the forget gate f = a P_{t-1} / Ppred; |mu| <= mu_abs), and
  * per channel the final state lam_T = 1 / P_T, eta_T = mu_T / P_T.
  */
-static void mixer_channel(const double *k, const double *v, const double *lv,
-                          const double *q, double a, double p, double lam0,
-                          double eta0, double *out, double *var, double *mu_abs,
-                          double *lamT, double *etaT, int64_t T, int64_t stride)
+static void mixer_filter(const double *k, const double *v, const double *lv,
+                         double a, double p, double lam0, double eta0,
+                         double *PV, double *MU, double *MAG, int64_t T, int64_t stride)
 {
+    /* index 0: the prior; index t: the posterior after token t */
     double P = 1.0 / lam0;
     double mu = eta0 / lam0;
     double mag = fabs(eta0);
+    PV[0] = P;
+    MU[0] = mu;
+    MAG[0] = mag;
 
     for (int64_t t = 0; t < T; ++t) {
         const int64_t i = t * stride;
@@ -344,17 +347,31 @@ static void mixer_channel(const double *k, const double *v, const double *lv,
 
         mag = f * mag + fabs(kt * lv[i] * v[i]);
 
-        out[i] = q[i] * mu;
-        var[i] = P;
-        mu_abs[i] = mag * P;
+        PV[t + 1] = P;
+        MU[t + 1] = mu;
+        MAG[t + 1] = mag;
     }
-    *lamT = 1.0 / P;
-    *etaT = mu / P;
+}
+
+/* The forward outputs of one channel from its filter run. */
+static void mixer_channel(const double *q, const double *PV, const double *MU,
+                          const double *MAG, double *out, double *var, double *mu_abs,
+                          double *lamT, double *etaT, int64_t T, int64_t stride)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        const int64_t i = t * stride;
+        out[i] = q[i] * MU[t + 1];
+        var[i] = PV[t + 1];
+        mu_abs[i] = MAG[t + 1] * PV[t + 1];
+    }
+    *lamT = 1.0 / PV[T];
+    *etaT = MU[T] / PV[T];
 }
 
 /*
  * k, v, lv, q: [B,H,T,D]; a, p: [H,D]; lam0, eta0: [B,H,D];
- * out, var, mu_abs: [B,H,T,D]; lamT, etaT: [B,H,D].  Returns 0 or -1.
+ * out, var, mu_abs: [B,H,T,D]; lamT, etaT: [B,H,D].  Returns 0, -1 on a bad
+ * size, -2 if scratch memory could not be allocated.
  */
 int kla_oracle_mixer(const double *k, const double *v, const double *lv,
                      const double *q, const double *a, const double *p,
@@ -372,17 +389,31 @@ int kla_oracle_mixer(const double *k, const double *v, const double *lv,
     (void)nthreads;
 #endif
 
-#pragma omp parallel for schedule(dynamic, 16)
-    for (int64_t c = 0; c < channels; ++c) {
-        const int64_t slab = c / D;
-        const int64_t d = c % D;
-        const int64_t hd = (slab % H) * D + d;
-        const int64_t base = slab * T * D + d;
-        mixer_channel(k + base, v + base, lv + base, q + base, a[hd], p[hd],
-                      lam0[c], eta0[c], out + base, var + base, mu_abs + base,
-                      lamT + c, etaT + c, T, D);
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *work = (double *)malloc(sizeof(double) * 3 * (size_t)(T + 1));
+        if (!work) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t c = 0; c < channels; ++c) {
+            if (!work)
+                continue;
+            const int64_t slab = c / D;
+            const int64_t d = c % D;
+            const int64_t hd = (slab % H) * D + d;
+            const int64_t base = slab * T * D + d;
+            double *PV = work, *MU = work + (T + 1), *MAG = work + 2 * (T + 1);
+            mixer_filter(k + base, v + base, lv + base, a[hd], p[hd], lam0[c], eta0[c],
+                         PV, MU, MAG, T, D);
+            mixer_channel(q + base, PV, MU, MAG, out + base, var + base, mu_abs + base,
+                          lamT + c, etaT + c, T, D);
+        }
+        free(work);
     }
-    return 0;
+    return failed ? -2 : 0;
 }
 
 /*
@@ -414,27 +445,14 @@ static void mixer_channel_bwd(const double *k, const double *v, const double *lv
                               double *m_a, double *m_p, double *m_lam0, double *m_eta0,
                               int64_t T, int64_t stride, double *work)
 {
-    /* forward states (index 0 = before the first token), by the measurement
-     * update of mixer_channel */
+    /* forward states (index 0 = before the first token): precision, information
+     * mean and its magnitude from the same filter run as the forward outputs */
     double *LAM = work, *ETA = work + (T + 1), *EABS = work + 2 * (T + 1);
-    double P = 1.0 / lam0;
-    double mu = eta0 / lam0;
-    LAM[0] = lam0;
-    ETA[0] = eta0;
-    EABS[0] = fabs(eta0);
-    for (int64_t t = 1; t <= T; ++t) {
-        const int64_t i = (t - 1) * stride;
-        const double kt = k[i];
-        const double Ppred = a * a * P + p;
-        const double mupred = a * mu;
-        const double f = a * P / Ppred;
-        const double S = 1.0 + kt * kt * lv[i] * Ppred;
-        const double K = Ppred * kt * lv[i] / S;
-        mu = mupred + K * (v[i] - kt * mupred);
-        P = Ppred / S;
+    mixer_filter(k, v, lv, a, p, lam0, eta0, LAM, ETA, EABS, T, stride);
+    for (int64_t t = 0; t <= T; ++t) {
+        const double P = LAM[t];
         LAM[t] = 1.0 / P;
-        ETA[t] = mu / P;
-        EABS[t] = f * EABS[t - 1] + fabs(kt * lv[i] * v[i]);
+        ETA[t] = ETA[t] / P;
     }
 
     double cl = 0.0, ce = 0.0, ml = 0.0, me = 0.0;

@@ -109,19 +109,20 @@ MIXER_MUTANTS = {
     "mixer-innovation-ignores-operator": ("(v[i] - kt * mupred)", "(v[i] - mupred)"),
     "mixer-precision-linear-in-operator": ("1.0 + kt * kt * lv[i] * Ppred",
                                            "1.0 + kt * lv[i] * Ppred"),
-    "mixer-readout-without-q": ("out[i] = q[i] * mu;", "out[i] = mu;"),
+    "mixer-readout-without-q": ("out[i] = q[i] * MU[t + 1];", "out[i] = MU[t + 1];"),
     "mixer-variance-not-updated": ("mu = mupred + K * (v[i] - kt * mupred);\n        P = Ppred / S;",
                                    "mu = mupred + K * (v[i] - kt * mupred);\n        P = Ppred;"),
     "mixer-decay-not-squared": ("const double Ppred = a * a * P + p;",
                                 "const double Ppred = a * P + p;"),
     "mixer-noise-dropped": ("const double Ppred = a * a * P + p;",
                             "const double Ppred = a * a * P;"),
-    "mixer-final-precision-as-variance": ("*lamT = 1.0 / P;", "*lamT = P;"),
+    "mixer-final-precision-as-variance": ("*lamT = 1.0 / PV[T];", "*lamT = PV[T];"),
     "mixer-signed-magnitude": ("fabs(kt * lv[i] * v[i])", "(kt * lv[i] * v[i])"),
-    "mixer-wrong-channel-gates": ("(slab % H) * D + d", "(slab / H) * D + d"),
-    "mixer-variance-before-update": ("var[i] = P;", "var[i] = Ppred;"),
-    "mixer-prior-mean-ignored": ("    double mu = eta0 / lam0;\n    double mag = fabs(eta0);\n\n    for (int64_t t = 0; t < T; ++t) {\n        const int64_t i = t * stride;\n        const double kt",
-                                 "    double mu = 0.0;\n    double mag = fabs(eta0);\n\n    for (int64_t t = 0; t < T; ++t) {\n        const int64_t i = t * stride;\n        const double kt"),
+    "mixer-wrong-channel-gates": ("(slab % H) * D + d;\n            const int64_t base = slab * T * D + d;\n            double *PV",
+                                  "(slab / H) * D + d;\n            const int64_t base = slab * T * D + d;\n            double *PV"),
+    "mixer-variance-one-token-early": ("var[i] = PV[t + 1];", "var[i] = PV[t];"),
+    "mixer-prior-mean-ignored": ("    double mu = eta0 / lam0;\n    double mag = fabs(eta0);\n    PV[0] = P;",
+                                 "    double mu = 0.0;\n    double mag = fabs(eta0);\n    PV[0] = P;"),
 }
 
 

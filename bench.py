@@ -32,15 +32,16 @@ KERNEL_SOURCES = {"fwd": ("kla_scan_fwd.hip", "kla_lookback.h", "kla_internal.h"
                   "bwd": ("kla_scan_bwd.hip", "kla_lookback.h", "kla_internal.h"),
                   "decode": ("kla_decode.hip", "kla_lookback.h", "kla_internal.h"),
                   "mixer": ("kla_scan_fwd.hip", "kla_lookback.h", "kla_internal.h"),
-                  "lti": ("kla_scan_fwd.hip", "kla_lookback.h", "kla_internal.h")}
+                  "lti": ("kla_scan_fwd.hip", "kla_lookback.h", "kla_internal.h"),
+                  "mixer_bwd": ("kla_scan_bwd.hip", "kla_lookback.h", "kla_internal.h")}
 KERNEL_NAMES = {"fwd": "kla_scan_kernel", "bwd": "kla_scan_bwd_kernel",
                 "decode": "kla_decode_kernel", "mixer": "kla_scan_kernel",
-                "lti": "kla_scan_kernel"}
+                "lti": "kla_scan_kernel", "mixer_bwd": "kla_mixer_bwd_kernel"}
 # the forward kernel template's last parameter selects the fused-mixer mode
 KERNEL_SUFFIX = {"fwd": "Mode)0>", "mixer": "Mode)1>", "lti": "Mode)2>"}
 PROFILE_NAMES = {"fwd": "kla_scan_kernel", "bwd": "kla_scan_bwd_kernel",
                  "decode": "kla_decode_kernel", "mixer": "kla_scan_kernel_mixer",
-                 "lti": "kla_scan_kernel_lti"}
+                 "lti": "kla_scan_kernel_lti", "mixer_bwd": "kla_mixer_bwd_kernel"}
 
 
 def is_kernel(name: str, direction: str) -> bool:
@@ -80,7 +81,20 @@ def bytes_per_element(dtype: str, direction: str = "fwd") -> int:
         return 4 * gate + 2 * 4
     if direction == "lti":  # b read (gates once per channel); lam, eta written
         return gate + 2 * 4
+    if direction == "mixer_bwd":  # the whole call: recompute, backward kernel, reduction
+        return 3 * gate + 2 * 4 + kernel_bytes_per_element(dtype, direction)
     return 2 * gate + 4 * 4 + 4 * 4
+
+
+def kernel_bytes_per_element(dtype: str, direction: str = "fwd") -> int:
+    """Algorithmic bytes per element of the direction's dominant kernel.  For
+    mixer_bwd that is the backward kernel alone: k, v, lam_v, q, the states
+    lam, eta and the upstream g_out, g_var read; g_k, g_v, g_lam_v, g_q
+    written."""
+    if direction == "mixer_bwd":
+        gate = 4 if dtype == "f32" else 2
+        return 4 * gate + 2 * 4 + 2 * 4 + 4 * 4
+    return bytes_per_element(dtype, direction)
 
 
 def traffic_path(workload_key: int, direction: str) -> str:
@@ -139,7 +153,7 @@ def summarize_counters(args):
     f_fetch = copy_bytes / (cf * 1024.0)
     f_write = copy_bytes / (cw * 1024.0)
     traffic = fetch * 1024.0 * f_fetch + write * 1024.0 * f_write
-    algo = w.elements * bytes_per_element(w.dtype, d)
+    algo = w.elements * kernel_bytes_per_element(w.dtype, d)
     avg_ns = float(st["AverageNs"])
     rec = {"workload": w.describe(), "kernel": st["Name"], "kernel_sha256_16": kernel_hash(d),
            "hbm_bytes_per_launch": traffic, "algorithmic_bytes_per_launch": algo,
@@ -161,7 +175,7 @@ def summarize_counters(args):
         f.write("| %s | %.0f | %s | %s |\n\n" % (st["Calls"], avg_ns, st["MinNs"], st["MaxNs"]))
         f.write("Algorithmic bytes per launch: %d (%d elements x %d B); at the average "
                 "duration: %.0f GB/s = %.3f of 8 TB/s.\n\n"
-                % (algo, w.elements, bytes_per_element(w.dtype, d), algo / avg_ns,
+                % (algo, w.elements, kernel_bytes_per_element(w.dtype, d), algo / avg_ns,
                    algo / avg_ns / HBM_PEAK_GBS))
         f.write("## HBM counters (rocprofv3 --pmc, one counter per run)\n\n")
         f.write("| counter | scan KiB/dispatch | plain copy of %d MiB, KiB | scale |\n"
@@ -180,7 +194,8 @@ def summarize_counters(args):
 
 def workloads_for(direction: str):
     from kla_inputs import LTI_WORKLOADS, MIXER_WORKLOADS, WORKLOADS
-    return {"mixer": MIXER_WORKLOADS, "lti": LTI_WORKLOADS}.get(direction, WORKLOADS)
+    return {"mixer": MIXER_WORKLOADS, "mixer_bwd": MIXER_WORKLOADS,
+            "lti": LTI_WORKLOADS}.get(direction, WORKLOADS)
 
 
 def cpu_baseline(w, g_dev, budget_s: float = 10.0):
@@ -222,11 +237,12 @@ def main(argv=None):
     ap.add_argument("--workload", type=int, default=1,
                     help="0..4; the headline is 1 (small-LM layer)")
     ap.add_argument("--sets", type=int, default=2, help="input/output sets to rotate")
-    ap.add_argument("--direction", choices=("fwd", "bwd", "decode", "mixer", "lti"),
+    ap.add_argument("--direction", choices=("fwd", "bwd", "decode", "mixer", "mixer_bwd", "lti"),
                     default="fwd",
                     help="fwd: kla_scan_fwd (the headline); bwd: kla_scan_bwd; decode: "
                          "kla_decode_step on one token of every channel of the workload; "
                          "mixer: kla_mixer_fwd on the mixer workload of the same key; "
+                         "mixer_bwd: kla_mixer_bwd on the mixer workload; "
                          "lti: kla_scan_lti_fwd on the time-invariant workload of that key")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
@@ -267,8 +283,9 @@ def main(argv=None):
 
     from kla_inputs import make_lti_workload, make_mixer_workload, make_workload
     from linear_attention_sequence_kla_amd import (
-        bwd_workspace_size, decode_step, get_workspace, lti_workspace_size, mixer_fwd, scan_bwd,
-        scan_fwd, scan_lti_fwd, workspace_health, workspace_size)
+        bwd_workspace_size, decode_step, get_workspace, lti_workspace_size, mixer_bwd,
+        mixer_bwd_workspace_size, mixer_fwd, scan_bwd, scan_fwd, scan_lti_fwd, workspace_health,
+        workspace_size)
 
     d = args.direction
     w = workloads_for(d)[args.workload]
@@ -277,10 +294,12 @@ def main(argv=None):
     stream = torch.cuda.current_stream(dev)
     ws = get_workspace(max(workspace_size(*w.shape, TORCH_DTYPE[w.dtype]),
                            bwd_workspace_size(*w.shape, TORCH_DTYPE[w.dtype]),
-                           lti_workspace_size(*w.shape, TORCH_DTYPE[w.dtype])), dev, stream)
+                           lti_workspace_size(*w.shape, TORCH_DTYPE[w.dtype]),
+                           mixer_bwd_workspace_size(*w.shape, TORCH_DTYPE[w.dtype])), dev, stream)
     sets = []
     for k in range(args.sets if d != "decode" else 0):
-        make = {"mixer": make_mixer_workload, "lti": make_lti_workload}.get(d, make_workload)
+        make = {"mixer": make_mixer_workload, "mixer_bwd": make_mixer_workload,
+                "lti": make_lti_workload}.get(d, make_workload)
         g = make(args.workload, device=dev, seed=w.seed + 1000 * k)
         lam = torch.empty(w.shape, dtype=torch.float32, device=dev)
         eta = torch.empty(w.shape, dtype=torch.float32, device=dev)
@@ -291,6 +310,12 @@ def main(argv=None):
             gen.manual_seed(w.seed + 77 + k)
             g["g_lam"] = torch.randn(w.shape, generator=gen, device=dev)
             g["g_eta"] = torch.randn(w.shape, generator=gen, device=dev)
+        if d == "mixer_bwd":
+            # upstream gradients of the readout and the variance ~ N(0, 1)
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(w.seed + 77 + k)
+            g["g_out"] = torch.randn(w.shape, generator=gen, device=dev)
+            g["g_var"] = torch.randn(w.shape, generator=gen, device=dev)
         sets.append((g, (lam, eta)))
     if d == "decode":
         # one token per channel; the state is updated in place each step
@@ -303,6 +328,9 @@ def main(argv=None):
     grads = None
     if d == "bwd":
         grads = tuple(torch.empty(w.shape, dtype=torch.float32, device=dev) for _ in range(4))
+    if d == "mixer_bwd":
+        grads = tuple(torch.empty(w.shape, dtype=torch.float32, device=dev) for _ in range(4)) + \
+            tuple(torch.empty((w.H, w.D), dtype=torch.float32, device=dev) for _ in range(2))
     torch.cuda.synchronize(dev)
 
     def step(i):
@@ -315,6 +343,9 @@ def main(argv=None):
         elif d == "lti":
             scan_lti_fwd(g["a"], g["p"], g["phi"], g["b"], g["lam0"], g["eta0"], out=out,
                          workspace=ws)
+        elif d == "mixer_bwd":
+            mixer_bwd(g["k"], g["v"], g["lam_v"], g["q"], g["a"], g["p"], g["g_out"], g["g_var"],
+                      g["lam0"], g["eta0"], need_state_grads=False, workspace=ws, out=grads)
         elif d == "mixer":
             mixer_fwd(g["k"], g["v"], g["lam_v"], g["q"], g["a"], g["p"], g["lam0"], g["eta0"],
                       out=out[0], var=out[1], workspace=ws)
@@ -394,6 +425,11 @@ def main(argv=None):
     if d == "lti":
         rec["metric"] = ("KLA scan with time-invariant gates, elements (B*H*T*D)/s and "
                          "achieved HBM GB/s vs peak")
+    if d == "mixer_bwd":
+        rec["roofline"]["scope"] = ("the whole call (state recompute, backward kernel, "
+                                    "reduction); traffic is the backward kernel's alone")
+        rec["metric"] = ("KLA fused mixer backward elements (B*H*T*D)/s and achieved HBM GB/s "
+                         "vs peak (the whole call: state recompute, adjoint scan, reduction)")
     if d == "mixer":
         rec["metric"] = ("KLA fused mixer elements (B*H*T*D)/s and achieved HBM GB/s vs peak "
                          "(gates, scan, readout and variance in one pass)")

@@ -1,7 +1,8 @@
 /*
  * kla.h -- C ABI of libkla: the Kalman Linear Attention (KLA) scan on AMD
  * Instinct MI355X (gfx950) -- forward pass, its backward pass, the fused
- * mixer forward, the time-invariant-gate form and the one-token decode step.
+ * mixer (forward and backward), the time-invariant-gate form and the
+ * one-token decode step.
  *
  * The operation (Pith review of arXiv 2602.10743, "What carries the
  * argument" and "Circularity check"; "KLA Part 1" primer, sections 2 and
@@ -241,6 +242,45 @@ KLA_API kla_status kla_mixer_fwd(const void *k, const void *v, const void *lam_v
                                  const float *a, const float *p,
                                  const float *lam0, const float *eta0,
                                  float *out, float *var, float *lam_T, float *eta_T,
+                                 int64_t B, int64_t H, int64_t T, int64_t D,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Fused KLA mixer backward: the vector-Jacobian product of kla_mixer_fwd.
+ *
+ * For a loss with upstream gradients g_out (of out) and g_var (of var),
+ * returns the gradients of the token inputs, of the channel gates (summed
+ * over the batch and the sequence) and of the initial state.  The readout
+ * gives per token the adjoints d/dlam = -(g_out q eta + g_var) / lam^2 and
+ * d/deta = g_out q / lam, which run through the reverse scan of
+ * kla_scan_bwd (the review's Theorems 1 and 2 differentiated); the gate
+ * adjoints reach k, v, lam_v through phi = k^2 lam_v and b = k lam_v v.
+ * The forward states are recomputed from the inputs (into the workspace),
+ * so nothing needs saving between the forward and backward calls.
+ *
+ *   k, v, lam_v, q, a, p, lam0, eta0   as passed to kla_mixer_fwd.
+ *   g_out           device pointer, [B, H, T, D] float32.
+ *   g_var           device pointer, [B, H, T, D] float32, or NULL (zero).
+ *   g_k, g_v, g_lam_v, g_q   device pointers, [B, H, T, D] float32, written.
+ *   g_a, g_p        device pointers, [H, D] float32, written (sums over b, t
+ *                   in a fixed order: deterministic).
+ *   g_lam0, g_eta0  device pointers, [B, H, D] float32, written; may be NULL.
+ *   workspace       kla_mixer_bwd_workspace_size bytes (it holds the
+ *                   recomputed states: about 8 bytes per element), zero-filled
+ *                   once before first use, as for kla_scan_fwd; it may also
+ *                   serve the other entry points in turn.
+ * A size-0 problem is a no-op.  Errors and stream semantics as for
+ * kla_scan_fwd.
+ */
+KLA_API size_t kla_mixer_bwd_workspace_size(int64_t B, int64_t H, int64_t T, int64_t D,
+                                            kla_dtype in_dtype);
+KLA_API kla_status kla_mixer_bwd(const void *k, const void *v, const void *lam_v,
+                                 const void *q, kla_dtype in_dtype,
+                                 const float *a, const float *p,
+                                 const float *lam0, const float *eta0,
+                                 const float *g_out, const float *g_var,
+                                 float *g_k, float *g_v, float *g_lam_v, float *g_q,
+                                 float *g_a, float *g_p, float *g_lam0, float *g_eta0,
                                  int64_t B, int64_t H, int64_t T, int64_t D,
                                  void *workspace, size_t workspace_bytes, void *stream);
 

@@ -1,12 +1,13 @@
 """libkla: the Kalman Linear Attention (KLA) scan on AMD MI355X (gfx950):
-forward and backward scan, time-invariant-gate scan, fused mixer forward,
-decode step.
+forward and backward scan, time-invariant-gate scan, fused mixer (forward
+and backward), decode step.
 
 The work happens in ``libkla.so`` (HIP kernels behind a C ABI declared in
 ``include/kla.h``); ``kla`` is its ctypes binding.
 """
 
 from .kla import (  # noqa: F401
-    KLAScan, KlaError, LIBRARY, bwd_workspace_size, decode_step, get_workspace, kla_scan, library,
-    lti_workspace_size, mixer_fwd, mixer_workspace_size, scan_bwd, scan_fwd, scan_lti_fwd,
-    workspace_health, workspace_size)
+    KLAMixer, KLAScan, KlaError, LIBRARY, bwd_workspace_size, decode_step, get_workspace,
+    kla_mixer, kla_scan, library, lti_workspace_size, mixer_bwd, mixer_bwd_workspace_size,
+    mixer_fwd, mixer_workspace_size, scan_bwd, scan_fwd, scan_lti_fwd, workspace_health,
+    workspace_size)

@@ -120,6 +120,30 @@ kla_status check_workspace(void* workspace, size_t bytes, const Plan& pl) {
     return KLA_OK;
 }
 
+// Workspace of kla_mixer_bwd: the look-back region (shared in turn by the
+// forward recompute and the backward kernel), the recomputed states lam and
+// eta, and the per-tile sums of the channel-gate gradients.
+struct MixerBwdLayout {
+    Plan fwd, bwd;
+    size_t off_lam, off_eta, off_partial, bytes;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool mixer_bwd_layout(int64_t B, int64_t H, int64_t T, int64_t D, MixerBwdLayout* l) {
+    if (!kla::make_plan(B, H, T, D, kla::kFwdRows, kla::kFwdWaves, kla::kFwdMatrixWords,
+                        kla::kFwdStateWords, &l->fwd) ||
+        !kla::make_plan(B, H, T, D, kla::kMixBwdRows, kla::kMixBwdWaves, kla::kBwdMatrixWords,
+                        kla::kBwdStateWords, &l->bwd))
+        return false;
+    const size_t states = align256(size_t(l->fwd.N) * 4);
+    l->off_lam = align256(l->fwd.ws.bytes > l->bwd.ws.bytes ? l->fwd.ws.bytes : l->bwd.ws.bytes);
+    l->off_eta = l->off_lam + states;
+    l->off_partial = l->off_eta + states;
+    l->bytes = l->off_partial + size_t(l->bwd.n_tiles) * 2 * kla::kWave * sizeof(double);
+    return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -266,6 +290,135 @@ kla_status kla_scan_lti_fwd(const float* a, const float* p, const float* phi, co
     args.ws = kla::workspace_view(workspace, pl.ws);
     const hipError_t err = kla::launch_scan_fwd(args, in_dtype, kla::FwdMode::kLti,
                                                 static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(KLA_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
+    return KLA_OK;
+}
+
+size_t kla_mixer_bwd_workspace_size(int64_t B, int64_t H, int64_t T, int64_t D,
+                                    kla_dtype in_dtype) {
+    if (in_dtype != KLA_DTYPE_F32 && in_dtype != KLA_DTYPE_BF16) return 0;
+    MixerBwdLayout l;
+    if (!mixer_bwd_layout(B, H, T, D, &l) || l.fwd.N == 0) return 0;
+    return l.bytes;
+}
+
+kla_status kla_mixer_bwd(const void* k, const void* v, const void* lam_v, const void* q,
+                         kla_dtype in_dtype, const float* a, const float* p, const float* lam0,
+                         const float* eta0, const float* g_out, const float* g_var, float* g_k,
+                         float* g_v, float* g_lam_v, float* g_q, float* g_a, float* g_p,
+                         float* g_lam0, float* g_eta0, int64_t B, int64_t H, int64_t T,
+                         int64_t D, void* workspace, size_t workspace_bytes, void* stream) {
+    Plan pl;
+    bool empty = false;
+    kla_status st = common_checks(B, H, T, D, in_dtype, kla::kMixBwdRows, kla::kMixBwdWaves,
+                                  kla::kBwdMatrixWords, kla::kBwdStateWords, &pl, &empty);
+    if (st != KLA_OK || empty) return st;
+    MixerBwdLayout lay;
+    if (!mixer_bwd_layout(B, H, T, D, &lay) || !lay.fwd.offsets_fit)
+        return fail(KLA_ERR_UNSUPPORTED, "sizes not supported: B=%lld H=%lld T=%lld D=%lld",
+                    (long long)B, (long long)H, (long long)T, (long long)D);
+
+    const void* ins[4] = {k, v, lam_v, q};
+    const char* names[4] = {"k", "v", "lam_v", "q"};
+    const size_t esz = in_dtype == KLA_DTYPE_F32 ? 4 : 2;
+    for (int i = 0; i < 4; ++i) {
+        if (!ins[i]) return fail(KLA_ERR_INVALID_ARG, "%s is NULL", names[i]);
+        if (misaligned(ins[i], esz))
+            return fail(KLA_ERR_UNSUPPORTED, "%s is not %zu-byte aligned", names[i], esz);
+    }
+    const void* req[9] = {a, p, g_out, g_k, g_v, g_lam_v, g_q, g_a, g_p};
+    const char* rnames[9] = {"a", "p", "g_out", "g_k", "g_v", "g_lam_v", "g_q", "g_a", "g_p"};
+    for (int i = 0; i < 9; ++i)
+        if (!req[i]) return fail(KLA_ERR_INVALID_ARG, "%s is NULL", rnames[i]);
+    const void* f32s[14] = {a, p, lam0, eta0, g_out, g_var, g_k, g_v, g_lam_v, g_q, g_a, g_p,
+                            g_lam0, g_eta0};
+    for (int i = 0; i < 14; ++i)
+        if (f32s[i] && misaligned(f32s[i], 4))
+            return fail(KLA_ERR_UNSUPPORTED, "float32 arguments must be 4-byte aligned");
+    if (!workspace) return fail(KLA_ERR_WORKSPACE, "workspace is NULL");
+    if (misaligned(workspace, 256))
+        return fail(KLA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    if (workspace_bytes < lay.bytes)
+        return fail(KLA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                    lay.bytes);
+
+    const size_t in_bytes = size_t(pl.N) * esz, f_bytes = size_t(pl.N) * 4;
+    const size_t st_bytes = size_t(pl.C) * 4, ch_bytes = size_t(H * D) * 4;
+    const Buffer bufs[19] = {
+        {k, in_bytes, "k", false},            {v, in_bytes, "v", false},
+        {lam_v, in_bytes, "lam_v", false},    {q, in_bytes, "q", false},
+        {a, ch_bytes, "a", false},            {p, ch_bytes, "p", false},
+        {lam0, st_bytes, "lam0", false},      {eta0, st_bytes, "eta0", false},
+        {g_out, f_bytes, "g_out", false},     {g_var, f_bytes, "g_var", false},
+        {g_k, f_bytes, "g_k", true},          {g_v, f_bytes, "g_v", true},
+        {g_lam_v, f_bytes, "g_lam_v", true},  {g_q, f_bytes, "g_q", true},
+        {g_a, ch_bytes, "g_a", true},         {g_p, ch_bytes, "g_p", true},
+        {g_lam0, st_bytes, "g_lam0", true},   {g_eta0, st_bytes, "g_eta0", true},
+        {workspace, lay.bytes, "workspace", true}};
+    if ((st = check_overlaps(bufs, 19)) != KLA_OK) return st;
+
+    char* ws = static_cast<char*>(workspace);
+    float* lam = reinterpret_cast<float*>(ws + lay.off_lam);
+    float* eta = reinterpret_cast<float*>(ws + lay.off_eta);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+
+    // 1. recompute the forward states
+    kla::FwdArgs fa = {};
+    fa.in[0] = k;
+    fa.in[1] = v;
+    fa.in[2] = lam_v;
+    fa.lam0 = lam0;
+    fa.eta0 = eta0;
+    fa.lam = lam;
+    fa.eta = eta;
+    fa.a_ch = a;
+    fa.p_ch = p;
+    fa.T = T;
+    fa.D = D;
+    fa.C = lay.fwd.C;
+    fa.G = lay.fwd.G;
+    fa.n_chunks = lay.fwd.n_chunks;
+    fa.n_tiles = lay.fwd.n_tiles;
+    fa.HD = H * D;
+    fa.ws = kla::workspace_view(workspace, lay.fwd.ws);
+    hipError_t err = kla::launch_scan_fwd(fa, in_dtype, kla::FwdMode::kMixerState, s);
+    if (err != hipSuccess) return fail(KLA_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
+
+    // 2. the adjoint scan with the mixer's front and back ends
+    kla::MixerBwdArgs ba;
+    ba.k = k;
+    ba.v = v;
+    ba.lam_v = lam_v;
+    ba.q = q;
+    ba.a_ch = a;
+    ba.p_ch = p;
+    ba.lam0 = lam0;
+    ba.eta0 = eta0;
+    ba.lam = lam;
+    ba.eta = eta;
+    ba.g_out = g_out;
+    ba.g_var = g_var;
+    ba.g_k = g_k;
+    ba.g_v = g_v;
+    ba.g_lam_v = g_lam_v;
+    ba.g_q = g_q;
+    ba.g_lam0 = g_lam0;
+    ba.g_eta0 = g_eta0;
+    ba.partial = reinterpret_cast<double*>(ws + lay.off_partial);
+    ba.T = T;
+    ba.D = D;
+    ba.C = lay.bwd.C;
+    ba.G = lay.bwd.G;
+    ba.n_chunks = lay.bwd.n_chunks;
+    ba.n_tiles = lay.bwd.n_tiles;
+    ba.HD = H * D;
+    ba.ws = kla::workspace_view(workspace, lay.bwd.ws);
+    err = kla::launch_mixer_bwd(ba, in_dtype, s);
+    if (err != hipSuccess) return fail(KLA_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
+
+    // 3. channel-gate gradients
+    err = kla::launch_mixer_grad_reduce(ba.partial, g_a, g_p, B, H, D, lay.bwd.G,
+                                        lay.bwd.n_chunks, s);
     if (err != hipSuccess) return fail(KLA_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
     return KLA_OK;
 }

@@ -72,11 +72,49 @@ struct BwdArgs {
 // Tile shapes (rows per wave, waves per workgroup) and record sizes.
 constexpr int kFwdRows = 28, kFwdWaves = 4, kFwdMatrixWords = 7, kFwdStateWords = 2;
 constexpr int kLtiRows = 64, kLtiWaves = 4;
+constexpr int kMixBwdRows = 8, kMixBwdWaves = 8;
 constexpr int kBwdRows = 20, kBwdWaves = 4, kBwdMatrixWords = 6, kBwdStateWords = 2;
 
-enum class FwdMode { kScan, kMixer, kLti };
+// kMixerState: the mixer's gates, the scan's outputs (lam, eta), for the
+// mixer's backward pass.
+enum class FwdMode { kScan, kMixer, kLti, kMixerState };
 hipError_t launch_scan_fwd(const FwdArgs& args, kla_dtype dtype, FwdMode mode, hipStream_t stream);
 hipError_t launch_scan_bwd(const BwdArgs& args, kla_dtype dtype, hipStream_t stream);
+
+// Fused-mixer backward: token inputs k, v, lam_v, q; channel gates a, p; the
+// forward states lam, eta (recomputed by the caller); upstream g_out, g_var.
+// Writes g_k, g_v, g_lam_v, g_q, g_lam0, g_eta0 and, per tile and lane, the
+// tile's sums of the channel-gate gradients into `partial` ([tile][2][64]).
+struct MixerBwdArgs {
+    const void* k;
+    const void* v;
+    const void* lam_v;
+    const void* q;
+    const float* a_ch;
+    const float* p_ch;
+    const float* lam0;   // may be NULL (1)
+    const float* eta0;   // may be NULL (0)
+    const float* lam;    // forward states
+    const float* eta;
+    const float* g_out;
+    const float* g_var;  // may be NULL (0)
+    float* g_k;
+    float* g_v;
+    float* g_lam_v;
+    float* g_q;
+    float* g_lam0;  // may be NULL
+    float* g_eta0;  // may be NULL
+    double* partial;
+    int64_t T, D, C, G, n_chunks, n_tiles, HD;
+    Workspace ws;
+};
+
+hipError_t launch_mixer_bwd(const MixerBwdArgs& args, kla_dtype dtype, hipStream_t stream);
+// g_a[h, d], g_p[h, d]: the per-tile sums added over the batch and the chunks
+// in a fixed order.
+hipError_t launch_mixer_grad_reduce(const double* partial, float* g_a, float* g_p, int64_t B,
+                                    int64_t H, int64_t D, int64_t G, int64_t n_chunks,
+                                    hipStream_t stream);
 hipError_t launch_decode(const void* a, const void* p, const void* phi, const void* b,
                          kla_dtype dtype, float* lam, float* eta, int64_t n, hipStream_t stream);
 

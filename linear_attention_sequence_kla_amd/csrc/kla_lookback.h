@@ -33,9 +33,14 @@
 namespace kla {
 
 constexpr int kWave = 64;
-constexpr uint32_t kStatusAggregate = 1;  // the tile's own map is published
-constexpr uint32_t kStatusInclusive = 2;  // the tile's inclusive carry is published
-constexpr uint32_t kStatusFinished = 3;   // a last tile of its column has its carry-in
+// Status words.  Calls of different shapes or kernels that share a workspace
+// lay out flags and records differently, so a flag slot may hold a record
+// word (a float64) left by another call; a status is a 32-bit pattern next to
+// the 32-bit tag so that such a word is not mistaken for a flag.
+constexpr uint32_t kStatusMagic = 0x4b4c4100u;                 // "KLA"
+constexpr uint32_t kStatusAggregate = kStatusMagic | 1u;  // the tile's own map is published
+constexpr uint32_t kStatusInclusive = kStatusMagic | 2u;  // the tile's inclusive carry is published
+constexpr uint32_t kStatusFinished = kStatusMagic | 3u;   // a last tile of its column has its carry-in
 constexpr uint32_t kSpinLimit = 1u << 20; // polls before a wait gives up
 constexpr size_t kHeaderBytes = 256;
 
@@ -109,8 +114,8 @@ __device__ inline bool give_up(uint32_t spins, uint32_t* header) {
     return false;
 }
 
-// Waits until `flag` carries this call's tag with a non-empty status and
-// returns the status (0 if the wait gave up; the health word is then set).
+// Waits until `flag` carries this call's tag with a status and returns the
+// status (0 if the wait gave up; the health word is then set).
 // The caller's record loads are agent-coherent atomics issued after the flag
 // was seen, so they observe the records published before it.
 __device__ inline uint32_t wait_flag(uint64_t* flag, uint32_t tag, uint32_t* header) {
@@ -118,7 +123,8 @@ __device__ inline uint32_t wait_flag(uint64_t* flag, uint32_t tag, uint32_t* hea
         const uint64_t v = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
         const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
-        if (hi == tag && lo != 0) {
+        if (hi == tag && (lo == kStatusAggregate || lo == kStatusInclusive ||
+                          lo == kStatusFinished)) {
             asm volatile("" ::: "memory");
             return lo;
         }

@@ -110,6 +110,55 @@ __device__ inline float load_f32(const char* base, uint32_t off) {
     return __builtin_nontemporal_load(reinterpret_cast<const float*>(base + off));
 }
 
+// Wave 0 of a tile: publish the tile's map, look back over the tiles later
+// in time for the carry into the tile, publish the tile's inclusive carry,
+// and leave every wave's own carry-in in s_carry.  `c` is the tile's chunk
+// along T (tiles are numbered from the sequence's end).
+template <int W>
+__device__ inline void tile_carry(const Workspace& ws, int64_t ticket, int64_t G,
+                                  int64_t n_chunks, int64_t c, uint32_t tag,
+                                  const double (*s_adj)[6][kWave], double (*s_carry)[2][kWave],
+                                  int lane) {
+    const bool has_next = c > 0;  // earlier chunks follow in tile order
+    double* const matrix = ws.matrix;
+    double* const state = ws.state;
+    double cl = 0.0, ce = 0.0;  // nothing flows in past the sequence end
+    if (c + 1 < n_chunks) {
+        if (has_next) {
+            store_adj(matrix + size_t(ticket) * 6 * kWave, lane, tile_adj<W>(s_adj, lane));
+            publish(&ws.flags[ticket], lane, flag_word(tag, kStatusAggregate));
+        }
+        int64_t j = ticket - G;
+        uint32_t st;
+        while ((st = wait_flag(&ws.flags[j], tag, ws.header)) == kStatusAggregate) j -= G;
+        if (st == kStatusInclusive) {
+            cl = rec_load(state + size_t(j) * 2 * kWave + lane);
+            ce = rec_load(state + size_t(j) * 2 * kWave + kWave + lane);
+            for (int64_t k = j + G; k < ticket; k += G)
+                apply(load_adj(matrix + size_t(k) * 6 * kWave, lane), cl, ce);
+        }  // else the wait gave up: the health word is set, outputs are wrong
+    }
+    if (has_next) {
+        double l = cl, e = ce;
+        apply(tile_adj<W>(s_adj, lane), l, e);
+        rec_store(state + size_t(ticket) * 2 * kWave + lane, l);
+        rec_store(state + size_t(ticket) * 2 * kWave + kWave + lane, e);
+        publish(&ws.flags[ticket], lane, flag_word(tag, kStatusInclusive));
+    } else if (n_chunks > 1) {
+        publish(&ws.flags[ticket], lane, flag_word(tag, kStatusFinished));
+    }
+    // carry into every wave: the last wave gets the tile's, each earlier one
+    // the carry through the maps of the waves after it
+    s_carry[W - 1][0][lane] = cl;
+    s_carry[W - 1][1][lane] = ce;
+#pragma unroll 1
+    for (int j = W - 1; j > 0; --j) {
+        apply(lds_adj(s_adj, j, lane), cl, ce);
+        s_carry[j - 1][0][lane] = cl;
+        s_carry[j - 1][1][lane] = ce;
+    }
+}
+
 template <typename In, int L, int W>
 __global__ __launch_bounds__(W * kWave) void kla_scan_bwd_kernel(BwdArgs g) {
     __shared__ double s_adj[W][6][kWave];
@@ -210,47 +259,7 @@ __global__ __launch_bounds__(W * kWave) void kla_scan_bwd_kernel(BwdArgs g) {
         __syncthreads();
 
         // ---- tile carry (wave 0): publish, look back over later tiles ----
-        if (w == 0) {
-            const bool has_next = c > 0;  // earlier chunks follow in tile order
-            double* const matrix = g.ws.matrix;
-            double* const state = g.ws.state;
-            double cl = 0.0, ce = 0.0;  // nothing flows in past the sequence end
-            if (c + 1 < g.n_chunks) {
-                if (has_next) {
-                    store_adj(matrix + size_t(ticket) * 6 * kWave, lane, tile_adj<W>(s_adj, lane));
-                    publish(&g.ws.flags[ticket], lane, flag_word(tag, kStatusAggregate));
-                }
-                int64_t j = ticket - g.G;
-                uint32_t st;
-                while ((st = wait_flag(&g.ws.flags[j], tag, g.ws.header)) == kStatusAggregate)
-                    j -= g.G;
-                if (st == kStatusInclusive) {
-                    cl = rec_load(state + size_t(j) * 2 * kWave + lane);
-                    ce = rec_load(state + size_t(j) * 2 * kWave + kWave + lane);
-                    for (int64_t k = j + g.G; k < ticket; k += g.G)
-                        apply(load_adj(matrix + size_t(k) * 6 * kWave, lane), cl, ce);
-                }  // else the wait gave up: the health word is set, outputs are wrong
-            }
-            if (has_next) {
-                double l = cl, e = ce;
-                apply(tile_adj<W>(s_adj, lane), l, e);
-                rec_store(state + size_t(ticket) * 2 * kWave + lane, l);
-                rec_store(state + size_t(ticket) * 2 * kWave + kWave + lane, e);
-                publish(&g.ws.flags[ticket], lane, flag_word(tag, kStatusInclusive));
-            } else if (g.n_chunks > 1) {
-                publish(&g.ws.flags[ticket], lane, flag_word(tag, kStatusFinished));
-            }
-            // carry into every wave: the last wave gets the tile's, each
-            // earlier one the carry through the maps of the waves after it
-            s_carry[W - 1][0][lane] = cl;
-            s_carry[W - 1][1][lane] = ce;
-#pragma unroll 1
-            for (int j = W - 1; j > 0; --j) {
-                apply(lds_adj(s_adj, j, lane), cl, ce);
-                s_carry[j - 1][0][lane] = cl;
-                s_carry[j - 1][1][lane] = ce;
-            }
-        }
+        if (w == 0) tile_carry<W>(g.ws, ticket, g.G, g.n_chunks, c, tag, s_adj, s_carry, lane);
         __syncthreads();
 
         // ---- replay the wave's rows last to first, writing the gradients ----
@@ -293,6 +302,234 @@ __global__ __launch_bounds__(W * kWave) void kla_scan_bwd_kernel(BwdArgs g) {
         advance_epoch(g.ws, tag, (g.n_chunks - 1) * g.G, g.n_tiles, lane);
 }
 
+// Fused-mixer backward (the kernel above with the mixer's front and back
+// ends).  Per token the readout out = q eta / lam, var = 1 / lam feeds the
+// adjoint scan with
+//     g_lam[t] = -(g_out q eta + g_var) / lam^2,   g_eta[t] = g_out q / lam,
+// and writes g_q = g_out eta / lam; the gates phi = k^2 lam_v, b = k lam_v v
+// send the scan's adjoints Lam (of phi) and Eta (of b) to the token inputs:
+//     g_k = 2 Lam k lam_v + Eta lam_v v,  g_lam_v = Lam k^2 + Eta k v,
+//     g_v = Eta k lam_v;
+// the channel gates a, p collect their per-token adjoints (as g_a, g_p of
+// the kernel above) into one sum per tile and lane, added over the batch and
+// the chunks by kla_mixer_grad_reduce_kernel.
+template <typename In, int L, int W>
+__global__ __launch_bounds__(W * kWave) void kla_mixer_bwd_kernel(MixerBwdArgs g) {
+    __shared__ double s_adj[W][6][kWave];
+    __shared__ double s_carry[W][2][kWave];
+    __shared__ double s_part[W][2][kWave];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t ticket = blockIdx.x;
+    uint32_t tag = 0;
+
+    if (ticket < g.n_tiles) {
+        // ---- tile and lane coordinates; tiles run from the sequence's end ----
+        const int64_t cc = ticket / g.G;
+        const int64_t grp = ticket - cc * g.G;
+        const int64_t c = g.n_chunks - 1 - cc;
+        const int64_t t0 = (c * W + w) * L;
+        const int nr = int(min(int64_t(L), g.T - t0));
+        const LaneMap lm = lane_map(grp, t0, lane, g.T, g.D, g.C);
+        const uint32_t in_row = uint32_t(g.D * sizeof(In));
+        const uint32_t f_row = uint32_t(g.D * sizeof(float));
+        const uint32_t in_off = lm.lane_el * uint32_t(sizeof(In));
+        const uint32_t f_off = lm.lane_el * uint32_t(sizeof(float));
+        const int64_t in_base = lm.e0 * int64_t(sizeof(In));
+        const char* pk = static_cast<const char*>(g.k) + in_base;
+        const char* pv = static_cast<const char*>(g.v) + in_base;
+        const char* plv = static_cast<const char*>(g.lam_v) + in_base;
+        const char* pq = static_cast<const char*>(g.q) + in_base;
+        const char* pgo = reinterpret_cast<const char*>(g.g_out) + lm.e0 * 4;
+        const char* pgv = reinterpret_cast<const char*>(g.g_var) + lm.e0 * 4;
+        const char* pl = reinterpret_cast<const char*>(g.lam) + lm.e0 * 4;  // lam_t
+        const char* pe = reinterpret_cast<const char*>(g.eta) + lm.e0 * 4;
+        const int64_t hd = lm.qc % g.HD;
+        const double ac = g.a_ch[hd], pc = g.p_ch[hd];
+        char* oq = reinterpret_cast<char*>(g.g_q) + lm.e0 * 4;
+
+        // ---- load the rows; the readout's adjoints are formed here ----
+        // rl[i], re[i]: the state after row i (lam_t, eta_t); the state
+        // before the wave's first row is (l_in, e_in): row t0 - 1, or the
+        // initial state when the wave starts the sequence.
+        float rk[L], rv[L], rlv[L], rl[L], re[L], rgl[L], rge[L];
+        float l_in = 1.0f, e_in = 0.0f;
+        if (nr > 0) {
+            if (t0 > 0) {
+                l_in = load_f32(pl - f_row, f_off);
+                e_in = load_f32(pe - f_row, f_off);
+            } else {
+                l_in = g.lam0 ? g.lam0[lm.qc] : 1.0f;
+                e_in = g.eta0 ? g.eta0[lm.qc] : 0.0f;
+            }
+#pragma unroll
+            for (int i = 0; i < L; ++i) {
+                const int ri = min(i, nr - 1);
+                const uint32_t io = in_off + uint32_t(ri) * in_row;
+                const uint32_t fo = f_off + uint32_t(ri) * f_row;
+                rk[i] = load_gate<In>(pk, io);
+                rv[i] = load_gate<In>(pv, io);
+                rlv[i] = load_gate<In>(plv, io);
+                rl[i] = load_f32(pl, fo);
+                re[i] = load_f32(pe, fo);
+                const double qv = load_gate<In>(pq, io);
+                const double go = load_f32(pgo, fo);
+                const double gv = g.g_var ? load_f32(pgv, fo) : 0.0f;
+                const double lt = rl[i], et = re[i];
+                const double rlt = recip(lt);
+                rgl[i] = float(-fma(go * qv, et, gv) * rlt * rlt);
+                rge[i] = float(go * qv * rlt);
+                if (i < nr && lm.valid)
+                    __builtin_nontemporal_store(float(go * et * rlt),
+                                                reinterpret_cast<float*>(oq + fo));
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < L; ++i) {
+                rk[i] = rv[i] = rlv[i] = 0.0f;
+                rl[i] = 1.0f;
+                re[i] = rgl[i] = rge[i] = 0.0f;
+            }
+        }
+        if (w == 0) tag = read_tag(g.ws);
+
+        // ---- the wave's map: per-token maps multiplied in time order ----
+        Adj m{1.0, 0.0, 0.0, 1.0, 0.0, 1.0};
+#pragma unroll
+        for (int i = 0; i < L; ++i) {
+            if (i < nr) {
+                const double lp = i ? rl[i - 1] : l_in, ep = i ? re[i - 1] : e_in;
+                const double rd = recip(fma(pc, lp, ac * ac));
+                const double f = ac * rd;
+                const double al = f * f;
+                const double be = -pc * f * ep * rd;
+                const double ge = rge[i];
+                const double o1 = fma(al, double(rgl[i]), be * ge);
+                const double o2 = f * ge;
+                const double nx = fma(m.u, o1, fma(m.v, o2, m.x));
+                m.v = fma(m.u, be, m.v * f);
+                m.u = m.u * al;
+                m.y = fma(m.w, o2, m.y);
+                m.w = m.w * f;
+                m.x = nx;
+            }
+            if ((i % kRenormEvery) == kRenormEvery - 1 || i == L - 1) renorm(m);
+        }
+#pragma unroll
+        for (int i = 0; i < L; ++i)
+            asm volatile("" : "+v"(rk[i]), "+v"(rv[i]), "+v"(rlv[i]), "+v"(rl[i]), "+v"(re[i]),
+                         "+v"(rgl[i]), "+v"(rge[i]));
+        asm volatile("" : "+v"(l_in), "+v"(e_in));
+        s_adj[w][0][lane] = m.u;
+        s_adj[w][1][lane] = m.v;
+        s_adj[w][2][lane] = m.x;
+        s_adj[w][3][lane] = m.w;
+        s_adj[w][4][lane] = m.y;
+        s_adj[w][5][lane] = m.s;
+        __syncthreads();
+
+        if (w == 0) tile_carry<W>(g.ws, ticket, g.G, g.n_chunks, c, tag, s_adj, s_carry, lane);
+        __syncthreads();
+
+        // ---- replay last to first: token-input gradients, gate sums ----
+        double sa = 0.0, sp = 0.0;
+        if (nr > 0) {
+            double cl = s_carry[w][0][lane], ce = s_carry[w][1][lane];
+            char* ok = reinterpret_cast<char*>(g.g_k) + lm.e0 * 4;
+            char* ov = reinterpret_cast<char*>(g.g_v) + lm.e0 * 4;
+            char* olv = reinterpret_cast<char*>(g.g_lam_v) + lm.e0 * 4;
+#pragma unroll
+            for (int i = L - 1; i >= 0; --i) {
+                if (i >= nr) continue;
+                const double lp = i ? rl[i - 1] : l_in, ep = i ? re[i - 1] : e_in;
+                const double rd = recip(fma(pc, lp, ac * ac));
+                const double rd2 = rd * rd;
+                const double f = ac * rd;
+                const double Lam = double(rgl[i]) + cl;
+                const double Eta = double(rge[i]) + ce;
+                sa += (Lam * (-2.0 * ac * lp) + Eta * ep * fma(pc, lp, -ac * ac)) * rd2;
+                sp += -lp * (Lam * lp + Eta * ac * ep) * rd2;
+                const double k = rk[i], vv = rv[i], lv = rlv[i];
+                if (lm.valid) {
+                    const uint32_t off = f_off + uint32_t(i) * f_row;
+                    __builtin_nontemporal_store(float(fma(Lam * 2.0 * k, lv, Eta * lv * vv)),
+                                                reinterpret_cast<float*>(ok + off));
+                    __builtin_nontemporal_store(float(Eta * k * lv),
+                                                reinterpret_cast<float*>(ov + off));
+                    __builtin_nontemporal_store(float(fma(Lam * k, k, Eta * k * vv)),
+                                                reinterpret_cast<float*>(olv + off));
+                }
+                cl = fma(f * f, Lam, -pc * f * ep * rd * Eta);
+                ce = f * Eta;
+            }
+            if (t0 == 0 && lm.valid) {
+                if (g.g_lam0) g.g_lam0[lm.q] = float(cl);
+                if (g.g_eta0) g.g_eta0[lm.q] = float(ce);
+            }
+        }
+        // ---- the tile's sums of the channel-gate gradients ----
+        s_part[w][0][lane] = sa;
+        s_part[w][1][lane] = sp;
+        __syncthreads();
+        if (w == 0) {
+            double ta = 0.0, tp = 0.0;
+#pragma unroll
+            for (int j = 0; j < W; ++j) {
+                ta += s_part[j][0][lane];
+                tp += s_part[j][1][lane];
+            }
+            g.partial[(size_t(ticket) * 2) * kWave + lane] = ta;
+            g.partial[(size_t(ticket) * 2 + 1) * kWave + lane] = tp;
+        }
+    }
+
+    // ---- the last workgroup advances the epoch once every tile read it ----
+    if (ticket == int64_t(gridDim.x) - 1 && g.n_chunks > 1 && w == 0)
+        advance_epoch(g.ws, tag, (g.n_chunks - 1) * g.G, g.n_tiles, lane);
+}
+
+// g_a[h, d] and g_p[h, d]: a workgroup of kReduceWaves waves per 64 channels
+// (h, d); wave w adds the per-tile sums of the (b, chunk) pairs j = w,
+// w + kReduceWaves, ... and wave 0 adds the waves' totals in order, so the
+// result does not depend on timing (deterministic).
+constexpr int kReduceWaves = 16;
+
+__global__ __launch_bounds__(kReduceWaves * kWave) void kla_mixer_grad_reduce_kernel(
+    const double* partial, float* g_a, float* g_p, int64_t B, int64_t H, int64_t D, int64_t G,
+    int64_t n_chunks) {
+    __shared__ double s_sum[kReduceWaves][2][kWave];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x / kWave;
+    const int64_t HD = H * D;
+    const int64_t hd = int64_t(blockIdx.x) * kWave + lane;
+    const int64_t n = B * n_chunks;
+    double sa = 0.0, sp = 0.0;
+    if (hd < HD) {
+#pragma unroll 4
+        for (int64_t j = w; j < n; j += kReduceWaves) {
+            const int64_t b = j / n_chunks, cc = j - b * n_chunks;
+            const int64_t q = b * HD + hd;
+            const int64_t grp = q / kWave, ln = q - grp * kWave;
+            const size_t t = size_t(cc * G + grp);
+            sa += partial[(t * 2) * kWave + ln];
+            sp += partial[(t * 2 + 1) * kWave + ln];
+        }
+    }
+    s_sum[w][0][lane] = sa;
+    s_sum[w][1][lane] = sp;
+    __syncthreads();
+    if (w == 0 && hd < HD) {
+        double ta = 0.0, tp = 0.0;
+        for (int j = 0; j < kReduceWaves; ++j) {
+            ta += s_sum[j][0][lane];
+            tp += s_sum[j][1][lane];
+        }
+        g_a[hd] = float(ta);
+        g_p[hd] = float(tp);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_scan_bwd(const BwdArgs& args, kla_dtype dtype, hipStream_t stream) {
@@ -303,6 +540,27 @@ hipError_t launch_scan_bwd(const BwdArgs& args, kla_dtype dtype, hipStream_t str
     else
         hipLaunchKernelGGL((kla_scan_bwd_kernel<uint16_t, kBwdRows, kBwdWaves>), grid, block, 0,
                            stream, args);
+    return hipGetLastError();
+}
+
+hipError_t launch_mixer_bwd(const MixerBwdArgs& args, kla_dtype dtype, hipStream_t stream) {
+    const dim3 grid(unsigned(args.n_tiles)), block(kMixBwdWaves * kWave);
+    if (dtype == KLA_DTYPE_F32)
+        hipLaunchKernelGGL((kla_mixer_bwd_kernel<float, kMixBwdRows, kMixBwdWaves>), grid, block,
+                           0, stream, args);
+    else
+        hipLaunchKernelGGL((kla_mixer_bwd_kernel<uint16_t, kMixBwdRows, kMixBwdWaves>), grid,
+                           block, 0, stream, args);
+    return hipGetLastError();
+}
+
+hipError_t launch_mixer_grad_reduce(const double* partial, float* g_a, float* g_p, int64_t B,
+                                    int64_t H, int64_t D, int64_t G, int64_t n_chunks,
+                                    hipStream_t stream) {
+    const int64_t n = H * D;
+    hipLaunchKernelGGL(kla_mixer_grad_reduce_kernel, dim3(unsigned((n + kWave - 1) / kWave)),
+                       dim3(kReduceWaves * kWave), 0, stream, partial, g_a, g_p, B, H, D, G,
+                       n_chunks);
     return hipGetLastError();
 }
 

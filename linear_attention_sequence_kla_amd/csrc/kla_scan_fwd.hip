@@ -136,6 +136,7 @@ enum class Mode {
     Scan,   // a, p, phi, b per token -> lam, eta
     Mixer,  // k, v, lam_v, q per token, (a, p) per channel -> q eta / lam, 1 / lam
     Lti,    // b per token, (a, p, phi) per channel -> lam, eta
+    MixerState,  // k, v, lam_v per token, (a, p) per channel -> lam, eta
 };
 
 // The float64 gates (a, p, phi, b) of one token.  Scan mode reads them from
@@ -150,7 +151,7 @@ enum class Mode {
 template <Mode M>
 __device__ inline void token_gates(float x0, float x1, float x2, float x3, double ac, double pc,
                                    double fc, double& a, double& p, double& ph, double& b) {
-    if constexpr (M == Mode::Mixer) {
+    if constexpr (M == Mode::Mixer || M == Mode::MixerState) {
         const double k = x0, lv = x2;
         a = ac;
         p = pc;
@@ -172,7 +173,8 @@ __device__ inline void token_gates(float x0, float x1, float x2, float x3, doubl
 template <typename In, int L, int W, Mode M>
 __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(3))) void kla_scan_kernel(FwdArgs g) {
     constexpr bool kMixer = M == Mode::Mixer;
-    constexpr bool kAll = M != Mode::Lti;  // all four token inputs are read
+    constexpr bool kAll = M != Mode::Lti;            // the first three token inputs are read
+    constexpr bool kFourth = M != Mode::MixerState;  // the fourth one is read
     __shared__ double s_lift[W][7][kWave];
     __shared__ double s_carry[W][2][kWave];
     static_assert(kFwdMatrixWords == 7 && kFwdStateWords == 2, "record layout");
@@ -221,7 +223,7 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
                 } else {
                     ra[i] = rp[i] = rf[i] = 0.0f;
                 }
-                rb[i] = load_gate<In>(pb, off);
+                rb[i] = kFourth ? load_gate<In>(pb, off) : 0.0f;
             }
         } else {
 #pragma unroll
@@ -267,7 +269,7 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
 #pragma unroll
         for (int i = 0; i < L; ++i) {
             if constexpr (kAll) asm volatile("" : "+v"(ra[i]), "+v"(rp[i]), "+v"(rf[i]));
-            asm volatile("" : "+v"(rb[i]));
+            if constexpr (kFourth) asm volatile("" : "+v"(rb[i]));
         }
         s_lift[w][0][lane] = m.A;
         s_lift[w][1][lane] = m.B;
@@ -399,6 +401,8 @@ hipError_t launch_scan_fwd(const FwdArgs& args, kla_dtype dtype, FwdMode mode,
         launch<kFwdRows, kFwdWaves, Mode::Scan>(args, dtype, stream);
     else if (mode == FwdMode::kMixer)
         launch<kFwdRows, kFwdWaves, Mode::Mixer>(args, dtype, stream);
+    else if (mode == FwdMode::kMixerState)
+        launch<kFwdRows, kFwdWaves, Mode::MixerState>(args, dtype, stream);
     else
         launch<kLtiRows, kLtiWaves, Mode::Lti>(args, dtype, stream);
     return hipGetLastError();

@@ -66,6 +66,11 @@ def library() -> ctypes.CDLL:
         lib.kla_scan_lti_fwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, vp,
                                          i64, i64, i64, i64, vp, sz, vp]
         lib.kla_scan_lti_fwd.restype = ctypes.c_int
+        lib.kla_mixer_bwd_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+        lib.kla_mixer_bwd_workspace_size.restype = sz
+        lib.kla_mixer_bwd.argtypes = [vp, vp, vp, vp, ctypes.c_int] + [vp] * 14 + [i64] * 4 + [
+            vp, sz, vp]
+        lib.kla_mixer_bwd.restype = ctypes.c_int
         lib.kla_decode_step.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, vp, i64, vp]
         lib.kla_decode_step.restype = ctypes.c_int
         lib.kla_workspace_health.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), vp]
@@ -362,6 +367,102 @@ def mixer_fwd(k: torch.Tensor, v: torch.Tensor, lam_v: torch.Tensor, q: torch.Te
         _ptr(eta0), _ptr(out), _ptr(var), _ptr(lam_T), _ptr(eta_T), B, H, T, D, _ptr(workspace),
         workspace.numel(), ctypes.c_void_p(stream.cuda_stream)))
     return out, var, lam_T, eta_T
+
+
+def mixer_bwd_workspace_size(B: int, H: int, T: int, D: int, dtype=torch.float32) -> int:
+    """Bytes of workspace kla_mixer_bwd needs (0 for an empty problem)."""
+    return int(library().kla_mixer_bwd_workspace_size(B, H, T, D, _DTYPES[dtype]))
+
+
+def mixer_bwd(k: torch.Tensor, v: torch.Tensor, lam_v: torch.Tensor, q: torch.Tensor,
+              a: torch.Tensor, p: torch.Tensor, g_out: torch.Tensor,
+              g_var: torch.Tensor | None = None, lam0: torch.Tensor | None = None,
+              eta0: torch.Tensor | None = None, need_state_grads: bool = True,
+              workspace: torch.Tensor | None = None, out: tuple | None = None):
+    """Fused KLA mixer backward on the current stream (kla_mixer_bwd).
+
+    Inputs as for ``mixer_fwd``; g_out, g_var: float32 [B, H, T, D] upstream
+    gradients of the readout and the variance (g_var None: zero).  Returns
+    (g_k, g_v, g_lam_v, g_q, g_a, g_p, g_lam0, g_eta0), float32; the last two
+    are None unless need_state_grads.  ``out`` may supply the first six.
+    """
+    if k.dim() != 4:
+        raise ValueError("token inputs must be [B, H, T, D], got shape %s" % (tuple(k.shape),))
+    for name, t in zip(("k", "v", "lam_v", "q"), (k, v, lam_v, q)):
+        if t.shape != k.shape or t.dtype != k.dtype:
+            raise ValueError("%s must match k in shape and dtype" % name)
+        if not t.is_cuda or t.device != k.device or not t.is_contiguous():
+            raise ValueError("%s must be contiguous on k's GPU" % name)
+    if k.dtype not in _DTYPES:
+        raise ValueError("token dtype must be float32 or bfloat16, got %s" % k.dtype)
+    B, H, T, D = k.shape
+    dev = k.device
+    for name, t in (("a", a), ("p", p)):
+        if t is None:
+            raise ValueError("%s is required" % name)
+        _check_f32(name, t, (H, D), dev)
+    if g_out is None:
+        raise ValueError("g_out is required")
+    for name, t in (("g_out", g_out), ("g_var", g_var)):
+        _check_f32(name, t, k.shape, dev)
+    for name, t in (("lam0", lam0), ("eta0", eta0)):
+        _check_f32(name, t, (B, H, D), dev)
+    if out is None:
+        g_k, g_v, g_lam_v, g_q = (torch.empty(k.shape, dtype=torch.float32, device=dev)
+                                  for _ in range(4))
+        g_a = torch.empty((H, D), dtype=torch.float32, device=dev)
+        g_p = torch.empty((H, D), dtype=torch.float32, device=dev)
+    else:
+        g_k, g_v, g_lam_v, g_q, g_a, g_p = out
+        for name, t, sh in (("g_k", g_k, k.shape), ("g_v", g_v, k.shape),
+                            ("g_lam_v", g_lam_v, k.shape), ("g_q", g_q, k.shape),
+                            ("g_a", g_a, (H, D)), ("g_p", g_p, (H, D))):
+            if t is None:
+                raise ValueError("%s output is required" % name)
+            _check_f32(name, t, sh, dev)
+    g_lam0 = g_eta0 = None
+    if need_state_grads:
+        g_lam0 = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+        g_eta0 = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    if workspace is None:
+        workspace = get_workspace(mixer_bwd_workspace_size(B, H, T, D, k.dtype), dev, stream)
+    _check(library().kla_mixer_bwd(
+        _ptr(k), _ptr(v), _ptr(lam_v), _ptr(q), _DTYPES[k.dtype], _ptr(a), _ptr(p), _ptr(lam0),
+        _ptr(eta0), _ptr(g_out), _ptr(g_var), _ptr(g_k), _ptr(g_v), _ptr(g_lam_v), _ptr(g_q),
+        _ptr(g_a), _ptr(g_p), _ptr(g_lam0), _ptr(g_eta0), B, H, T, D, _ptr(workspace),
+        workspace.numel(), ctypes.c_void_p(stream.cuda_stream)))
+    return g_k, g_v, g_lam_v, g_q, g_a, g_p, g_lam0, g_eta0
+
+
+class KLAMixer(torch.autograd.Function):
+    """Differentiable fused mixer: kla_mixer_fwd forward, kla_mixer_bwd
+    backward (which recomputes the forward states).  Returns (out, var).
+    Gradients are float32 and are cast to each input's dtype."""
+
+    @staticmethod
+    def forward(ctx, k, v, lam_v, q, a, p, lam0, eta0):
+        out, var, _, _ = mixer_fwd(k, v, lam_v, q, a, p, lam0, eta0)
+        ctx.save_for_backward(k, v, lam_v, q, a, p, lam0, eta0)
+        return out, var
+
+    @staticmethod
+    def backward(ctx, g_out, g_var):
+        k, v, lam_v, q, a, p, lam0, eta0 = ctx.saved_tensors
+        need = ctx.needs_input_grad
+        if g_out is None:
+            g_out = torch.zeros(k.shape, dtype=torch.float32, device=k.device)
+        g = mixer_bwd(k, v, lam_v, q, a, p, g_out.contiguous().float(),
+                      None if g_var is None else g_var.contiguous().float(), lam0, eta0,
+                      need_state_grads=need[6] or need[7])
+        cast = (lambda t, x: t.to(x.dtype))  # noqa: E731
+        return (cast(g[0], k), cast(g[1], v), cast(g[2], lam_v), cast(g[3], q), g[4], g[5],
+                g[6] if need[6] else None, g[7] if need[7] else None)
+
+
+def kla_mixer(k, v, lam_v, q, a, p, lam0=None, eta0=None):
+    """Differentiable fused KLA mixer: returns (out, var); see KLAMixer."""
+    return KLAMixer.apply(k, v, lam_v, q, a, p, lam0, eta0)
 
 
 def decode_step(a: torch.Tensor, p: torch.Tensor, phi: torch.Tensor, b: torch.Tensor,

@@ -173,3 +173,43 @@ def test_lti_argument_errors_before_launch(lib):
     assert st == 1 and "overlaps" in msg
     st, msg = call(ws_bytes=16)
     assert st == 3
+
+
+def test_mixer_bwd_workspace_size(lib):
+    ws = lib.kla_mixer_bwd_workspace_size
+    assert ws(0, 1, 1, 1, 0) == 0
+    assert ws(1, 1, 1, 1, 9) == 0
+    n = 8 * 16 * 2048 * 64
+    big = ws(8, 16, 2048, 64, 0)
+    # holds the recomputed states (8 bytes per element) and the carry records
+    assert big >= 8 * n + lib.kla_scan_fwd_workspace_size(8, 16, 2048, 64, 0)
+    assert big % 256 == 0
+
+
+def test_mixer_bwd_argument_errors_before_launch(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("uses fake device pointers; argument errors are tested on GPUs elsewhere")
+    vp = ctypes.c_void_p
+    shape = (2, 1, 4, 4)
+    need = lib.kla_mixer_bwd_workspace_size(*shape, 0)
+
+    def call(k=0x100000, g_out=0x700000, g_k=0x1000000, g_a=0x1800000, ws=0x4000000,
+             ws_bytes=need):
+        st = lib.kla_mixer_bwd(vp(k), vp(0x200000), vp(0x300000), vp(0x400000), 0,
+                               vp(0x500000), vp(0x600000), None, None, vp(g_out), None,
+                               vp(g_k), vp(0x1100000), vp(0x1200000), vp(0x1300000), vp(g_a),
+                               vp(0x1900000), None, None, *shape, vp(ws), ws_bytes, None)
+        return st, lib.kla_last_error_detail().decode()
+    st, msg = call(k=0)
+    assert st == 1 and "k is NULL" in msg
+    st, msg = call(g_out=0)
+    assert st == 1 and "g_out is NULL" in msg
+    st, msg = call(g_a=0)
+    assert st == 1 and "g_a is NULL" in msg
+    st, msg = call(g_k=0x700000)
+    assert st == 1 and "overlaps" in msg
+    st, msg = call(ws_bytes=need - 8)
+    assert st == 3 and "needs" in msg
+    st, _ = call(ws=0x4000010)
+    assert st == 3

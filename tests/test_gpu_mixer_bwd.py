@@ -1,0 +1,150 @@
+"""GPU parity of the fused mixer's backward pass (kla_mixer_bwd through the C
+ABI, and the KLAMixer autograd Function) against the float64 mixer backward
+oracle.  Bar: kla_metric.compare_grads (error over the cancellation-free
+magnitude) within 1e-4 for fp32 inputs, 2e-2 for bf16, no NaN."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from kla_inputs import MIXER_WORKLOADS, make_initial_state, make_mixer_inputs
+from kla_metric import TOL_BF16, TOL_F32, assert_grad_parity, compare_grads
+from oracle import oracle_mixer_bwd
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+TOKEN = ("k", "v", "lam_v", "q")
+NAMES = ("k", "v", "lam_v", "q", "a", "p", "lam0", "eta0")
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _case(shape, dtype="f32", seed=0, random_state=True, with_var=True):
+    g = make_mixer_inputs(shape, dtype, seed=seed)
+    g["lam0"], g["eta0"] = make_initial_state(shape[0], shape[1], shape[3],
+                                              random=random_state, seed=seed)
+    gen = torch.Generator().manual_seed(seed + 99)
+    g["g_out"] = torch.randn(shape, generator=gen)
+    g["g_var"] = torch.randn(shape, generator=gen) if with_var else None
+    return g
+
+
+def run_gpu(g, need_state=True):
+    from linear_attention_sequence_kla_amd import get_workspace, mixer_bwd, workspace_health
+    d = {n: (None if t is None else t.to(DEV)) for n, t in g.items()}
+    res = mixer_bwd(*(d[n] for n in TOKEN), d["a"], d["p"], d["g_out"], d["g_var"], d["lam0"],
+                    d["eta0"], need_state_grads=need_state)
+    torch.cuda.synchronize(DEV)
+    assert workspace_health(get_workspace(0, DEV, torch.cuda.current_stream(DEV))) == 0
+    return dict(zip(NAMES, res))
+
+
+def oracle(g):
+    return oracle_mixer_bwd(*(g[n] for n in TOKEN), g["a"], g["p"], g["lam0"], g["eta0"],
+                            g["g_out"], g["g_var"])
+
+
+def parity(g, tol, what, need_state=True):
+    got = run_gpu(g, need_state)
+    grads, mags = oracle(g)
+    rep = compare_grads({n: (None if t is None else t.cpu()) for n, t in got.items()}, grads,
+                        mags)
+    _say("%s: %s" % (what, rep))
+    assert_grad_parity(rep, tol, what)
+    return rep
+
+
+@pytest.mark.parametrize("key", [0, 1])
+def test_mixer_bwd_workload(key):
+    w = MIXER_WORKLOADS[key]
+    _say("mixer backward, workload %s" % w.describe())
+    parity(_case(w.shape, w.dtype, seed=w.seed), TOL_F32, w.describe())
+
+
+SHAPES = [(1, 1, 1, 1), (1, 1, 7, 3), (2, 3, 113, 7), (1, 2, 337, 64), (3, 1, 450, 65),
+          (2, 2, 1000, 33), (1, 1, 2049, 128)]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_mixer_bwd_shapes(shape):
+    parity(_case(shape, seed=sum(shape)), TOL_F32, "shape %s" % (shape,))
+
+
+def test_mixer_bwd_bf16_no_var_default_state():
+    g = _case((2, 2, 600, 48), "bf16", seed=3, random_state=False, with_var=False)
+    parity(g, TOL_BF16, "bf16, g_var NULL, default state", need_state=False)
+
+
+def test_mixer_bwd_full_size_sampled():
+    """The 1B-scale layer shape in full (the benchmark's launch); the oracle
+    checks the token-input gradients of a sample of whole channels."""
+    from linear_attention_sequence_kla_amd import mixer_bwd
+    w = MIXER_WORKLOADS[2]
+    _say("mixer backward, workload %s (sampled channels)" % w.describe())
+    g = make_mixer_inputs(w.shape, w.dtype, w.seed, device=DEV)
+    g["lam0"], g["eta0"] = make_initial_state(w.B, w.H, w.D, random=True, seed=w.seed,
+                                              device=DEV)
+    gen = torch.Generator(device=DEV).manual_seed(5)
+    g["g_out"] = torch.randn(w.shape, generator=gen, device=DEV)
+    g["g_var"] = torch.randn(w.shape, generator=gen, device=DEV)
+    res = dict(zip(NAMES, mixer_bwd(*(g[n] for n in TOKEN), g["a"], g["p"], g["g_out"],
+                                    g["g_var"], g["lam0"], g["eta0"])))
+    torch.cuda.synchronize(DEV)
+    rng = np.random.default_rng(2)
+    qs = np.array(sorted(set(rng.choice(w.channels, 256, replace=False).tolist())
+                         | {0, w.channels - 1}))
+
+    def gather(x):
+        flat = x.reshape(w.B * w.H, w.T, w.D)
+        qd = torch.as_tensor(qs, device=x.device)
+        return flat[qd // w.D, :, qd % w.D].transpose(0, 1).reshape(1, 1, w.T, -1).contiguous()
+
+    sub = {n: gather(g[n]).cpu() for n in TOKEN + ("g_out", "g_var")}
+    hd = torch.as_tensor(qs % (w.H * w.D), device=DEV)
+    sub["a"] = g["a"].reshape(-1)[hd].reshape(1, -1).cpu()
+    sub["p"] = g["p"].reshape(-1)[hd].reshape(1, -1).cpu()
+    qd = torch.as_tensor(qs, device=DEV)
+    sub["lam0"] = g["lam0"].reshape(-1)[qd].reshape(1, 1, -1).cpu()
+    sub["eta0"] = g["eta0"].reshape(-1)[qd].reshape(1, 1, -1).cpu()
+    grads, mags = oracle(sub)
+    got = {n: gather(res[n]).cpu() for n in TOKEN}
+    got["lam0"] = res["lam0"].reshape(-1)[qd].reshape(1, 1, -1).cpu()
+    got["eta0"] = res["eta0"].reshape(-1)[qd].reshape(1, 1, -1).cpu()
+    rep = compare_grads(got, {n: grads[n] for n in got}, {n: mags[n] for n in got})
+    _say("sampled: %s" % rep)
+    assert_grad_parity(rep, TOL_BF16, w.describe())
+    assert bool(torch.isfinite(res["a"]).all()) and bool(torch.isfinite(res["p"]).all())
+
+
+def test_kla_mixer_autograd():
+    """torch.autograd through KLAMixer equals the oracle's gradients of
+    sum(g_out * out + g_var * var)."""
+    from linear_attention_sequence_kla_amd import kla_mixer
+    shape = (2, 3, 500, 24)
+    g = _case(shape, seed=12)
+    leaves = {n: g[n].to(DEV).clone().requires_grad_(True) for n in NAMES}
+    out, var = kla_mixer(*(leaves[n] for n in NAMES))
+    ((out * g["g_out"].to(DEV)).sum() + (var * g["g_var"].to(DEV)).sum()).backward()
+    torch.cuda.synchronize(DEV)
+    grads, mags = oracle(g)
+    rep = compare_grads({n: leaves[n].grad.cpu() for n in NAMES}, grads, mags)
+    _say("autograd: %s" % rep)
+    assert_grad_parity(rep, TOL_F32, "autograd")
+
+
+def test_mixer_bwd_argument_errors_on_device():
+    from linear_attention_sequence_kla_amd import mixer_bwd
+    g = {n: (None if t is None else t.to(DEV)) for n, t in _case((1, 2, 8, 4), seed=1).items()}
+    with pytest.raises(ValueError):
+        mixer_bwd(g["k"], g["v"], g["lam_v"], g["q"], g["a"], g["p"], None)
+    with pytest.raises(ValueError):
+        mixer_bwd(g["k"], g["v"], g["lam_v"], g["q"], g["a"], g["p"],
+                  g["g_out"][:, :, :4].contiguous())
+    with pytest.raises(ValueError):
+        mixer_bwd(g["k"], g["v"], g["lam_v"], g["q"], g["a"][:1].contiguous(), g["p"],
+                  g["g_out"])

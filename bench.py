@@ -1,16 +1,20 @@
-"""Benchmark of the forward KLA scan (libkla) on one MI355X.
+"""Benchmark of the KLA scan (libkla) on one MI355X.
 
-A step is one kla_scan_fwd call over one batch of synthetic gates: the whole
-scan (chunk matrices, carry look-back, replay and output writes) in a single
-kernel launch.  The K timed steps are captured once into a HIP graph and
-replayed (--no-graph launches them one by one).  Inputs are generated on the GPU and are resident in HBM
-before timing; two input/output sets alternate so that the 256 MB Infinity
-Cache cannot serve one step from the previous one.
+The headline (default) is the forward scan: a step is one kla_scan_fwd call
+over one batch of synthetic gates, the whole scan (chunk matrices, carry
+look-back, replay and output writes) in a single kernel launch.  --direction
+selects the backward scan, the fused mixer (forward or backward), the
+time-invariant form or the decode step instead.  The K timed steps are
+captured once into a HIP graph and replayed (--no-graph launches them one by
+one).  Inputs are generated on the GPU and are resident in HBM before timing;
+two input/output sets alternate so that the 256 MB Infinity Cache cannot
+serve one step from the previous one.
 
 Prints one JSON line: throughput in scanned elements (B*H*T*D) per second,
-the roofline of the scan kernel (HBM bound; algorithmic bytes are 4 gate
-reads + 2 float32 writes per element) and the float64 CPU oracle timed on a
-sample of the same workload as a baseline.
+the roofline of the kernel (HBM bound; for the forward scan the algorithmic
+bytes are 4 gate reads + 2 float32 writes per element), the HBM traffic from
+the committed rocprofv3 counters when they match the kernel source, and the
+float64 CPU oracle timed on a sample of the same workload as a baseline.
 """
 
 from __future__ import annotations
@@ -37,7 +41,7 @@ KERNEL_SOURCES = {"fwd": ("kla_scan_fwd.hip", "kla_lookback.h", "kla_internal.h"
 KERNEL_NAMES = {"fwd": "kla_scan_kernel", "bwd": "kla_scan_bwd_kernel",
                 "decode": "kla_decode_kernel", "mixer": "kla_scan_kernel",
                 "lti": "kla_scan_kernel", "mixer_bwd": "kla_mixer_bwd_kernel"}
-# the forward kernel template's last parameter selects the fused-mixer mode
+# the forward kernel template's last parameter is its mode (scan, mixer, LTI)
 KERNEL_SUFFIX = {"fwd": "Mode)0>", "mixer": "Mode)1>", "lti": "Mode)2>"}
 PROFILE_NAMES = {"fwd": "kla_scan_kernel", "bwd": "kla_scan_bwd_kernel",
                  "decode": "kla_decode_kernel", "mixer": "kla_scan_kernel_mixer",

@@ -451,7 +451,7 @@ kla_status kla_mixer_fwd(const void* k, const void* v, const void* lam_v, const 
     if (!out) return fail(KLA_ERR_INVALID_ARG, "out is NULL");
     if (!lam_T != !eta_T)
         return fail(KLA_ERR_INVALID_ARG, "lam_T and eta_T must both be given or both be NULL");
-    const void* f32s[9] = {a, p, lam0, eta0, out, var, lam_T, eta_T, nullptr};
+    const void* f32s[8] = {a, p, lam0, eta0, out, var, lam_T, eta_T};
     for (int i = 0; i < 8; ++i)
         if (f32s[i] && misaligned(f32s[i], 4))
             return fail(KLA_ERR_UNSUPPORTED, "float32 arguments must be 4-byte aligned");
@@ -459,14 +459,13 @@ kla_status kla_mixer_fwd(const void* k, const void* v, const void* lam_v, const 
 
     const size_t in_bytes = size_t(pl.N) * esz, out_bytes = size_t(pl.N) * 4;
     const size_t st_bytes = size_t(pl.C) * 4, ch_bytes = size_t(H * D) * 4;
-    const Buffer bufs[14] = {{k, in_bytes, "k", false},           {v, in_bytes, "v", false},
+    const Buffer bufs[13] = {{k, in_bytes, "k", false},           {v, in_bytes, "v", false},
                              {lam_v, in_bytes, "lam_v", false},   {q, in_bytes, "q", false},
                              {a, ch_bytes, "a", false},           {p, ch_bytes, "p", false},
                              {lam0, st_bytes, "lam0", false},     {eta0, st_bytes, "eta0", false},
                              {out, out_bytes, "out", true},       {var, out_bytes, "var", true},
                              {lam_T, st_bytes, "lam_T", true},    {eta_T, st_bytes, "eta_T", true},
-                             {workspace, pl.ws.bytes, "workspace", true},
-                             {nullptr, 0, "", false}};
+                             {workspace, pl.ws.bytes, "workspace", true}};
     if ((st = check_overlaps(bufs, 13)) != KLA_OK) return st;
 
     kla::FwdArgs args = {};

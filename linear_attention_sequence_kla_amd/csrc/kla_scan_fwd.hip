@@ -33,17 +33,23 @@
 //     matrices of the waves before it, then replays its rows sequentially from
 //     on-chip data, writing lam and eta.
 //
-// Mixer mode (the same kernel with Mixer = true) is the fused KLA mixer: the
-// inputs are the token tensors k, v, lam_v, q and per-channel gates (a, p);
-// phi = k^2 lam_v and b = k lam_v v are formed on the fly (token_gates), and
-// the replay writes the readout q * eta / lam = q * Y / X and the variance
-// 1 / lam = Z / X instead of lam and eta, so no gate or state tensor crosses
-// HBM.
+// The kernel has four modes (template parameter Mode):
+//   * Scan: the four token inputs are the gates a, p, phi, b; writes lam, eta.
+//   * Mixer: the fused KLA mixer.  The inputs are the token tensors k, v,
+//     lam_v, q and per-channel gates (a, p); phi = k^2 lam_v and b = k lam_v v
+//     are formed on the fly (token_gates), and the replay writes the readout
+//     q * eta / lam = q * Y / X and the variance 1 / lam = Z / X, so no gate
+//     or state tensor crosses HBM.
+//   * MixerState: the mixer's gates, writing lam and eta (the states its
+//     backward pass needs); q is not read.
+//   * Lti: per-channel (a, p, phi) and the token's b only (time-invariant
+//     gates; one input row per token, so 64 rows per wave).
 //
 // Arithmetic is float64 for everything carried (chunk matrices, states): the
 // exact precision can reach 1e88 and the information mean 1e-51 on hard gates,
 // beyond float32's exponent range, and on gfx950 a float64 FMA issues at the
-// same rate as an unpacked float32 FMA.  Inputs and outputs stay 32-bit.
+// same rate as an unpacked float32 FMA.  Inputs are float32 or bfloat16 and
+// outputs float32.
 
 #include "kla_internal.h"
 
@@ -171,7 +177,8 @@ __device__ inline void token_gates(float x0, float x1, float x2, float x3, doubl
 }
 
 template <typename In, int L, int W, Mode M>
-__global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(3))) void kla_scan_kernel(FwdArgs g) {
+__global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(3)))
+void kla_scan_kernel(FwdArgs g) {
     constexpr bool kMixer = M == Mode::Mixer;
     constexpr bool kAll = M != Mode::Lti;            // the first three token inputs are read
     constexpr bool kFourth = M != Mode::MixerState;  // the fourth one is read
@@ -195,10 +202,12 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(3))) 
         const LaneMap lm = lane_map(grp, t0, lane, g.T, g.D, g.C);
         const uint32_t in_row = uint32_t(g.D * sizeof(In));
         const uint32_t out_row = uint32_t(g.D * sizeof(float));
-        const char* pa = static_cast<const char*>(g.in[0]) + lm.e0 * int64_t(sizeof(In));
-        const char* pp = static_cast<const char*>(g.in[1]) + lm.e0 * int64_t(sizeof(In));
-        const char* pf = static_cast<const char*>(g.in[2]) + lm.e0 * int64_t(sizeof(In));
-        const char* pb = static_cast<const char*>(g.in[3]) + lm.e0 * int64_t(sizeof(In));
+        // (inputs a mode does not read are NULL and get no address)
+        const int64_t in_base = lm.e0 * int64_t(sizeof(In));
+        const char* pa = kAll ? static_cast<const char*>(g.in[0]) + in_base : nullptr;
+        const char* pp = kAll ? static_cast<const char*>(g.in[1]) + in_base : nullptr;
+        const char* pf = kAll ? static_cast<const char*>(g.in[2]) + in_base : nullptr;
+        const char* pb = kFourth ? static_cast<const char*>(g.in[3]) + in_base : nullptr;
         // mixer and LTI modes: the channel's time-invariant gates
         double ac = 1.0, pc = 0.0, fc = 0.0;
         if constexpr (M != Mode::Scan) {

@@ -227,10 +227,21 @@ def cpu_baseline(w, g_dev, budget_s: float = 10.0):
         oracle_scan(sel["a"], sel["p"], sel["phi"], sel["b"], lam0, eta0, nthreads=used)
         t_total += time.perf_counter() - t0
         reps += 1
+    # one thread, on one slab
+    one = {k: v[:, :1] for k, v in sel.items()}
+    reps1, t1 = 0, 0.0
+    while t1 < budget_s / 4 and reps1 < 100000:
+        t0 = time.perf_counter()
+        oracle_scan(one["a"], one["p"], one["phi"], one["b"], lam0[:, :1], eta0[:, :1],
+                    nthreads=1)
+        t1 += time.perf_counter() - t0
+        reps1 += 1
     return {"value": elems * reps / t_total, "unit": "elements/s", "cores": used,
             "kind": "oracle",
             "sample": "%d of %d slabs (all %d channels, full T=%d), %d runs, %.1f s"
-                      % (n_slabs, slabs_total, w.D, w.T, reps, t_total)}
+                      % (n_slabs, slabs_total, w.D, w.T, reps, t_total),
+            "value_1thread": per_slab * reps1 / t1,
+            "sample_1thread": "1 slab, %d runs, %.1f s, 1 thread" % (reps1, t1)}
 
 
 def main(argv=None):
@@ -391,6 +402,16 @@ def main(argv=None):
         torch.cuda.synchronize(dev)
         wall = time.perf_counter() - t0
         kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    # outside the timed region: the per-launch distribution of eager launches
+    n_eager = min(20, max(1, args.steps))
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n_eager)]
+    for i, (e0, e1) in enumerate(ev):
+        e0.record(stream)
+        step(i)
+        e1.record(stream)
+    torch.cuda.synchronize(dev)
+    eager_ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
     health = workspace_health(ws)
     if health != 0:
         print("warning: workspace health word %#x" % health, file=sys.stderr)
@@ -423,6 +444,8 @@ def main(argv=None):
                      "kernel_ms_min": min(kernel_ms), "bytes_per_element": bpe},
         "health": health,
         "launch": "hip graph of %d launches" % args.steps if args.graph else "eager",
+        "eager_launch_ms": {"median": eager_ms[len(eager_ms) // 2], "min": eager_ms[0],
+                            "max": eager_ms[-1], "launches": n_eager},
     }
     if d == "bwd":
         rec["metric"] = "KLA backward scan elements (B*H*T*D)/s and achieved HBM GB/s vs peak"

@@ -1,4 +1,7 @@
-"""Builds libkla.so (the HIP kernels and the C ABI) in-tree for gfx950.
+"""Builds libkla.so (the HIP kernels and the C ABI) in-tree for gfx950, and
+libkla_debug.so, the same library with pseudo-random pauses before every
+carry flag is published (a test build that forces the look-back through all
+its orders; see kla_lookback.h).
 
     python -m linear_attention_sequence_kla_amd.build
 """
@@ -15,6 +18,7 @@ SOURCES = [os.path.join(HERE, "csrc", f)
            for f in ("kla_api.cpp", "kla_scan_fwd.hip", "kla_scan_bwd.hip", "kla_decode.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "libkla.so")
+DEBUG_LIBRARY = os.path.join(HERE, "libkla_debug.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -42,6 +46,11 @@ def build(out: str = LIBRARY, extra=(), verbose: bool = False) -> str:
     return out
 
 
+def build_debug(verbose: bool = False) -> str:
+    return build(DEBUG_LIBRARY, extra=("-DKLA_DEBUG_DELAYS",), verbose=verbose)
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_debug(verbose=True))
     sys.exit(0)

@@ -94,10 +94,25 @@ __device__ inline double rec_load(double* p) {
         reinterpret_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
 }
 
+#ifdef KLA_DEBUG_DELAYS
+// Test builds only (libkla_debug.so): a pause of 0..15 x 127 sleep units,
+// pseudo-random per flag and call, before a flag is published, so that
+// look-backs meet predecessors in every state (not yet published, aggregate
+// only, inclusive late) and walk back over several tiles.
+__device__ inline void debug_delay(const uint64_t* flag, uint64_t value) {
+    const uint64_t x = (reinterpret_cast<uintptr_t>(flag) >> 3) ^ (value >> 32) * 0x9e3779b9u;
+    const uint32_t n = uint32_t((x * 0x9e3779b97f4a7c15ull) >> 60);
+    for (uint32_t i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(127);
+}
+#endif
+
 // Publishes a flag once every record store of this wave has completed.  The
 // records are agent-coherent atomics, so completion (vmcnt reaching zero) is
 // visibility to every other workgroup; no L2 write-back is needed.
 __device__ inline void publish(uint64_t* flag, int lane, uint64_t value) {
+#ifdef KLA_DEBUG_DELAYS
+    debug_delay(flag, value);
+#endif
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (lane == 0) __hip_atomic_store(flag, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

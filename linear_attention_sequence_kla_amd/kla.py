@@ -39,48 +39,52 @@ def library() -> ctypes.CDLL:
     """Loads libkla.so (built by ``python -m linear_attention_sequence_kla_amd.build``)."""
     global _lib
     with _lock:
-        if _lib is not None:
-            return _lib
-        if not os.path.exists(LIBRARY):
-            raise RuntimeError(
-                "libkla.so is not built (%s); run __graft_entry__.build() or "
-                "python -m linear_attention_sequence_kla_amd.build" % LIBRARY)
-        lib = ctypes.CDLL(LIBRARY)
-        vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
-        lib.kla_scan_fwd_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int]
-        lib.kla_scan_fwd_workspace_size.restype = sz
-        lib.kla_scan_fwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, vp,
+        if _lib is None:
+            _lib = load_library(LIBRARY)
+        return _lib
+
+
+def load_library(path: str) -> ctypes.CDLL:
+    """Loads a build of libkla from `path` and declares its entry points."""
+    if not os.path.exists(path):
+        raise RuntimeError(
+            "%s is not built; run __graft_entry__.build() or "
+            "python -m linear_attention_sequence_kla_amd.build" % path)
+    lib = ctypes.CDLL(path)
+    vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    lib.kla_scan_fwd_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+    lib.kla_scan_fwd_workspace_size.restype = sz
+    lib.kla_scan_fwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, vp,
+                                 i64, i64, i64, i64, vp, sz, vp]
+    lib.kla_scan_fwd.restype = ctypes.c_int
+    lib.kla_scan_bwd_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+    lib.kla_scan_bwd_workspace_size.restype = sz
+    lib.kla_scan_bwd.argtypes = [vp, vp, ctypes.c_int] + [vp] * 12 + [i64] * 4 + [vp, sz, vp]
+    lib.kla_scan_bwd.restype = ctypes.c_int
+    lib.kla_mixer_fwd_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+    lib.kla_mixer_fwd_workspace_size.restype = sz
+    lib.kla_mixer_fwd.argtypes = [vp, vp, vp, vp, ctypes.c_int] + [vp] * 8 + [i64] * 4 + [
+        vp, sz, vp]
+    lib.kla_mixer_fwd.restype = ctypes.c_int
+    lib.kla_scan_lti_fwd_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+    lib.kla_scan_lti_fwd_workspace_size.restype = sz
+    lib.kla_scan_lti_fwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, vp,
                                      i64, i64, i64, i64, vp, sz, vp]
-        lib.kla_scan_fwd.restype = ctypes.c_int
-        lib.kla_scan_bwd_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int]
-        lib.kla_scan_bwd_workspace_size.restype = sz
-        lib.kla_scan_bwd.argtypes = [vp, vp, ctypes.c_int] + [vp] * 12 + [i64] * 4 + [vp, sz, vp]
-        lib.kla_scan_bwd.restype = ctypes.c_int
-        lib.kla_mixer_fwd_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int]
-        lib.kla_mixer_fwd_workspace_size.restype = sz
-        lib.kla_mixer_fwd.argtypes = [vp, vp, vp, vp, ctypes.c_int] + [vp] * 8 + [i64] * 4 + [
-            vp, sz, vp]
-        lib.kla_mixer_fwd.restype = ctypes.c_int
-        lib.kla_scan_lti_fwd_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int]
-        lib.kla_scan_lti_fwd_workspace_size.restype = sz
-        lib.kla_scan_lti_fwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, vp,
-                                         i64, i64, i64, i64, vp, sz, vp]
-        lib.kla_scan_lti_fwd.restype = ctypes.c_int
-        lib.kla_mixer_bwd_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int]
-        lib.kla_mixer_bwd_workspace_size.restype = sz
-        lib.kla_mixer_bwd.argtypes = [vp, vp, vp, vp, ctypes.c_int] + [vp] * 14 + [i64] * 4 + [
-            vp, sz, vp]
-        lib.kla_mixer_bwd.restype = ctypes.c_int
-        lib.kla_decode_step.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, vp, i64, vp]
-        lib.kla_decode_step.restype = ctypes.c_int
-        lib.kla_workspace_health.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), vp]
-        lib.kla_workspace_health.restype = ctypes.c_int
-        lib.kla_status_string.argtypes = [ctypes.c_int]
-        lib.kla_status_string.restype = ctypes.c_char_p
-        lib.kla_last_error_detail.argtypes = []
-        lib.kla_last_error_detail.restype = ctypes.c_char_p
-        _lib = lib
-        return lib
+    lib.kla_scan_lti_fwd.restype = ctypes.c_int
+    lib.kla_mixer_bwd_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+    lib.kla_mixer_bwd_workspace_size.restype = sz
+    lib.kla_mixer_bwd.argtypes = [vp, vp, vp, vp, ctypes.c_int] + [vp] * 14 + [i64] * 4 + [
+        vp, sz, vp]
+    lib.kla_mixer_bwd.restype = ctypes.c_int
+    lib.kla_decode_step.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, vp, i64, vp]
+    lib.kla_decode_step.restype = ctypes.c_int
+    lib.kla_workspace_health.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), vp]
+    lib.kla_workspace_health.restype = ctypes.c_int
+    lib.kla_status_string.argtypes = [ctypes.c_int]
+    lib.kla_status_string.restype = ctypes.c_char_p
+    lib.kla_last_error_detail.argtypes = []
+    lib.kla_last_error_detail.restype = ctypes.c_char_p
+    return lib
 
 
 def _check(status: int):

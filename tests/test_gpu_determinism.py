@@ -1,0 +1,55 @@
+"""Bitwise reproducibility.  A tile's carry-in is the same sequence of float64
+operations whichever way the look-back reaches it (the inclusive state of its
+predecessor, or an older inclusive state with the intervening tile matrices
+applied one by one: each application is exactly the step that produced the
+predecessor's state), and the channel-gate gradients of the mixer are added
+in a fixed order.  So repeated calls -- and calls through the debug build,
+whose pauses force other look-back paths -- give identical bits."""
+
+from __future__ import annotations
+
+import os
+
+import pytest
+import torch
+
+from kla_inputs import make_gates, make_initial_state, make_lti_inputs, make_mixer_inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def _run_all():
+    from linear_attention_sequence_kla_amd import (mixer_bwd, mixer_fwd, scan_bwd, scan_fwd,
+                                                   scan_lti_fwd)
+    shape = (2, 3, 4000, 64)
+    g = {n: v.to(DEV) for n, v in make_gates(shape, "std", "f32", seed=1).items()}
+    lam0, eta0 = (x.to(DEV) for x in make_initial_state(2, 3, 64, random=True, seed=1))
+    gen = torch.Generator(device=DEV).manual_seed(2)
+    up = [torch.randn(shape, generator=gen, device=DEV) for _ in range(2)]
+    lam, eta = scan_fwd(g["a"], g["p"], g["phi"], g["b"], lam0, eta0)
+    grads = scan_bwd(g["a"], g["p"], lam, eta, up[0], up[1], lam0, eta0)
+    m = {n: v.to(DEV) for n, v in make_mixer_inputs(shape, "f32", seed=3).items()}
+    out, var, lam_T, eta_T = mixer_fwd(m["k"], m["v"], m["lam_v"], m["q"], m["a"], m["p"],
+                                       lam0, eta0, want_state=True)
+    mgrads = mixer_bwd(m["k"], m["v"], m["lam_v"], m["q"], m["a"], m["p"], up[0], up[1], lam0,
+                       eta0)
+    t = {n: v.to(DEV) for n, v in make_lti_inputs(shape, "std", "f32", seed=4).items()}
+    lt = scan_lti_fwd(t["a"], t["p"], t["phi"], t["b"], lam0, eta0)
+    torch.cuda.synchronize(DEV)
+    return [x.clone() for x in (lam, eta, *grads, out, var, lam_T, eta_T, *mgrads, *lt)]
+
+
+def test_repeated_calls_are_bitwise_identical(monkeypatch):
+    first = _run_all()
+    for _ in range(2):
+        again = _run_all()
+        for i, (x, y) in enumerate(zip(first, again)):
+            assert torch.equal(x, y), "output %d differs between calls" % i
+    from linear_attention_sequence_kla_amd import kla
+    monkeypatch.setattr(kla, "_lib", kla.load_library(os.path.join(kla.HERE, "libkla_debug.so")))
+    monkeypatch.setattr(kla, "_workspaces", {})
+    delayed = _run_all()
+    for i, (x, y) in enumerate(zip(first, delayed)):
+        assert torch.equal(x, y), "output %d differs under other look-back orders" % i

@@ -175,3 +175,20 @@ def test_mixer_argument_errors_on_device():
         mixer_fwd(g["k"], g["v"], g["lam_v"].double(), g["q"], g["a"], g["p"])
     with pytest.raises(ValueError):
         mixer_fwd(g["k"], g["v"], g["lam_v"], g["q"], g["a"], g["p"].double())
+
+
+def test_mixer_edge_values():
+    """Missing observations (lam_v = 0), a zero observation operator, a zero
+    readout operator (the output must be exactly 0) and very precise
+    observations (lam_v = 1e4) in one sequence."""
+    shape = (2, 2, 900, 24)
+    g = make_mixer_inputs(shape, "f32", seed=31)
+    gen = torch.Generator().manual_seed(32)
+    r = torch.rand(shape, generator=gen)
+    g["lam_v"] = torch.where(r < 0.25, torch.zeros(()), g["lam_v"])
+    g["lam_v"] = torch.where((r > 0.9), torch.full((), 1e4), g["lam_v"])
+    g["k"] = torch.where((r > 0.25) & (r < 0.35), torch.zeros(()), g["k"])
+    g["q"] = torch.where((r > 0.5) & (r < 0.55), torch.zeros(()), g["q"])
+    g["lam0"], g["eta0"] = make_initial_state(2, 2, 24, random=True, seed=31)
+    rep = full_parity(g, TOL_F32, "edge values")
+    assert rep["zero_q_nonzero_out"] == 0

@@ -303,6 +303,11 @@ def main(argv=None):
         workspace_size)
 
     d = args.direction
+    if args.workload not in workloads_for(d):
+        print("no workload %d for --direction %s (workloads: %s)"
+              % (args.workload, d, ", ".join(map(str, sorted(workloads_for(d))))),
+              file=sys.stderr)
+        return 2
     w = workloads_for(d)[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -313,8 +313,14 @@ __global__ __launch_bounds__(W * kWave) void kla_scan_bwd_kernel(BwdArgs g) {
 // the channel gates a, p collect their per-token adjoints (as g_a, g_p of
 // the kernel above) into one sum per tile and lane, added over the batch and
 // the chunks by kla_mixer_grad_reduce_kernel.
+//
+// Four waves per SIMD (two workgroups of eight waves per CU) are asked for
+// explicitly: left to itself the compiler gives the bfloat16 instance a few
+// registers more than 128, which halves the workgroups per CU and costs a
+// quarter of the bandwidth on bfloat16 inputs.
 template <typename In, int L, int W>
-__global__ __launch_bounds__(W * kWave) void kla_mixer_bwd_kernel(MixerBwdArgs g) {
+__global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(4)))
+void kla_mixer_bwd_kernel(MixerBwdArgs g) {
     __shared__ double s_adj[W][6][kWave];
     __shared__ double s_carry[W][2][kWave];
     __shared__ double s_part[W][2][kWave];

@@ -3,9 +3,12 @@
 // Garland, "Single-pass Parallel Prefix Scan with Decoupled Look-back", 2016),
 // as it runs on gfx950.
 //
-// A scan is cut into tiles; tile k's carry depends only on tiles with lower
-// ids, and tiles are workgroup ids.  Workgroups are dispatched in increasing
-// id, so every tile a workgroup waits for belongs to one already running.
+// A scan is cut into tiles; tile k's carry depends only on tiles k - G,
+// k - 2G, ... (the same column group in earlier chunks; G >= 1 column
+// groups).  Workgroups are dispatched in increasing id and run the tile
+// tile_of_workgroup() assigns them, which never places a tile a workgroup
+// waits for on a higher workgroup id, so every such tile belongs to a
+// workgroup already running.
 //
 // Workspace (caller-owned, zero-filled before first use, self-resetting):
 //   [0, 256)        header: u32 reserved[2], u32 epoch, u32 health
@@ -182,6 +185,23 @@ __device__ inline double pow2_scale(double x, int e) { return __builtin_amdgcn_l
 // -e such that max(|values|) * 2^-e lies in [0.5, 1).
 __device__ inline int renorm_exponent(double max_abs) {
     return -__builtin_amdgcn_frexp_exp(max_abs);
+}
+
+// The tile workgroup `wg` runs.  gfx950 hands workgroups to its eight XCDs
+// (each with its own L2) in turn, by workgroup id modulo 8, so tiles k and
+// k + 1 land on different XCDs.  When a slab row spans several 64-channel
+// groups (D a multiple of 128), column groups 2m and 2m + 1 of a chunk read
+// and write the two halves of the same rows; they are given to workgroups
+// with ids x and x + 8 of the same aligned block of 16 (x < 8), i.e. to the
+// same XCD, which measured 3-4% faster on such shapes.  The map permutes
+// each full block of 16 and leaves a partial last block alone; with G >= 16
+// a tile's predecessors (G or more tiles earlier) lie in earlier blocks,
+// hence on workgroups with lower ids.
+__device__ inline int64_t tile_of_workgroup(int64_t wg, int64_t G, int64_t D, int64_t n_tiles) {
+    if (D % 128 != 0 || G < 16) return wg;
+    const int64_t block = wg >> 4, r = wg & 15;
+    if ((block + 1) * 16 > n_tiles) return wg;
+    return block * 16 + (r & 7) * 2 + (r >> 3);
 }
 
 // Loads one gate from `base + off` (a byte offset) and widens it to float.

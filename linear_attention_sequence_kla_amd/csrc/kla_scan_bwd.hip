@@ -167,7 +167,7 @@ __global__ __launch_bounds__(W * kWave) void kla_scan_bwd_kernel(BwdArgs g) {
 
     const int lane = threadIdx.x & (kWave - 1);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int64_t ticket = blockIdx.x;
+    const int64_t ticket = tile_of_workgroup(blockIdx.x, g.G, g.D, g.n_tiles);
     uint32_t tag = 0;
 
     if (ticket < g.n_tiles) {
@@ -298,7 +298,7 @@ __global__ __launch_bounds__(W * kWave) void kla_scan_bwd_kernel(BwdArgs g) {
     }
 
     // ---- the last workgroup advances the epoch once every tile read it ----
-    if (ticket == int64_t(gridDim.x) - 1 && g.n_chunks > 1 && w == 0)
+    if (blockIdx.x == gridDim.x - 1 && g.n_chunks > 1 && w == 0)
         advance_epoch(g.ws, tag, (g.n_chunks - 1) * g.G, g.n_tiles, lane);
 }
 
@@ -327,7 +327,7 @@ void kla_mixer_bwd_kernel(MixerBwdArgs g) {
 
     const int lane = threadIdx.x & (kWave - 1);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int64_t ticket = blockIdx.x;
+    const int64_t ticket = tile_of_workgroup(blockIdx.x, g.G, g.D, g.n_tiles);
     uint32_t tag = 0;
 
     if (ticket < g.n_tiles) {
@@ -491,7 +491,7 @@ void kla_mixer_bwd_kernel(MixerBwdArgs g) {
     }
 
     // ---- the last workgroup advances the epoch once every tile read it ----
-    if (ticket == int64_t(gridDim.x) - 1 && g.n_chunks > 1 && w == 0)
+    if (blockIdx.x == gridDim.x - 1 && g.n_chunks > 1 && w == 0)
         advance_epoch(g.ws, tag, (g.n_chunks - 1) * g.G, g.n_tiles, lane);
 }
 

@@ -188,7 +188,7 @@ void kla_scan_kernel(FwdArgs g) {
 
     const int lane = threadIdx.x & (kWave - 1);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int64_t ticket = blockIdx.x;
+    const int64_t ticket = tile_of_workgroup(blockIdx.x, g.G, g.D, g.n_tiles);
     // This call's tag; only wave 0 (the look-back wave) needs it.  Its load
     // is issued after the tile loads so that it costs no extra latency.
     uint32_t tag = 0;
@@ -389,7 +389,7 @@ void kla_scan_kernel(FwdArgs g) {
     }
 
     // ---- the last workgroup advances the epoch once every tile read it ----
-    if (ticket == int64_t(gridDim.x) - 1 && g.n_chunks > 1 && w == 0)
+    if (blockIdx.x == gridDim.x - 1 && g.n_chunks > 1 && w == 0)
         advance_epoch(g.ws, tag, (g.n_chunks - 1) * g.G, g.n_tiles, lane);
 }
 

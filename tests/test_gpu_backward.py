@@ -66,6 +66,8 @@ SHAPES = [
     (1, 2, 333, 64, "hard", "f32"),
     (2, 2, 300, 128, "std", "bf16"),
     (1, 1, 2500, 65, "slow", "bf16"),
+    (3, 3, 700, 128, "std", "f32"),     # row halves paired per XCD, partial last block
+    (2, 5, 300, 256, "slow", "bf16"),
 ]
 
 

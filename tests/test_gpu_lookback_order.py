@@ -23,7 +23,7 @@ pytestmark = pytest.mark.gpu
 
 DEV = torch.device("cuda:0")
 # a few columns with long chains of tiles, and many columns
-SHAPES = [(1, 2, 9000, 64), (2, 2, 3000, 96)]
+SHAPES = [(1, 2, 9000, 64), (2, 2, 3000, 96), (3, 3, 2000, 128)]
 
 
 @pytest.fixture
@@ -65,11 +65,12 @@ def test_scan_forward_and_backward(debug_build, shape):
     assert_grad_parity(compare_grads(got, grads, mags), TOL_F32, "backward %s" % (shape,))
 
 
-def test_mixer_forward_and_backward(debug_build):
+@pytest.mark.parametrize("shape", [(1, 2, 6000, 64), (2, 4, 1500, 128)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_mixer_forward_and_backward(debug_build, shape):
     from linear_attention_sequence_kla_amd import mixer_bwd, mixer_fwd
-    shape = (1, 2, 6000, 64)
     g = make_mixer_inputs(shape, "f32", seed=4)
-    g["lam0"], g["eta0"] = make_initial_state(1, 2, 64, random=True, seed=4)
+    g["lam0"], g["eta0"] = make_initial_state(shape[0], shape[1], shape[3], random=True, seed=4)
     d = {n: v.to(DEV) for n, v in g.items()}
     out, var, _, _ = mixer_fwd(d["k"], d["v"], d["lam_v"], d["q"], d["a"], d["p"], d["lam0"],
                                d["eta0"])

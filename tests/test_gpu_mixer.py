@@ -108,7 +108,7 @@ def test_mixer_workload_full_size_sampled(key):
 
 SHAPES = [
     (1, 1, 1, 1), (1, 1, 5, 3), (2, 3, 113, 7), (1, 2, 337, 64), (3, 1, 450, 65),
-    (2, 2, 1000, 33), (1, 1, 2049, 128), (4, 3, 96, 40),
+    (2, 2, 1000, 33), (1, 1, 2049, 128), (4, 3, 96, 40), (3, 3, 500, 128),
 ]
 
 

@@ -67,7 +67,7 @@ def test_mixer_bwd_workload(key):
 
 
 SHAPES = [(1, 1, 1, 1), (1, 1, 7, 3), (2, 3, 113, 7), (1, 2, 337, 64), (3, 1, 450, 65),
-          (2, 2, 1000, 33), (1, 1, 2049, 128)]
+          (2, 2, 1000, 33), (1, 1, 2049, 128), (3, 3, 300, 128)]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))

@@ -112,6 +112,8 @@ SHAPES = [
     (2, 2, 300, 128, "std", "bf16"),     # bf16
     (1, 1, 5000, 200, "slow", "bf16"),   # bf16, ragged D > 64
     (5, 1, 64, 13, "hard", "f32"),       # T below one wave's rows
+    (3, 3, 1000, 128, "hard", "f32"),    # row halves paired per XCD, partial last block
+    (2, 5, 400, 256, "std", "bf16"),     # paired quarter rows, bf16
 ]
 
 

@@ -85,19 +85,20 @@ def bytes_per_element(dtype: str, direction: str = "fwd") -> int:
         return 4 * gate + 2 * 4
     if direction == "lti":  # b read (gates once per channel); lam, eta written
         return gate + 2 * 4
-    if direction == "mixer_bwd":  # the whole call: recompute, backward kernel, reduction
-        return 3 * gate + 2 * 4 + kernel_bytes_per_element(dtype, direction)
+    if direction == "mixer_bwd":  # the whole call: recompute (k, v, lam_v read, boundary
+        # states written), backward kernel, reduction
+        return 3 * gate + 2 + kernel_bytes_per_element(dtype, direction)
     return 2 * gate + 4 * 4 + 4 * 4
 
 
 def kernel_bytes_per_element(dtype: str, direction: str = "fwd") -> int:
     """Algorithmic bytes per element of the direction's dominant kernel.  For
-    mixer_bwd that is the backward kernel alone: k, v, lam_v, q, the states
-    lam, eta and the upstream g_out, g_var read; g_k, g_v, g_lam_v, g_q
-    written."""
+    mixer_bwd that is the backward kernel alone: k, v, lam_v, q, the float64
+    boundary state (16 bytes per 8 rows) and the upstream g_out, g_var read;
+    g_k, g_v, g_lam_v, g_q written."""
     if direction == "mixer_bwd":
         gate = 4 if dtype == "f32" else 2
-        return 4 * gate + 2 * 4 + 2 * 4 + 4 * 4
+        return 4 * gate + 2 + 2 * 4 + 4 * 4
     return bytes_per_element(dtype, direction)
 
 

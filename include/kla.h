@@ -255,8 +255,10 @@ KLA_API kla_status kla_mixer_fwd(const void *k, const void *v, const void *lam_v
  * d/deta = g_out q / lam, which run through the reverse scan of
  * kla_scan_bwd (the review's Theorems 1 and 2 differentiated); the gate
  * adjoints reach k, v, lam_v through phi = k^2 lam_v and b = k lam_v v.
- * The forward states are recomputed from the inputs (into the workspace),
- * so nothing needs saving between the forward and backward calls.
+ * The forward states are recomputed from the inputs (the float64 state
+ * after every 8th token goes into the workspace; the rows in between are
+ * replayed on chip), so nothing needs saving between the forward and
+ * backward calls.
  *
  *   k, v, lam_v, q, a, p, lam0, eta0   as passed to kla_mixer_fwd.
  *   g_out           device pointer, [B, H, T, D] float32.
@@ -266,7 +268,7 @@ KLA_API kla_status kla_mixer_fwd(const void *k, const void *v, const void *lam_v
  *                   in a fixed order: deterministic).
  *   g_lam0, g_eta0  device pointers, [B, H, D] float32, written; may be NULL.
  *   workspace       kla_mixer_bwd_workspace_size bytes (it holds the
- *                   recomputed states: about 8 bytes per element), zero-filled
+ *                   recomputed states: about 2 bytes per element), zero-filled
  *                   once before first use, as for kla_scan_fwd; it may also
  *                   serve the other entry points in turn.
  * A size-0 problem is a no-op.  Errors and stream semantics as for

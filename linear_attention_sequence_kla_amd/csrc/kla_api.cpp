@@ -121,11 +121,12 @@ kla_status check_workspace(void* workspace, size_t bytes, const Plan& pl) {
 }
 
 // Workspace of kla_mixer_bwd: the look-back region (shared in turn by the
-// forward recompute and the backward kernel), the recomputed states lam and
-// eta, and the per-tile sums of the channel-gate gradients.
+// forward recompute and the backward kernel), the recomputed float64 states
+// after every kMixBwdRows-th row, and the per-tile sums of the channel-gate
+// gradients.
 struct MixerBwdLayout {
     Plan fwd, bwd;
-    size_t off_lam, off_eta, off_partial, bytes;
+    size_t off_bstate, off_partial, bytes;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -136,10 +137,10 @@ bool mixer_bwd_layout(int64_t B, int64_t H, int64_t T, int64_t D, MixerBwdLayout
         !kla::make_plan(B, H, T, D, kla::kMixBwdRows, kla::kMixBwdWaves, kla::kBwdMatrixWords,
                         kla::kBwdStateWords, &l->bwd))
         return false;
-    const size_t states = align256(size_t(l->fwd.N) * 4);
-    l->off_lam = align256(l->fwd.ws.bytes > l->bwd.ws.bytes ? l->fwd.ws.bytes : l->bwd.ws.bytes);
-    l->off_eta = l->off_lam + states;
-    l->off_partial = l->off_eta + states;
+    const int64_t blocks = (T + kla::kMixBwdRows - 1) / kla::kMixBwdRows;
+    const size_t states = align256(size_t(blocks) * size_t(l->fwd.C) * 2 * sizeof(double));
+    l->off_bstate = align256(l->fwd.ws.bytes > l->bwd.ws.bytes ? l->fwd.ws.bytes : l->bwd.ws.bytes);
+    l->off_partial = l->off_bstate + states;
     l->bytes = l->off_partial + size_t(l->bwd.n_tiles) * 2 * kla::kWave * sizeof(double);
     return true;
 }
@@ -358,19 +359,17 @@ kla_status kla_mixer_bwd(const void* k, const void* v, const void* lam_v, const 
     if ((st = check_overlaps(bufs, 19)) != KLA_OK) return st;
 
     char* ws = static_cast<char*>(workspace);
-    float* lam = reinterpret_cast<float*>(ws + lay.off_lam);
-    float* eta = reinterpret_cast<float*>(ws + lay.off_eta);
+    double* bstate = reinterpret_cast<double*>(ws + lay.off_bstate);
     const hipStream_t s = static_cast<hipStream_t>(stream);
 
-    // 1. recompute the forward states
+    // 1. recompute the forward states at every kMixBwdRows-th row
     kla::FwdArgs fa = {};
     fa.in[0] = k;
     fa.in[1] = v;
     fa.in[2] = lam_v;
     fa.lam0 = lam0;
     fa.eta0 = eta0;
-    fa.lam = lam;
-    fa.eta = eta;
+    fa.bstate = bstate;
     fa.a_ch = a;
     fa.p_ch = p;
     fa.T = T;
@@ -394,8 +393,7 @@ kla_status kla_mixer_bwd(const void* k, const void* v, const void* lam_v, const 
     ba.p_ch = p;
     ba.lam0 = lam0;
     ba.eta0 = eta0;
-    ba.lam = lam;
-    ba.eta = eta;
+    ba.bstate = bstate;
     ba.g_out = g_out;
     ba.g_var = g_var;
     ba.g_k = g_k;

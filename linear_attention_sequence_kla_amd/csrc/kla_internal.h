@@ -46,6 +46,7 @@ struct FwdArgs {
     const float* phi_ch;   // LTI: [H, D]
     float* lam_T;          // mixer: final state [B, H, D] (may be NULL)
     float* eta_T;
+    double* bstate;        // mixer states: [ceil(T / kMixBwdRows)][C][2] float64
     int64_t T, D, C, G, n_chunks, n_tiles, HD;
     Workspace ws;
 };
@@ -75,14 +76,16 @@ constexpr int kLtiRows = 64, kLtiWaves = 4;
 constexpr int kMixBwdRows = 8, kMixBwdWaves = 8;
 constexpr int kBwdRows = 20, kBwdWaves = 4, kBwdMatrixWords = 6, kBwdStateWords = 2;
 
-// kMixerState: the mixer's gates, the scan's outputs (lam, eta), for the
-// mixer's backward pass.
+// kMixerState: the mixer's gates; writes the float64 states (lam, eta) after
+// every kMixBwdRows-th row into FwdArgs::bstate, for the mixer's backward
+// pass.
 enum class FwdMode { kScan, kMixer, kLti, kMixerState };
 hipError_t launch_scan_fwd(const FwdArgs& args, kla_dtype dtype, FwdMode mode, hipStream_t stream);
 hipError_t launch_scan_bwd(const BwdArgs& args, kla_dtype dtype, hipStream_t stream);
 
 // Fused-mixer backward: token inputs k, v, lam_v, q; channel gates a, p; the
-// forward states lam, eta (recomputed by the caller); upstream g_out, g_var.
+// forward boundary states (recomputed by the caller with kMixerState);
+// upstream g_out, g_var.
 // Writes g_k, g_v, g_lam_v, g_q, g_lam0, g_eta0 and, per tile and lane, the
 // tile's sums of the channel-gate gradients into `partial` ([tile][2][64]).
 struct MixerBwdArgs {
@@ -94,8 +97,7 @@ struct MixerBwdArgs {
     const float* p_ch;
     const float* lam0;   // may be NULL (1)
     const float* eta0;   // may be NULL (0)
-    const float* lam;    // forward states
-    const float* eta;
+    const double* bstate;  // forward states after every kMixBwdRows-th row (kMixerState)
     const float* g_out;
     const float* g_var;  // may be NULL (0)
     float* g_k;

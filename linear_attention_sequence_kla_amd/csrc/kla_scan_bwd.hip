@@ -314,6 +314,12 @@ __global__ __launch_bounds__(W * kWave) void kla_scan_bwd_kernel(BwdArgs g) {
 // the kernel above) into one sum per tile and lane, added over the batch and
 // the chunks by kla_mixer_grad_reduce_kernel.
 //
+// The forward states are not read per row: the recompute writes the float64
+// state after every L-th row (FwdMode::kMixerState), and each wave replays
+// its L rows forward from the state before its first row, which also yields
+// the readout adjoints; only float32 copies of the states stay in registers
+// for the reverse pass.
+//
 // Four waves per SIMD (two workgroups of eight waves per CU) are asked for
 // explicitly: left to itself the compiler gives the bfloat16 instance a few
 // registers more than 128, which halves the workgroups per CU and costs a
@@ -321,6 +327,7 @@ __global__ __launch_bounds__(W * kWave) void kla_scan_bwd_kernel(BwdArgs g) {
 template <typename In, int L, int W>
 __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(4)))
 void kla_mixer_bwd_kernel(MixerBwdArgs g) {
+    static_assert(L == kMixBwdRows, "the recompute keeps a state every kMixBwdRows rows");
     __shared__ double s_adj[W][6][kWave];
     __shared__ double s_carry[W][2][kWave];
     __shared__ double s_part[W][2][kWave];
@@ -349,25 +356,23 @@ void kla_mixer_bwd_kernel(MixerBwdArgs g) {
         const char* pq = static_cast<const char*>(g.q) + in_base;
         const char* pgo = reinterpret_cast<const char*>(g.g_out) + lm.e0 * 4;
         const char* pgv = reinterpret_cast<const char*>(g.g_var) + lm.e0 * 4;
-        const char* pl = reinterpret_cast<const char*>(g.lam) + lm.e0 * 4;  // lam_t
-        const char* pe = reinterpret_cast<const char*>(g.eta) + lm.e0 * 4;
         const int64_t hd = lm.qc % g.HD;
         const double ac = g.a_ch[hd], pc = g.p_ch[hd];
         char* oq = reinterpret_cast<char*>(g.g_q) + lm.e0 * 4;
 
-        // ---- load the rows; the readout's adjoints are formed here ----
-        // rl[i], re[i]: the state after row i (lam_t, eta_t); the state
-        // before the wave's first row is (l_in, e_in): row t0 - 1, or the
-        // initial state when the wave starts the sequence.
-        float rk[L], rv[L], rlv[L], rl[L], re[L], rgl[L], rge[L];
-        float l_in = 1.0f, e_in = 0.0f;
+        // ---- load the rows and the state before the wave's first row ----
+        // (row t0 - 1's boundary state, or the initial state at t0 = 0)
+        float rk[L], rv[L], rlv[L], rq[L], rgo[L], rgv[L];
+        double l_in = 1.0, e_in = 0.0;
         if (nr > 0) {
             if (t0 > 0) {
-                l_in = load_f32(pl - f_row, f_off);
-                e_in = load_f32(pe - f_row, f_off);
+                const double2 st = *reinterpret_cast<const double2*>(
+                    g.bstate + ((t0 / L - 1) * g.C + lm.qc) * 2);
+                l_in = st.x;
+                e_in = st.y;
             } else {
-                l_in = g.lam0 ? g.lam0[lm.qc] : 1.0f;
-                e_in = g.eta0 ? g.eta0[lm.qc] : 0.0f;
+                if (g.lam0) l_in = g.lam0[lm.qc];
+                if (g.eta0) e_in = g.eta0[lm.qc];
             }
 #pragma unroll
             for (int i = 0; i < L; ++i) {
@@ -377,50 +382,62 @@ void kla_mixer_bwd_kernel(MixerBwdArgs g) {
                 rk[i] = load_gate<In>(pk, io);
                 rv[i] = load_gate<In>(pv, io);
                 rlv[i] = load_gate<In>(plv, io);
-                rl[i] = load_f32(pl, fo);
-                re[i] = load_f32(pe, fo);
-                const double qv = load_gate<In>(pq, io);
-                const double go = load_f32(pgo, fo);
-                const double gv = g.g_var ? load_f32(pgv, fo) : 0.0f;
-                const double lt = rl[i], et = re[i];
-                const double rlt = recip(lt);
-                rgl[i] = float(-fma(go * qv, et, gv) * rlt * rlt);
-                rge[i] = float(go * qv * rlt);
-                if (i < nr && lm.valid)
-                    __builtin_nontemporal_store(float(go * et * rlt),
-                                                reinterpret_cast<float*>(oq + fo));
+                rq[i] = load_gate<In>(pq, io);
+                rgo[i] = load_f32(pgo, fo);
+                rgv[i] = g.g_var ? load_f32(pgv, fo) : 0.0f;
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < L; ++i) {
-                rk[i] = rv[i] = rlv[i] = 0.0f;
-                rl[i] = 1.0f;
-                re[i] = rgl[i] = rge[i] = 0.0f;
-            }
+            for (int i = 0; i < L; ++i) rk[i] = rv[i] = rlv[i] = rq[i] = rgo[i] = rgv[i] = 0.0f;
         }
         if (w == 0) tag = read_tag(g.ws);
 
-        // ---- the wave's map: per-token maps multiplied in time order ----
+        // ---- forward replay of the rows (float64): the states lam_t, eta_t,
+        // the readout's adjoints and g_q; and the wave's map, the per-token
+        // adjoint maps multiplied in time order ----
+        // rl[i], re[i]: the state after row i, kept as float32 for the
+        // reverse pass (which takes the state before row 0 from l_in, e_in).
+        float rl[L], re[L], rgl[L], rge[L];
         Adj m{1.0, 0.0, 0.0, 1.0, 0.0, 1.0};
+        {
+            double lp = l_in, ep = e_in;
 #pragma unroll
-        for (int i = 0; i < L; ++i) {
-            if (i < nr) {
-                const double lp = i ? rl[i - 1] : l_in, ep = i ? re[i - 1] : e_in;
-                const double rd = recip(fma(pc, lp, ac * ac));
-                const double f = ac * rd;
-                const double al = f * f;
-                const double be = -pc * f * ep * rd;
-                const double ge = rge[i];
-                const double o1 = fma(al, double(rgl[i]), be * ge);
-                const double o2 = f * ge;
-                const double nx = fma(m.u, o1, fma(m.v, o2, m.x));
-                m.v = fma(m.u, be, m.v * f);
-                m.u = m.u * al;
-                m.y = fma(m.w, o2, m.y);
-                m.w = m.w * f;
-                m.x = nx;
+            for (int i = 0; i < L; ++i) {
+                if (i < nr) {
+                    const double k = rk[i], lv = rlv[i];
+                    const double rd = recip(fma(pc, lp, ac * ac));
+                    const double f = ac * rd;
+                    const double lt = fma(lp, rd, k * k * lv);
+                    const double et = fma(f, ep, k * lv * double(rv[i]));
+                    const double rlt = recip(lt);
+                    const double go = rgo[i], gq = go * double(rq[i]);
+                    rgl[i] = float(-fma(gq, et, double(rgv[i])) * rlt * rlt);
+                    rge[i] = float(gq * rlt);
+                    if (lm.valid)
+                        __builtin_nontemporal_store(
+                            float(go * et * rlt),
+                            reinterpret_cast<float*>(oq + f_off + uint32_t(i) * f_row));
+                    const double al = f * f;
+                    const double be = -pc * f * ep * rd;
+                    const double ge = rge[i];
+                    const double o1 = fma(al, double(rgl[i]), be * ge);
+                    const double o2 = f * ge;
+                    const double nx = fma(m.u, o1, fma(m.v, o2, m.x));
+                    m.v = fma(m.u, be, m.v * f);
+                    m.u = m.u * al;
+                    m.y = fma(m.w, o2, m.y);
+                    m.w = m.w * f;
+                    m.x = nx;
+                    rl[i] = float(lt);
+                    re[i] = float(et);
+                    lp = lt;
+                    ep = et;
+                } else {
+                    rl[i] = 1.0f;
+                    re[i] = rgl[i] = rge[i] = 0.0f;
+                }
+                if ((i % kRenormEvery) == kRenormEvery - 1 || i == L - 1) renorm(m);
             }
-            if ((i % kRenormEvery) == kRenormEvery - 1 || i == L - 1) renorm(m);
         }
 #pragma unroll
         for (int i = 0; i < L; ++i)

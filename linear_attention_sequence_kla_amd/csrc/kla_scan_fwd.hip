@@ -40,8 +40,10 @@
 //     are formed on the fly (token_gates), and the replay writes the readout
 //     q * eta / lam = q * Y / X and the variance 1 / lam = Z / X, so no gate
 //     or state tensor crosses HBM.
-//   * MixerState: the mixer's gates, writing lam and eta (the states its
-//     backward pass needs); q is not read.
+//   * MixerState: the mixer's gates, writing the float64 state (lam, eta)
+//     after every kMixBwdRows-th row only (the boundary states from which
+//     the mixer's backward kernel recomputes its rows' states); q is not
+//     read.
 //   * Lti: per-channel (a, p, phi) and the token's b only (time-invariant
 //     gates; one input row per token, so 64 rows per wave).
 //
@@ -142,7 +144,7 @@ enum class Mode {
     Scan,   // a, p, phi, b per token -> lam, eta
     Mixer,  // k, v, lam_v, q per token, (a, p) per channel -> q eta / lam, 1 / lam
     Lti,    // b per token, (a, p, phi) per channel -> lam, eta
-    MixerState,  // k, v, lam_v per token, (a, p) per channel -> lam, eta
+    MixerState,  // k, v, lam_v per token, (a, p) per channel -> boundary (lam, eta)
 };
 
 // The float64 gates (a, p, phi, b) of one token.  Scan mode reads them from
@@ -356,7 +358,18 @@ void kla_scan_kernel(FwdArgs g) {
                 Y = fma(bb, zn, a * Y);
                 Z = zn;
                 const uint32_t off = lm.lane_el * uint32_t(sizeof(float)) + uint32_t(i) * out_row;
-                if constexpr (kMixer) {
+                if constexpr (M == Mode::MixerState) {
+                    // the state after rows kMixBwdRows * j - 1, j = 1, 2, ...
+                    // (the last row's is not needed), as float64 pairs
+                    // [j - 1][channel][lam, eta]
+                    const int64_t done = t0 + i + 1;
+                    if (done % kMixBwdRows == 0 && done < g.T && lm.valid) {
+                        const double r = recip(Z);
+                        double2* dst = reinterpret_cast<double2*>(
+                            g.bstate + ((done / kMixBwdRows - 1) * g.C + lm.q) * 2);
+                        *dst = make_double2(X * r, Y * r);
+                    }
+                } else if constexpr (kMixer) {
                     // readout: mean eta / lam = Y / X scaled by q, variance 1 / lam = Z / X
                     const double r = recip(X);
                     if (lm.valid) {

@@ -181,8 +181,10 @@ def test_mixer_bwd_workspace_size(lib):
     assert ws(1, 1, 1, 1, 9) == 0
     n = 8 * 16 * 2048 * 64
     big = ws(8, 16, 2048, 64, 0)
-    # holds the recomputed states (8 bytes per element) and the carry records
-    assert big >= 8 * n + lib.kla_scan_fwd_workspace_size(8, 16, 2048, 64, 0)
+    # holds the recomputed float64 states after every 8th row (2 bytes per
+    # element) and the carry records
+    assert big >= 2 * n + lib.kla_scan_fwd_workspace_size(8, 16, 2048, 64, 0)
+    assert big < 4 * n + lib.kla_scan_fwd_workspace_size(8, 16, 2048, 64, 0)
     assert big % 256 == 0
 
 

@@ -3,8 +3,8 @@
 The headline (default) is the forward scan: a step is one kla_scan_fwd call
 over one batch of synthetic gates, the whole scan (chunk matrices, carry
 look-back, replay and output writes) in a single kernel launch.  --direction
-selects the backward scan, the fused mixer (forward or backward), the
-time-invariant form or the decode step instead.  The K timed steps are
+selects the backward scan, the fused mixer (forward, backward, or a training
+step of both), the time-invariant form or the decode step instead.  The K timed steps are
 captured once into a HIP graph and replayed (--no-graph launches them one by
 one).  Inputs are generated on the GPU and are resident in HBM before timing;
 two input/output sets alternate so that the 256 MB Infinity Cache cannot
@@ -37,15 +37,18 @@ KERNEL_SOURCES = {"fwd": ("kla_scan_fwd.hip", "kla_lookback.h", "kla_internal.h"
                   "decode": ("kla_decode.hip", "kla_lookback.h", "kla_internal.h"),
                   "mixer": ("kla_scan_fwd.hip", "kla_lookback.h", "kla_internal.h"),
                   "lti": ("kla_scan_fwd.hip", "kla_lookback.h", "kla_internal.h"),
-                  "mixer_bwd": ("kla_scan_bwd.hip", "kla_lookback.h", "kla_internal.h")}
+                  "mixer_bwd": ("kla_scan_bwd.hip", "kla_lookback.h", "kla_internal.h"),
+                  "mixer_train": ("kla_scan_bwd.hip", "kla_lookback.h", "kla_internal.h")}
 KERNEL_NAMES = {"fwd": "kla_scan_kernel", "bwd": "kla_scan_bwd_kernel",
                 "decode": "kla_decode_kernel", "mixer": "kla_scan_kernel",
-                "lti": "kla_scan_kernel", "mixer_bwd": "kla_mixer_bwd_kernel"}
+                "lti": "kla_scan_kernel", "mixer_bwd": "kla_mixer_bwd_kernel",
+                "mixer_train": "kla_mixer_bwd_kernel"}
 # the forward kernel template's last parameter is its mode (scan, mixer, LTI)
 KERNEL_SUFFIX = {"fwd": "Mode)0>", "mixer": "Mode)1>", "lti": "Mode)2>"}
 PROFILE_NAMES = {"fwd": "kla_scan_kernel", "bwd": "kla_scan_bwd_kernel",
                  "decode": "kla_decode_kernel", "mixer": "kla_scan_kernel_mixer",
-                 "lti": "kla_scan_kernel_lti", "mixer_bwd": "kla_mixer_bwd_kernel"}
+                 "lti": "kla_scan_kernel_lti", "mixer_bwd": "kla_mixer_bwd_kernel",
+                 "mixer_train": "kla_mixer_bwd_kernel"}
 
 
 def is_kernel(name: str, direction: str) -> bool:
@@ -88,6 +91,9 @@ def bytes_per_element(dtype: str, direction: str = "fwd") -> int:
     if direction == "mixer_bwd":  # the whole call: recompute (k, v, lam_v read, boundary
         # states written), backward kernel, reduction
         return 3 * gate + 2 + kernel_bytes_per_element(dtype, direction)
+    if direction == "mixer_train":  # forward keeping the boundary states, then the backward
+        # from them (no recompute)
+        return 4 * gate + 2 * 4 + 2 + kernel_bytes_per_element(dtype, "mixer_bwd")
     return 2 * gate + 4 * 4 + 4 * 4
 
 
@@ -96,13 +102,15 @@ def kernel_bytes_per_element(dtype: str, direction: str = "fwd") -> int:
     mixer_bwd that is the backward kernel alone: k, v, lam_v, q, the float64
     boundary state (16 bytes per 8 rows) and the upstream g_out, g_var read;
     g_k, g_v, g_lam_v, g_q written."""
-    if direction == "mixer_bwd":
+    if direction in ("mixer_bwd", "mixer_train"):
         gate = 4 if dtype == "f32" else 2
         return 4 * gate + 2 + 2 * 4 + 4 * 4
     return bytes_per_element(dtype, direction)
 
 
 def traffic_path(workload_key: int, direction: str) -> str:
+    # a training step's dominant kernel is the mixer backward kernel
+    direction = {"mixer_train": "mixer_bwd"}.get(direction, direction)
     suffix = {"fwd": "", "bwd": "_bwd"}.get(direction, "_" + direction)
     return os.path.join(ROOT, "profiles", "traffic_workload%d%s.json" % (workload_key, suffix))
 
@@ -200,7 +208,7 @@ def summarize_counters(args):
 def workloads_for(direction: str):
     from kla_inputs import LTI_WORKLOADS, MIXER_WORKLOADS, WORKLOADS
     return {"mixer": MIXER_WORKLOADS, "mixer_bwd": MIXER_WORKLOADS,
-            "lti": LTI_WORKLOADS}.get(direction, WORKLOADS)
+            "mixer_train": MIXER_WORKLOADS, "lti": LTI_WORKLOADS}.get(direction, WORKLOADS)
 
 
 def cpu_baseline(w, g_dev, budget_s: float = 10.0):
@@ -253,12 +261,15 @@ def main(argv=None):
     ap.add_argument("--workload", type=int, default=1,
                     help="0..4; the headline is 1 (small-LM layer)")
     ap.add_argument("--sets", type=int, default=2, help="input/output sets to rotate")
-    ap.add_argument("--direction", choices=("fwd", "bwd", "decode", "mixer", "mixer_bwd", "lti"),
+    ap.add_argument("--direction",
+                    choices=("fwd", "bwd", "decode", "mixer", "mixer_bwd", "mixer_train", "lti"),
                     default="fwd",
                     help="fwd: kla_scan_fwd (the headline); bwd: kla_scan_bwd; decode: "
                          "kla_decode_step on one token of every channel of the workload; "
                          "mixer: kla_mixer_fwd on the mixer workload of the same key; "
                          "mixer_bwd: kla_mixer_bwd on the mixer workload; "
+                         "mixer_train: kla_mixer_fwd keeping its states, then kla_mixer_bwd "
+                         "from them (one training step of the layer); "
                          "lti: kla_scan_lti_fwd on the time-invariant workload of that key")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
@@ -300,8 +311,8 @@ def main(argv=None):
     from kla_inputs import make_lti_workload, make_mixer_workload, make_workload
     from linear_attention_sequence_kla_amd import (
         bwd_workspace_size, decode_step, get_workspace, lti_workspace_size, mixer_bwd,
-        mixer_bwd_workspace_size, mixer_fwd, scan_bwd, scan_fwd, scan_lti_fwd, workspace_health,
-        workspace_size)
+        mixer_bwd_workspace_size, mixer_fwd, mixer_states_shape, scan_bwd, scan_fwd,
+        scan_lti_fwd, workspace_health, workspace_size)
 
     d = args.direction
     if args.workload not in workloads_for(d):
@@ -320,7 +331,7 @@ def main(argv=None):
     sets = []
     for k in range(args.sets if d != "decode" else 0):
         make = {"mixer": make_mixer_workload, "mixer_bwd": make_mixer_workload,
-                "lti": make_lti_workload}.get(d, make_workload)
+                "mixer_train": make_mixer_workload, "lti": make_lti_workload}.get(d, make_workload)
         g = make(args.workload, device=dev, seed=w.seed + 1000 * k)
         lam = torch.empty(w.shape, dtype=torch.float32, device=dev)
         eta = torch.empty(w.shape, dtype=torch.float32, device=dev)
@@ -331,12 +342,15 @@ def main(argv=None):
             gen.manual_seed(w.seed + 77 + k)
             g["g_lam"] = torch.randn(w.shape, generator=gen, device=dev)
             g["g_eta"] = torch.randn(w.shape, generator=gen, device=dev)
-        if d == "mixer_bwd":
+        if d in ("mixer_bwd", "mixer_train"):
             # upstream gradients of the readout and the variance ~ N(0, 1)
             gen = torch.Generator(device=dev)
             gen.manual_seed(w.seed + 77 + k)
             g["g_out"] = torch.randn(w.shape, generator=gen, device=dev)
             g["g_var"] = torch.randn(w.shape, generator=gen, device=dev)
+        if d == "mixer_train":
+            g["states"] = torch.empty(mixer_states_shape(*w.shape), dtype=torch.float64,
+                                      device=dev)
         sets.append((g, (lam, eta)))
     if d == "decode":
         # one token per channel; the state is updated in place each step
@@ -349,7 +363,7 @@ def main(argv=None):
     grads = None
     if d == "bwd":
         grads = tuple(torch.empty(w.shape, dtype=torch.float32, device=dev) for _ in range(4))
-    if d == "mixer_bwd":
+    if d in ("mixer_bwd", "mixer_train"):
         grads = tuple(torch.empty(w.shape, dtype=torch.float32, device=dev) for _ in range(4)) + \
             tuple(torch.empty((w.H, w.D), dtype=torch.float32, device=dev) for _ in range(2))
     torch.cuda.synchronize(dev)
@@ -370,6 +384,12 @@ def main(argv=None):
         elif d == "mixer":
             mixer_fwd(g["k"], g["v"], g["lam_v"], g["q"], g["a"], g["p"], g["lam0"], g["eta0"],
                       out=out[0], var=out[1], workspace=ws)
+        elif d == "mixer_train":
+            mixer_fwd(g["k"], g["v"], g["lam_v"], g["q"], g["a"], g["p"], g["lam0"], g["eta0"],
+                      out=out[0], var=out[1], workspace=ws, states=g["states"])
+            mixer_bwd(g["k"], g["v"], g["lam_v"], g["q"], g["a"], g["p"], g["g_out"], g["g_var"],
+                      g["lam0"], g["eta0"], need_state_grads=False, workspace=ws, out=grads,
+                      states=g["states"])
         else:
             scan_bwd(g["a"], g["p"], out[0], out[1], g["g_lam"], g["g_eta"], g["lam0"],
                      g["eta0"], workspace=ws, out=grads)
@@ -463,6 +483,12 @@ def main(argv=None):
                                     "reduction); traffic is the backward kernel's alone")
         rec["metric"] = ("KLA fused mixer backward elements (B*H*T*D)/s and achieved HBM GB/s "
                          "vs peak (the whole call: state recompute, adjoint scan, reduction)")
+    if d == "mixer_train":
+        rec["roofline"]["scope"] = ("the whole step (mixer forward keeping the states, "
+                                    "backward kernel, reduction); traffic is the backward "
+                                    "kernel's alone")
+        rec["metric"] = ("KLA fused mixer training step (forward + backward) elements "
+                         "(B*H*T*D)/s and achieved HBM GB/s vs peak")
     if d == "mixer":
         rec["metric"] = ("KLA fused mixer elements (B*H*T*D)/s and achieved HBM GB/s vs peak "
                          "(gates, scan, readout and variance in one pass)")

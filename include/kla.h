@@ -231,6 +231,12 @@ KLA_API kla_status kla_scan_lti_fwd(const float *a, const float *p, const float 
  *   lam_T, eta_T    device pointers, [B, H, D] float32: the state after the
  *                   last token (pass it as lam0/eta0 of a following call);
  *                   both NULL or both given.
+ *   states          device pointer, 16-byte aligned, kla_mixer_states_size
+ *                   bytes, written; or NULL.  Receives the float64 pair
+ *                   (lam, eta) of every channel after every 8th token
+ *                   ([ceil(T / 8)][B * H * D][2]); a training caller keeps it
+ *                   and hands it to kla_mixer_bwd, which then skips its
+ *                   recompute of the forward states.
  *   workspace       kla_mixer_fwd_workspace_size bytes, same contract as for
  *                   kla_scan_fwd (one workspace serves both entry points).
  * Errors, stream semantics and the overflow rule as for kla_scan_fwd.
@@ -242,8 +248,12 @@ KLA_API kla_status kla_mixer_fwd(const void *k, const void *v, const void *lam_v
                                  const float *a, const float *p,
                                  const float *lam0, const float *eta0,
                                  float *out, float *var, float *lam_T, float *eta_T,
+                                 double *states,
                                  int64_t B, int64_t H, int64_t T, int64_t D,
                                  void *workspace, size_t workspace_bytes, void *stream);
+/* Bytes of kla_mixer_fwd's `states` output (0 for an empty or overflowing
+ * problem): 16 bytes per channel per 8 tokens, about 2 bytes per element. */
+KLA_API size_t kla_mixer_states_size(int64_t B, int64_t H, int64_t T, int64_t D);
 
 /*
  * Fused KLA mixer backward: the vector-Jacobian product of kla_mixer_fwd.
@@ -255,12 +265,15 @@ KLA_API kla_status kla_mixer_fwd(const void *k, const void *v, const void *lam_v
  * d/deta = g_out q / lam, which run through the reverse scan of
  * kla_scan_bwd (the review's Theorems 1 and 2 differentiated); the gate
  * adjoints reach k, v, lam_v through phi = k^2 lam_v and b = k lam_v v.
- * The forward states are recomputed from the inputs (the float64 state
- * after every 8th token goes into the workspace; the rows in between are
- * replayed on chip), so nothing needs saving between the forward and
- * backward calls.
+ * The backward kernel needs the float64 forward state after every 8th token
+ * and replays the rows in between on chip.  Given `states` (kept by
+ * kla_mixer_fwd on the same inputs) it uses them; with states NULL it first
+ * recomputes them from the inputs into the workspace, so nothing needs
+ * saving between the forward and backward calls.
  *
  *   k, v, lam_v, q, a, p, lam0, eta0   as passed to kla_mixer_fwd.
+ *   states          device pointer, as written by kla_mixer_fwd for these
+ *                   inputs, or NULL (recompute).  Read only.
  *   g_out           device pointer, [B, H, T, D] float32.
  *   g_var           device pointer, [B, H, T, D] float32, or NULL (zero).
  *   g_k, g_v, g_lam_v, g_q   device pointers, [B, H, T, D] float32, written.
@@ -280,6 +293,7 @@ KLA_API kla_status kla_mixer_bwd(const void *k, const void *v, const void *lam_v
                                  const void *q, kla_dtype in_dtype,
                                  const float *a, const float *p,
                                  const float *lam0, const float *eta0,
+                                 const double *states,
                                  const float *g_out, const float *g_var,
                                  float *g_k, float *g_v, float *g_lam_v, float *g_q,
                                  float *g_a, float *g_p, float *g_lam0, float *g_eta0,

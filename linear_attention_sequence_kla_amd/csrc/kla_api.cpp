@@ -131,14 +131,20 @@ struct MixerBwdLayout {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Bytes of the mixer's boundary states: the float64 pair (lam, eta) of every
+// channel after every kMixBwdRows-th token, [ceil(T / kMixBwdRows)][C][2].
+size_t mixer_states_bytes(const Plan& pl, int64_t T) {
+    const int64_t blocks = (T + kla::kMixBwdRows - 1) / kla::kMixBwdRows;
+    return size_t(blocks) * size_t(pl.C) * 2 * sizeof(double);
+}
+
 bool mixer_bwd_layout(int64_t B, int64_t H, int64_t T, int64_t D, MixerBwdLayout* l) {
     if (!kla::make_plan(B, H, T, D, kla::kFwdRows, kla::kFwdWaves, kla::kFwdMatrixWords,
                         kla::kFwdStateWords, &l->fwd) ||
         !kla::make_plan(B, H, T, D, kla::kMixBwdRows, kla::kMixBwdWaves, kla::kBwdMatrixWords,
                         kla::kBwdStateWords, &l->bwd))
         return false;
-    const int64_t blocks = (T + kla::kMixBwdRows - 1) / kla::kMixBwdRows;
-    const size_t states = align256(size_t(blocks) * size_t(l->fwd.C) * 2 * sizeof(double));
+    const size_t states = align256(mixer_states_bytes(l->fwd, T));
     l->off_bstate = align256(l->fwd.ws.bytes > l->bwd.ws.bytes ? l->fwd.ws.bytes : l->bwd.ws.bytes);
     l->off_partial = l->off_bstate + states;
     l->bytes = l->off_partial + size_t(l->bwd.n_tiles) * 2 * kla::kWave * sizeof(double);
@@ -305,7 +311,8 @@ size_t kla_mixer_bwd_workspace_size(int64_t B, int64_t H, int64_t T, int64_t D,
 
 kla_status kla_mixer_bwd(const void* k, const void* v, const void* lam_v, const void* q,
                          kla_dtype in_dtype, const float* a, const float* p, const float* lam0,
-                         const float* eta0, const float* g_out, const float* g_var, float* g_k,
+                         const float* eta0, const double* states, const float* g_out,
+                         const float* g_var, float* g_k,
                          float* g_v, float* g_lam_v, float* g_q, float* g_a, float* g_p,
                          float* g_lam0, float* g_eta0, int64_t B, int64_t H, int64_t T,
                          int64_t D, void* workspace, size_t workspace_bytes, void* stream) {
@@ -336,6 +343,8 @@ kla_status kla_mixer_bwd(const void* k, const void* v, const void* lam_v, const 
     for (int i = 0; i < 14; ++i)
         if (f32s[i] && misaligned(f32s[i], 4))
             return fail(KLA_ERR_UNSUPPORTED, "float32 arguments must be 4-byte aligned");
+    if (states && misaligned(states, 16))
+        return fail(KLA_ERR_UNSUPPORTED, "states is not 16-byte aligned");
     if (!workspace) return fail(KLA_ERR_WORKSPACE, "workspace is NULL");
     if (misaligned(workspace, 256))
         return fail(KLA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
@@ -345,7 +354,7 @@ kla_status kla_mixer_bwd(const void* k, const void* v, const void* lam_v, const 
 
     const size_t in_bytes = size_t(pl.N) * esz, f_bytes = size_t(pl.N) * 4;
     const size_t st_bytes = size_t(pl.C) * 4, ch_bytes = size_t(H * D) * 4;
-    const Buffer bufs[19] = {
+    const Buffer bufs[20] = {
         {k, in_bytes, "k", false},            {v, in_bytes, "v", false},
         {lam_v, in_bytes, "lam_v", false},    {q, in_bytes, "q", false},
         {a, ch_bytes, "a", false},            {p, ch_bytes, "p", false},
@@ -355,33 +364,40 @@ kla_status kla_mixer_bwd(const void* k, const void* v, const void* lam_v, const 
         {g_lam_v, f_bytes, "g_lam_v", true},  {g_q, f_bytes, "g_q", true},
         {g_a, ch_bytes, "g_a", true},         {g_p, ch_bytes, "g_p", true},
         {g_lam0, st_bytes, "g_lam0", true},   {g_eta0, st_bytes, "g_eta0", true},
-        {workspace, lay.bytes, "workspace", true}};
-    if ((st = check_overlaps(bufs, 19)) != KLA_OK) return st;
+        {workspace, lay.bytes, "workspace", true},
+        {states, mixer_states_bytes(lay.fwd, T), "states", false}};
+    if ((st = check_overlaps(bufs, 20)) != KLA_OK) return st;
 
     char* ws = static_cast<char*>(workspace);
-    double* bstate = reinterpret_cast<double*>(ws + lay.off_bstate);
     const hipStream_t s = static_cast<hipStream_t>(stream);
-
-    // 1. recompute the forward states at every kMixBwdRows-th row
-    kla::FwdArgs fa = {};
-    fa.in[0] = k;
-    fa.in[1] = v;
-    fa.in[2] = lam_v;
-    fa.lam0 = lam0;
-    fa.eta0 = eta0;
-    fa.bstate = bstate;
-    fa.a_ch = a;
-    fa.p_ch = p;
-    fa.T = T;
-    fa.D = D;
-    fa.C = lay.fwd.C;
-    fa.G = lay.fwd.G;
-    fa.n_chunks = lay.fwd.n_chunks;
-    fa.n_tiles = lay.fwd.n_tiles;
-    fa.HD = H * D;
-    fa.ws = kla::workspace_view(workspace, lay.fwd.ws);
-    hipError_t err = kla::launch_scan_fwd(fa, in_dtype, kla::FwdMode::kMixerState, s);
-    if (err != hipSuccess) return fail(KLA_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
+    hipError_t err = hipSuccess;
+    const double* bstate = states;
+    if (!bstate) {
+        // 1. recompute the forward states at every kMixBwdRows-th row (unless
+        //    the forward call kept them)
+        double* rec = reinterpret_cast<double*>(ws + lay.off_bstate);
+        bstate = rec;
+        kla::FwdArgs fa = {};
+        fa.in[0] = k;
+        fa.in[1] = v;
+        fa.in[2] = lam_v;
+        fa.lam0 = lam0;
+        fa.eta0 = eta0;
+        fa.bstate = rec;
+        fa.a_ch = a;
+        fa.p_ch = p;
+        fa.T = T;
+        fa.D = D;
+        fa.C = lay.fwd.C;
+        fa.G = lay.fwd.G;
+        fa.n_chunks = lay.fwd.n_chunks;
+        fa.n_tiles = lay.fwd.n_tiles;
+        fa.HD = H * D;
+        fa.ws = kla::workspace_view(workspace, lay.fwd.ws);
+        err = kla::launch_scan_fwd(fa, in_dtype, kla::FwdMode::kMixerState, s);
+        if (err != hipSuccess)
+            return fail(KLA_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
+    }
 
     // 2. the adjoint scan with the mixer's front and back ends
     kla::MixerBwdArgs ba;
@@ -426,11 +442,19 @@ size_t kla_mixer_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int64_t D,
     return kla_scan_fwd_workspace_size(B, H, T, D, in_dtype);
 }
 
+size_t kla_mixer_states_size(int64_t B, int64_t H, int64_t T, int64_t D) {
+    Plan pl;
+    if (!kla::make_plan(B, H, T, D, kla::kFwdRows, kla::kFwdWaves, kla::kFwdMatrixWords,
+                        kla::kFwdStateWords, &pl) || pl.N == 0)
+        return 0;
+    return mixer_states_bytes(pl, T);
+}
+
 kla_status kla_mixer_fwd(const void* k, const void* v, const void* lam_v, const void* q,
                          kla_dtype in_dtype, const float* a, const float* p, const float* lam0,
                          const float* eta0, float* out, float* var, float* lam_T, float* eta_T,
-                         int64_t B, int64_t H, int64_t T, int64_t D, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+                         double* states, int64_t B, int64_t H, int64_t T, int64_t D,
+                         void* workspace, size_t workspace_bytes, void* stream) {
     Plan pl;
     bool empty = false;
     kla_status st = common_checks(B, H, T, D, in_dtype, kla::kFwdRows, kla::kFwdWaves,
@@ -453,18 +477,21 @@ kla_status kla_mixer_fwd(const void* k, const void* v, const void* lam_v, const 
     for (int i = 0; i < 8; ++i)
         if (f32s[i] && misaligned(f32s[i], 4))
             return fail(KLA_ERR_UNSUPPORTED, "float32 arguments must be 4-byte aligned");
+    if (states && misaligned(states, 16))
+        return fail(KLA_ERR_UNSUPPORTED, "states is not 16-byte aligned");
     if ((st = check_workspace(workspace, workspace_bytes, pl)) != KLA_OK) return st;
 
     const size_t in_bytes = size_t(pl.N) * esz, out_bytes = size_t(pl.N) * 4;
     const size_t st_bytes = size_t(pl.C) * 4, ch_bytes = size_t(H * D) * 4;
-    const Buffer bufs[13] = {{k, in_bytes, "k", false},           {v, in_bytes, "v", false},
+    const Buffer bufs[14] = {{k, in_bytes, "k", false},           {v, in_bytes, "v", false},
                              {lam_v, in_bytes, "lam_v", false},   {q, in_bytes, "q", false},
                              {a, ch_bytes, "a", false},           {p, ch_bytes, "p", false},
                              {lam0, st_bytes, "lam0", false},     {eta0, st_bytes, "eta0", false},
                              {out, out_bytes, "out", true},       {var, out_bytes, "var", true},
                              {lam_T, st_bytes, "lam_T", true},    {eta_T, st_bytes, "eta_T", true},
-                             {workspace, pl.ws.bytes, "workspace", true}};
-    if ((st = check_overlaps(bufs, 13)) != KLA_OK) return st;
+                             {workspace, pl.ws.bytes, "workspace", true},
+                             {states, mixer_states_bytes(pl, T), "states", true}};
+    if ((st = check_overlaps(bufs, 14)) != KLA_OK) return st;
 
     kla::FwdArgs args = {};
     args.in[0] = k;
@@ -479,6 +506,7 @@ kla_status kla_mixer_fwd(const void* k, const void* v, const void* lam_v, const 
     args.p_ch = p;
     args.lam_T = lam_T;
     args.eta_T = eta_T;
+    args.bstate = states;
     args.T = T;
     args.D = D;
     args.C = pl.C;

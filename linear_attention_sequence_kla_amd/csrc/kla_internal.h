@@ -47,6 +47,7 @@ struct FwdArgs {
     float* lam_T;          // mixer: final state [B, H, D] (may be NULL)
     float* eta_T;
     double* bstate;        // mixer states: [ceil(T / kMixBwdRows)][C][2] float64
+                           // (MixerState: required; Mixer: may be NULL)
     int64_t T, D, C, G, n_chunks, n_tiles, HD;
     Workspace ws;
 };

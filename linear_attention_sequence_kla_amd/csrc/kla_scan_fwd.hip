@@ -39,7 +39,8 @@
 //     lam_v, q and per-channel gates (a, p); phi = k^2 lam_v and b = k lam_v v
 //     are formed on the fly (token_gates), and the replay writes the readout
 //     q * eta / lam = q * Y / X and the variance 1 / lam = Z / X, so no gate
-//     or state tensor crosses HBM.
+//     or state tensor crosses HBM; optionally also the boundary states of
+//     MixerState, kept by a training caller for the backward pass.
 //   * MixerState: the mixer's gates, writing the float64 state (lam, eta)
 //     after every kMixBwdRows-th row only (the boundary states from which
 //     the mixer's backward kernel recomputes its rows' states); q is not
@@ -358,18 +359,21 @@ void kla_scan_kernel(FwdArgs g) {
                 Y = fma(bb, zn, a * Y);
                 Z = zn;
                 const uint32_t off = lm.lane_el * uint32_t(sizeof(float)) + uint32_t(i) * out_row;
-                if constexpr (M == Mode::MixerState) {
+                if constexpr (M == Mode::MixerState || M == Mode::Mixer) {
                     // the state after rows kMixBwdRows * j - 1, j = 1, 2, ...
                     // (the last row's is not needed), as float64 pairs
-                    // [j - 1][channel][lam, eta]
+                    // [j - 1][channel][lam, eta]: always in MixerState mode,
+                    // in Mixer mode when the caller keeps them for the backward
                     const int64_t done = t0 + i + 1;
-                    if (done % kMixBwdRows == 0 && done < g.T && lm.valid) {
+                    if ((M == Mode::MixerState || g.bstate) && done % kMixBwdRows == 0 &&
+                        done < g.T && lm.valid) {
                         const double r = recip(Z);
                         double2* dst = reinterpret_cast<double2*>(
                             g.bstate + ((done / kMixBwdRows - 1) * g.C + lm.q) * 2);
                         *dst = make_double2(X * r, Y * r);
                     }
-                } else if constexpr (kMixer) {
+                }
+                if constexpr (kMixer) {
                     // readout: mean eta / lam = Y / X scaled by q, variance 1 / lam = Z / X
                     const double r = recip(X);
                     if (lm.valid) {
@@ -384,7 +388,7 @@ void kla_scan_kernel(FwdArgs g) {
                         g.lam_T[lm.q] = float(X * rz);
                         g.eta_T[lm.q] = float(Y * rz);
                     }
-                } else {
+                } else if constexpr (M != Mode::MixerState) {
                     const double r = recip(Z);
                     if (lm.valid) {
                         __builtin_nontemporal_store(float(X * r), reinterpret_cast<float*>(olam + off));

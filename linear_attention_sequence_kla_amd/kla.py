@@ -63,9 +63,11 @@ def load_library(path: str) -> ctypes.CDLL:
     lib.kla_scan_bwd.restype = ctypes.c_int
     lib.kla_mixer_fwd_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int]
     lib.kla_mixer_fwd_workspace_size.restype = sz
-    lib.kla_mixer_fwd.argtypes = [vp, vp, vp, vp, ctypes.c_int] + [vp] * 8 + [i64] * 4 + [
+    lib.kla_mixer_fwd.argtypes = [vp, vp, vp, vp, ctypes.c_int] + [vp] * 9 + [i64] * 4 + [
         vp, sz, vp]
     lib.kla_mixer_fwd.restype = ctypes.c_int
+    lib.kla_mixer_states_size.argtypes = [i64, i64, i64, i64]
+    lib.kla_mixer_states_size.restype = sz
     lib.kla_scan_lti_fwd_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int]
     lib.kla_scan_lti_fwd_workspace_size.restype = sz
     lib.kla_scan_lti_fwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, vp,
@@ -73,7 +75,7 @@ def load_library(path: str) -> ctypes.CDLL:
     lib.kla_scan_lti_fwd.restype = ctypes.c_int
     lib.kla_mixer_bwd_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int]
     lib.kla_mixer_bwd_workspace_size.restype = sz
-    lib.kla_mixer_bwd.argtypes = [vp, vp, vp, vp, ctypes.c_int] + [vp] * 14 + [i64] * 4 + [
+    lib.kla_mixer_bwd.argtypes = [vp, vp, vp, vp, ctypes.c_int] + [vp] * 15 + [i64] * 4 + [
         vp, sz, vp]
     lib.kla_mixer_bwd.restype = ctypes.c_int
     lib.kla_decode_step.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, vp, i64, vp]
@@ -323,7 +325,8 @@ def mixer_fwd(k: torch.Tensor, v: torch.Tensor, lam_v: torch.Tensor, q: torch.Te
               a: torch.Tensor, p: torch.Tensor, lam0: torch.Tensor | None = None,
               eta0: torch.Tensor | None = None, want_var: bool = True,
               want_state: bool = False, out: torch.Tensor | None = None,
-              var: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+              var: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+              states: torch.Tensor | None = None):
     """Fused KLA mixer forward on the current stream (kla_mixer_fwd).
 
     k, v, lam_v, q: [B, H, T, D] contiguous, all float32 or all bfloat16 (the
@@ -331,7 +334,9 @@ def mixer_fwd(k: torch.Tensor, v: torch.Tensor, lam_v: torch.Tensor, q: torch.Te
     a, p: [H, D] float32 state decay and process noise.  lam0, eta0: [B, H, D]
     float32 (None: 1 and 0).  Returns (out, var, lam_T, eta_T): the readout
     q * eta / lam, the posterior variance 1 / lam (None unless want_var) and
-    the final state (None unless want_state), float32.
+    the final state (None unless want_state), float32.  ``states``, a float64
+    tensor of ``mixer_states_shape(B, H, T, D)`` on k's GPU, receives the
+    state after every 8th token for ``mixer_bwd``.
     """
     ins = (k, v, lam_v, q)
     if k.dim() != 4:
@@ -364,13 +369,31 @@ def mixer_fwd(k: torch.Tensor, v: torch.Tensor, lam_v: torch.Tensor, q: torch.Te
         lam_T = torch.empty((B, H, D), dtype=torch.float32, device=dev)
         eta_T = torch.empty((B, H, D), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    _check_states(states, (B, H, T, D), dev)
     if workspace is None:
         workspace = get_workspace(mixer_workspace_size(B, H, T, D, k.dtype), dev, stream)
     _check(library().kla_mixer_fwd(
         _ptr(k), _ptr(v), _ptr(lam_v), _ptr(q), _DTYPES[k.dtype], _ptr(a), _ptr(p), _ptr(lam0),
-        _ptr(eta0), _ptr(out), _ptr(var), _ptr(lam_T), _ptr(eta_T), B, H, T, D, _ptr(workspace),
-        workspace.numel(), ctypes.c_void_p(stream.cuda_stream)))
+        _ptr(eta0), _ptr(out), _ptr(var), _ptr(lam_T), _ptr(eta_T), _ptr(states), B, H, T, D,
+        _ptr(workspace), workspace.numel(), ctypes.c_void_p(stream.cuda_stream)))
     return out, var, lam_T, eta_T
+
+
+def mixer_states_shape(B: int, H: int, T: int, D: int) -> tuple:
+    """Shape of the float64 tensor of mixer states (kla_mixer_fwd's `states`):
+    the (lam, eta) of every channel after every 8th token."""
+    C = B * H * D
+    n = int(library().kla_mixer_states_size(B, H, T, D))
+    return (n // (16 * C) if C else 0, C, 2)
+
+
+def _check_states(states, shape4, dev):
+    if states is None:
+        return
+    want = mixer_states_shape(*shape4)
+    if (tuple(states.shape) != want or states.dtype != torch.float64 or not states.is_cuda
+            or states.device != dev or not states.is_contiguous()):
+        raise ValueError("states must be a contiguous float64 %s tensor on %s" % (want, dev))
 
 
 def mixer_bwd_workspace_size(B: int, H: int, T: int, D: int, dtype=torch.float32) -> int:
@@ -382,13 +405,16 @@ def mixer_bwd(k: torch.Tensor, v: torch.Tensor, lam_v: torch.Tensor, q: torch.Te
               a: torch.Tensor, p: torch.Tensor, g_out: torch.Tensor,
               g_var: torch.Tensor | None = None, lam0: torch.Tensor | None = None,
               eta0: torch.Tensor | None = None, need_state_grads: bool = True,
-              workspace: torch.Tensor | None = None, out: tuple | None = None):
+              workspace: torch.Tensor | None = None, out: tuple | None = None,
+              states: torch.Tensor | None = None):
     """Fused KLA mixer backward on the current stream (kla_mixer_bwd).
 
     Inputs as for ``mixer_fwd``; g_out, g_var: float32 [B, H, T, D] upstream
     gradients of the readout and the variance (g_var None: zero).  Returns
     (g_k, g_v, g_lam_v, g_q, g_a, g_p, g_lam0, g_eta0), float32; the last two
     are None unless need_state_grads.  ``out`` may supply the first six.
+    ``states``: the tensor ``mixer_fwd`` filled for these inputs (the forward
+    states are then not recomputed), or None.
     """
     if k.dim() != 4:
         raise ValueError("token inputs must be [B, H, T, D], got shape %s" % (tuple(k.shape),))
@@ -429,36 +455,42 @@ def mixer_bwd(k: torch.Tensor, v: torch.Tensor, lam_v: torch.Tensor, q: torch.Te
         g_lam0 = torch.empty((B, H, D), dtype=torch.float32, device=dev)
         g_eta0 = torch.empty((B, H, D), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    _check_states(states, (B, H, T, D), dev)
     if workspace is None:
         workspace = get_workspace(mixer_bwd_workspace_size(B, H, T, D, k.dtype), dev, stream)
     _check(library().kla_mixer_bwd(
         _ptr(k), _ptr(v), _ptr(lam_v), _ptr(q), _DTYPES[k.dtype], _ptr(a), _ptr(p), _ptr(lam0),
-        _ptr(eta0), _ptr(g_out), _ptr(g_var), _ptr(g_k), _ptr(g_v), _ptr(g_lam_v), _ptr(g_q),
+        _ptr(eta0), _ptr(states), _ptr(g_out), _ptr(g_var), _ptr(g_k), _ptr(g_v), _ptr(g_lam_v), _ptr(g_q),
         _ptr(g_a), _ptr(g_p), _ptr(g_lam0), _ptr(g_eta0), B, H, T, D, _ptr(workspace),
         workspace.numel(), ctypes.c_void_p(stream.cuda_stream)))
     return g_k, g_v, g_lam_v, g_q, g_a, g_p, g_lam0, g_eta0
 
 
 class KLAMixer(torch.autograd.Function):
-    """Differentiable fused mixer: kla_mixer_fwd forward, kla_mixer_bwd
-    backward (which recomputes the forward states).  Returns (out, var).
-    Gradients are float32 and are cast to each input's dtype."""
+    """Differentiable fused mixer: kla_mixer_fwd forward, which also keeps the
+    float64 state after every 8th token (about 2 bytes per element), and
+    kla_mixer_bwd backward from those states.  Returns (out, var).  Gradients
+    are float32 and are cast to each input's dtype."""
 
     @staticmethod
     def forward(ctx, k, v, lam_v, q, a, p, lam0, eta0):
-        out, var, _, _ = mixer_fwd(k, v, lam_v, q, a, p, lam0, eta0)
-        ctx.save_for_backward(k, v, lam_v, q, a, p, lam0, eta0)
+        states = None
+        if any(ctx.needs_input_grad):
+            states = torch.empty(mixer_states_shape(*k.shape), dtype=torch.float64,
+                                 device=k.device)
+        out, var, _, _ = mixer_fwd(k, v, lam_v, q, a, p, lam0, eta0, states=states)
+        ctx.save_for_backward(k, v, lam_v, q, a, p, lam0, eta0, states)
         return out, var
 
     @staticmethod
     def backward(ctx, g_out, g_var):
-        k, v, lam_v, q, a, p, lam0, eta0 = ctx.saved_tensors
+        k, v, lam_v, q, a, p, lam0, eta0, states = ctx.saved_tensors
         need = ctx.needs_input_grad
         if g_out is None:
             g_out = torch.zeros(k.shape, dtype=torch.float32, device=k.device)
         g = mixer_bwd(k, v, lam_v, q, a, p, g_out.contiguous().float(),
                       None if g_var is None else g_var.contiguous().float(), lam0, eta0,
-                      need_state_grads=need[6] or need[7])
+                      need_state_grads=need[6] or need[7], states=states)
         cast = (lambda t, x: t.to(x.dtype))  # noqa: E731
         return (cast(g[0], k), cast(g[1], v), cast(g[2], lam_v), cast(g[3], q), g[4], g[5],
                 g[6] if need[6] else None, g[7] if need[7] else None)

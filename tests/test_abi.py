@@ -109,12 +109,12 @@ def test_health_rejects_null(lib):
 
 
 def _mixer_call(lib, k=1, a=0x500000, out=0x1000000, var=0x2000000, lam_T=0, eta_T=0,
-                shape=(2, 1, 4, 4), ws=0x4000000, ws_bytes=1 << 20):
+                states=0, shape=(2, 1, 4, 4), ws=0x4000000, ws_bytes=1 << 20):
     vp = ctypes.c_void_p
     B, H, T, D = shape
     st = lib.kla_mixer_fwd(vp(k * 0x100000), vp(0x200000), vp(0x300000), vp(0x400000), 0,
                            vp(a), vp(0x600000), None, None, vp(out), vp(var), vp(lam_T),
-                           vp(eta_T), B, H, T, D, vp(ws), ws_bytes, None)
+                           vp(eta_T), vp(states), B, H, T, D, vp(ws), ws_bytes, None)
     return st, lib.kla_last_error_detail().decode()
 
 
@@ -143,8 +143,20 @@ def test_mixer_argument_errors_before_launch(lib):
     assert st == 1 and "overlaps" in msg
     st, msg = _mixer_call(lib, ws_bytes=16)
     assert st == 3 and "needs" in msg
+    st, msg = _mixer_call(lib, states=0x3000008)
+    assert st == 2 and "16-byte" in msg
+    st, msg = _mixer_call(lib, states=0x1000000 - 64)  # runs into out
+    assert st == 1 and "overlaps" in msg
     st, _ = _mixer_call(lib, k=0, shape=(1, 1, 0, 4))
     assert st == 0
+
+
+def test_mixer_states_size(lib):
+    sz = lib.kla_mixer_states_size
+    assert sz(0, 1, 1, 1) == 0 and sz(-1, 1, 1, 1) == 0 and sz(2 ** 40, 2 ** 40, 1, 1) == 0
+    # float64 (lam, eta) of every channel after every 8th token
+    for B, H, T, D in ((1, 1, 1, 1), (2, 3, 8, 5), (2, 3, 9, 5), (8, 16, 2048, 64)):
+        assert sz(B, H, T, D) == ((T + 7) // 8) * B * H * D * 16
 
 
 def test_lti_workspace_size(lib):
@@ -197,9 +209,10 @@ def test_mixer_bwd_argument_errors_before_launch(lib):
     need = lib.kla_mixer_bwd_workspace_size(*shape, 0)
 
     def call(k=0x100000, g_out=0x700000, g_k=0x1000000, g_a=0x1800000, ws=0x4000000,
-             ws_bytes=need):
+             ws_bytes=need, states=0):
         st = lib.kla_mixer_bwd(vp(k), vp(0x200000), vp(0x300000), vp(0x400000), 0,
-                               vp(0x500000), vp(0x600000), None, None, vp(g_out), None,
+                               vp(0x500000), vp(0x600000), None, None, vp(states), vp(g_out),
+                               None,
                                vp(g_k), vp(0x1100000), vp(0x1200000), vp(0x1300000), vp(g_a),
                                vp(0x1900000), None, None, *shape, vp(ws), ws_bytes, None)
         return st, lib.kla_last_error_detail().decode()
@@ -215,3 +228,7 @@ def test_mixer_bwd_argument_errors_before_launch(lib):
     assert st == 3 and "needs" in msg
     st, _ = call(ws=0x4000010)
     assert st == 3
+    st, msg = call(states=0x3000008)
+    assert st == 2 and "16-byte" in msg
+    st, msg = call(states=0x1000000 - 64)  # g_k is written over the states
+    assert st == 1 and "overlaps" in msg

@@ -68,12 +68,13 @@ def test_scan_forward_and_backward(debug_build, shape):
 @pytest.mark.parametrize("shape", [(1, 2, 6000, 64), (2, 4, 1500, 128)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_mixer_forward_and_backward(debug_build, shape):
-    from linear_attention_sequence_kla_amd import mixer_bwd, mixer_fwd
+    from linear_attention_sequence_kla_amd import mixer_bwd, mixer_fwd, mixer_states_shape
     g = make_mixer_inputs(shape, "f32", seed=4)
     g["lam0"], g["eta0"] = make_initial_state(shape[0], shape[1], shape[3], random=True, seed=4)
     d = {n: v.to(DEV) for n, v in g.items()}
+    states = torch.empty(mixer_states_shape(*shape), dtype=torch.float64, device=DEV)
     out, var, _, _ = mixer_fwd(d["k"], d["v"], d["lam_v"], d["q"], d["a"], d["p"], d["lam0"],
-                               d["eta0"])
+                               d["eta0"], states=states)
     torch.cuda.synchronize(DEV)
     assert _health() == 0
     ref = oracle_mixer(g["k"], g["v"], g["lam_v"], g["q"], g["a"], g["p"], g["lam0"], g["eta0"])
@@ -89,6 +90,13 @@ def test_mixer_forward_and_backward(debug_build, shape):
                                    g["lam0"], g["eta0"], g_out, g_var)
     got = dict(zip(("k", "v", "lam_v", "q", "a", "p", "lam0", "eta0"), (t.cpu() for t in res)))
     assert_grad_parity(compare_grads(got, grads, mags), TOL_F32, "mixer backward")
+    # from the states the forward kept: bitwise the same gradients
+    kept = mixer_bwd(d["k"], d["v"], d["lam_v"], d["q"], d["a"], d["p"], g_out.to(DEV),
+                     g_var.to(DEV), d["lam0"], d["eta0"], states=states)
+    torch.cuda.synchronize(DEV)
+    assert _health() == 0
+    for x, y in zip(res, kept):
+        assert torch.equal(x, y)
 
 
 def test_lti(debug_build):

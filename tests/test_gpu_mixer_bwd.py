@@ -137,6 +137,33 @@ def test_kla_mixer_autograd():
     assert_grad_parity(rep, TOL_F32, "autograd")
 
 
+@pytest.mark.parametrize("shape,dtype", [((2, 3, 500, 24), "f32"), ((3, 3, 300, 128), "f32"),
+                                         ((2, 2, 601, 48), "bf16"), ((1, 1, 7, 3), "f32")],
+                         ids=lambda x: "x".join(map(str, x)) if isinstance(x, tuple) else x)
+def test_saved_states_equal_recompute(shape, dtype):
+    """States kept by kla_mixer_fwd give the backward bitwise the gradients of
+    its own recompute (the same kernel writes the same float64 states), and
+    those match the oracle."""
+    from linear_attention_sequence_kla_amd import mixer_bwd, mixer_fwd, mixer_states_shape
+    g = _case(shape, dtype, seed=sum(shape))
+    d = {n: (None if t is None else t.to(DEV)) for n, t in g.items()}
+    states = torch.full(mixer_states_shape(*shape), float("nan"), dtype=torch.float64,
+                        device=DEV)
+    mixer_fwd(*(d[n] for n in TOKEN), d["a"], d["p"], d["lam0"], d["eta0"], states=states)
+    args = (*(d[n] for n in TOKEN), d["a"], d["p"], d["g_out"], d["g_var"], d["lam0"], d["eta0"])
+    kept = mixer_bwd(*args, states=states)
+    again = mixer_bwd(*args)
+    torch.cuda.synchronize(DEV)
+    # every state the backward reads was written (all blocks but the last)
+    assert bool(torch.isfinite(states[:-1]).all())
+    for n, x, y in zip(NAMES, kept, again):
+        assert torch.equal(x, y), n
+    grads, mags = oracle(g)
+    rep = compare_grads(dict(zip(NAMES, (t.cpu() for t in kept))), grads, mags)
+    _say("saved states %s %s: %s" % (shape, dtype, rep))
+    assert_grad_parity(rep, TOL_BF16 if dtype == "bf16" else TOL_F32, "saved states")
+
+
 def test_mixer_bwd_argument_errors_on_device():
     from linear_attention_sequence_kla_amd import mixer_bwd
     g = {n: (None if t is None else t.to(DEV)) for n, t in _case((1, 2, 8, 4), seed=1).items()}
@@ -148,3 +175,6 @@ def test_mixer_bwd_argument_errors_on_device():
     with pytest.raises(ValueError):
         mixer_bwd(g["k"], g["v"], g["lam_v"], g["q"], g["a"][:1].contiguous(), g["p"],
                   g["g_out"])
+    with pytest.raises(ValueError):  # states of the wrong shape
+        mixer_bwd(g["k"], g["v"], g["lam_v"], g["q"], g["a"], g["p"], g["g_out"],
+                  states=torch.zeros((2, 8, 2), dtype=torch.float64, device=DEV))

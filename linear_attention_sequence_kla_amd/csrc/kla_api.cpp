@@ -515,8 +515,9 @@ kla_status kla_mixer_fwd(const void* k, const void* v, const void* lam_v, const 
     args.n_tiles = pl.n_tiles;
     args.HD = H * D;
     args.ws = kla::workspace_view(workspace, pl.ws);
-    const hipError_t err =
-        kla::launch_scan_fwd(args, in_dtype, kla::FwdMode::kMixer, static_cast<hipStream_t>(stream));
+    const hipError_t err = kla::launch_scan_fwd(
+        args, in_dtype, states ? kla::FwdMode::kMixerTrain : kla::FwdMode::kMixer,
+        static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return fail(KLA_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
     return KLA_OK;
 }

@@ -47,7 +47,7 @@ struct FwdArgs {
     float* lam_T;          // mixer: final state [B, H, D] (may be NULL)
     float* eta_T;
     double* bstate;        // mixer states: [ceil(T / kMixBwdRows)][C][2] float64
-                           // (MixerState: required; Mixer: may be NULL)
+                           // (kMixerState, kMixerTrain)
     int64_t T, D, C, G, n_chunks, n_tiles, HD;
     Workspace ws;
 };
@@ -79,8 +79,8 @@ constexpr int kBwdRows = 20, kBwdWaves = 4, kBwdMatrixWords = 6, kBwdStateWords 
 
 // kMixerState: the mixer's gates; writes the float64 states (lam, eta) after
 // every kMixBwdRows-th row into FwdArgs::bstate, for the mixer's backward
-// pass.
-enum class FwdMode { kScan, kMixer, kLti, kMixerState };
+// pass.  kMixerTrain: kMixer that also writes those states.
+enum class FwdMode { kScan, kMixer, kLti, kMixerState, kMixerTrain };
 hipError_t launch_scan_fwd(const FwdArgs& args, kla_dtype dtype, FwdMode mode, hipStream_t stream);
 hipError_t launch_scan_bwd(const BwdArgs& args, kla_dtype dtype, hipStream_t stream);
 

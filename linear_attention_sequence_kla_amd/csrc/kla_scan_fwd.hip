@@ -39,8 +39,10 @@
 //     lam_v, q and per-channel gates (a, p); phi = k^2 lam_v and b = k lam_v v
 //     are formed on the fly (token_gates), and the replay writes the readout
 //     q * eta / lam = q * Y / X and the variance 1 / lam = Z / X, so no gate
-//     or state tensor crosses HBM; optionally also the boundary states of
-//     MixerState, kept by a training caller for the backward pass.
+//     or state tensor crosses HBM.
+//   * MixerTrain: Mixer, also writing the boundary states of MixerState
+//     (kept by a training caller for the backward pass).  A mode of its own
+//     so that the plain mixer's replay carries no extra branch.
 //   * MixerState: the mixer's gates, writing the float64 state (lam, eta)
 //     after every kMixBwdRows-th row only (the boundary states from which
 //     the mixer's backward kernel recomputes its rows' states); q is not
@@ -146,6 +148,7 @@ enum class Mode {
     Mixer,  // k, v, lam_v, q per token, (a, p) per channel -> q eta / lam, 1 / lam
     Lti,    // b per token, (a, p, phi) per channel -> lam, eta
     MixerState,  // k, v, lam_v per token, (a, p) per channel -> boundary (lam, eta)
+    MixerTrain,  // Mixer's inputs -> Mixer's outputs and MixerState's
 };
 
 // The float64 gates (a, p, phi, b) of one token.  Scan mode reads them from
@@ -160,7 +163,7 @@ enum class Mode {
 template <Mode M>
 __device__ inline void token_gates(float x0, float x1, float x2, float x3, double ac, double pc,
                                    double fc, double& a, double& p, double& ph, double& b) {
-    if constexpr (M == Mode::Mixer || M == Mode::MixerState) {
+    if constexpr (M == Mode::Mixer || M == Mode::MixerState || M == Mode::MixerTrain) {
         const double k = x0, lv = x2;
         a = ac;
         p = pc;
@@ -182,7 +185,7 @@ __device__ inline void token_gates(float x0, float x1, float x2, float x3, doubl
 template <typename In, int L, int W, Mode M>
 __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(3)))
 void kla_scan_kernel(FwdArgs g) {
-    constexpr bool kMixer = M == Mode::Mixer;
+    constexpr bool kMixer = M == Mode::Mixer || M == Mode::MixerTrain;
     constexpr bool kAll = M != Mode::Lti;            // the first three token inputs are read
     constexpr bool kFourth = M != Mode::MixerState;  // the fourth one is read
     __shared__ double s_lift[W][7][kWave];
@@ -359,14 +362,12 @@ void kla_scan_kernel(FwdArgs g) {
                 Y = fma(bb, zn, a * Y);
                 Z = zn;
                 const uint32_t off = lm.lane_el * uint32_t(sizeof(float)) + uint32_t(i) * out_row;
-                if constexpr (M == Mode::MixerState || M == Mode::Mixer) {
+                if constexpr (M == Mode::MixerState || M == Mode::MixerTrain) {
                     // the state after rows kMixBwdRows * j - 1, j = 1, 2, ...
                     // (the last row's is not needed), as float64 pairs
-                    // [j - 1][channel][lam, eta]: always in MixerState mode,
-                    // in Mixer mode when the caller keeps them for the backward
+                    // [j - 1][channel][lam, eta]
                     const int64_t done = t0 + i + 1;
-                    if ((M == Mode::MixerState || g.bstate) && done % kMixBwdRows == 0 &&
-                        done < g.T && lm.valid) {
+                    if (done % kMixBwdRows == 0 && done < g.T && lm.valid) {
                         const double r = recip(Z);
                         double2* dst = reinterpret_cast<double2*>(
                             g.bstate + ((done / kMixBwdRows - 1) * g.C + lm.q) * 2);
@@ -427,6 +428,8 @@ hipError_t launch_scan_fwd(const FwdArgs& args, kla_dtype dtype, FwdMode mode,
         launch<kFwdRows, kFwdWaves, Mode::Scan>(args, dtype, stream);
     else if (mode == FwdMode::kMixer)
         launch<kFwdRows, kFwdWaves, Mode::Mixer>(args, dtype, stream);
+    else if (mode == FwdMode::kMixerTrain)
+        launch<kFwdRows, kFwdWaves, Mode::MixerTrain>(args, dtype, stream);
     else if (mode == FwdMode::kMixerState)
         launch<kFwdRows, kFwdWaves, Mode::MixerState>(args, dtype, stream);
     else

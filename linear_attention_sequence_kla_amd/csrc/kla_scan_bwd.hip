@@ -77,13 +77,24 @@ __device__ inline Adj lds_adj(const double (*s)[6][kWave], int j, int lane) {
                s[j][3][lane], s[j][4][lane], s[j][5][lane]};
 }
 
-// The tile's map: wave 0's map applied last (waves cover increasing times).
+// The maps of waves w+1..W-1 multiplied (the last wave's applied first;
+// waves cover increasing times): the map from the tile's carry to wave w's
+// (w < W - 1).
 template <int W>
-__device__ inline Adj tile_adj(const double (*s)[6][kWave], int lane) {
+__device__ inline Adj suffix_adj(const double (*s)[6][kWave], int w, int lane) {
     Adj t = lds_adj(s, W - 1, lane);
 #pragma unroll 1
-    for (int j = W - 2; j >= 0; --j) t = mul(lds_adj(s, j, lane), t);
+    for (int j = W - 2; j > w; --j) t = mul(lds_adj(s, j, lane), t);
     return t;
+}
+
+__device__ inline void lds_store_adj(double (*s)[6][kWave], int j, int lane, const Adj& m) {
+    s[j][0][lane] = m.u;
+    s[j][1][lane] = m.v;
+    s[j][2][lane] = m.x;
+    s[j][3][lane] = m.w;
+    s[j][4][lane] = m.y;
+    s[j][5][lane] = m.s;
 }
 
 __device__ inline void store_adj(double* rec, int lane, const Adj& m) {
@@ -110,24 +121,42 @@ __device__ inline float load_f32(const char* base, uint32_t off) {
     return __builtin_nontemporal_load(reinterpret_cast<const float*>(base + off));
 }
 
-// Wave 0 of a tile: publish the tile's map, look back over the tiles later
-// in time for the carry into the tile, publish the tile's inclusive carry,
-// and leave every wave's own carry-in in s_carry.  `c` is the tile's chunk
-// along T (tiles are numbered from the sequence's end).
+// The carry exchange of a tile, run after its waves' maps are in s_adj.
+// Waves 1..W-2 each store the map from the tile's carry to their own in
+// s_suf[w] (the last wave's is the identity).  Wave 0 stores its own such
+// map in s_suf[0] and the tile's map in s_suf[W - 1], publishes the tile's
+// map, looks back over the tiles later in time for the carry into the
+// tile, publishes the tile's inclusive carry and leaves the tile's carry in
+// s_tc.  `c` is the tile's chunk along T (tiles are numbered from the
+// sequence's end).
 template <int W>
 __device__ inline void tile_carry(const Workspace& ws, int64_t ticket, int64_t G,
                                   int64_t n_chunks, int64_t c, uint32_t tag,
-                                  const double (*s_adj)[6][kWave], double (*s_carry)[2][kWave],
-                                  int lane) {
+                                  const double (*s_adj)[6][kWave], double (*s_suf)[6][kWave],
+                                  double (*s_tc)[kWave], int w, int lane) {
+    static_assert(W >= 2, "the tile's map shares the last wave's slot");
+    if (w != 0) {
+        if (w + 1 < W) lds_store_adj(s_suf, w, lane, suffix_adj<W>(s_adj, w, lane));
+        return;
+    }
     const bool has_next = c > 0;  // earlier chunks follow in tile order
     double* const matrix = ws.matrix;
     double* const state = ws.state;
+    {
+        const Adj s0 = suffix_adj<W>(s_adj, 0, lane);
+        if (has_next) {
+            // the tile's map, kept in LDS rather than in registers across the
+            // wait (written while the record stores drain)
+            const Adj t = mul(lds_adj(s_adj, 0, lane), s0);
+            const bool agg = c + 1 < n_chunks;
+            if (agg) store_adj(matrix + size_t(ticket) * 6 * kWave, lane, t);
+            lds_store_adj(s_suf, W - 1, lane, t);
+            if (agg) publish(&ws.flags[ticket], lane, flag_word(tag, kStatusAggregate));
+        }
+        lds_store_adj(s_suf, 0, lane, s0);
+    }
     double cl = 0.0, ce = 0.0;  // nothing flows in past the sequence end
     if (c + 1 < n_chunks) {
-        if (has_next) {
-            store_adj(matrix + size_t(ticket) * 6 * kWave, lane, tile_adj<W>(s_adj, lane));
-            publish(&ws.flags[ticket], lane, flag_word(tag, kStatusAggregate));
-        }
         int64_t j = ticket - G;
         uint32_t st;
         while ((st = wait_flag(&ws.flags[j], tag, ws.header)) == kStatusAggregate) j -= G;
@@ -140,29 +169,32 @@ __device__ inline void tile_carry(const Workspace& ws, int64_t ticket, int64_t G
     }
     if (has_next) {
         double l = cl, e = ce;
-        apply(tile_adj<W>(s_adj, lane), l, e);
+        apply(lds_adj(s_suf, W - 1, lane), l, e);
         rec_store(state + size_t(ticket) * 2 * kWave + lane, l);
         rec_store(state + size_t(ticket) * 2 * kWave + kWave + lane, e);
         publish(&ws.flags[ticket], lane, flag_word(tag, kStatusInclusive));
     } else if (n_chunks > 1) {
         publish(&ws.flags[ticket], lane, flag_word(tag, kStatusFinished));
     }
-    // carry into every wave: the last wave gets the tile's, each earlier one
-    // the carry through the maps of the waves after it
-    s_carry[W - 1][0][lane] = cl;
-    s_carry[W - 1][1][lane] = ce;
-#pragma unroll 1
-    for (int j = W - 1; j > 0; --j) {
-        apply(lds_adj(s_adj, j, lane), cl, ce);
-        s_carry[j - 1][0][lane] = cl;
-        s_carry[j - 1][1][lane] = ce;
-    }
+    s_tc[0][lane] = cl;
+    s_tc[1][lane] = ce;
+}
+
+// The carry into wave w once tile_carry's results are visible: the tile's
+// carry through the maps of the waves after it.
+template <int W>
+__device__ inline void wave_carry(const double (*s_suf)[6][kWave], const double (*s_tc)[kWave],
+                                  int w, int lane, double& cl, double& ce) {
+    cl = s_tc[0][lane];
+    ce = s_tc[1][lane];
+    if (w + 1 < W) apply(lds_adj(s_suf, w, lane), cl, ce);
 }
 
 template <typename In, int L, int W>
 __global__ __launch_bounds__(W * kWave) void kla_scan_bwd_kernel(BwdArgs g) {
     __shared__ double s_adj[W][6][kWave];
-    __shared__ double s_carry[W][2][kWave];
+    __shared__ double s_suf[W][6][kWave];  // the maps tile_carry leaves
+    __shared__ double s_tc[2][kWave];       // the tile's carry
     static_assert(kBwdMatrixWords == 6 && kBwdStateWords == 2, "record layout");
 
     const int lane = threadIdx.x & (kWave - 1);
@@ -258,13 +290,15 @@ __global__ __launch_bounds__(W * kWave) void kla_scan_bwd_kernel(BwdArgs g) {
         s_adj[w][5][lane] = m.s;
         __syncthreads();
 
-        // ---- tile carry (wave 0): publish, look back over later tiles ----
-        if (w == 0) tile_carry<W>(g.ws, ticket, g.G, g.n_chunks, c, tag, s_adj, s_carry, lane);
+        // ---- tile carry (wave 0: publish, look back over later tiles;
+        // the others: their maps from the tile's carry) ----
+        tile_carry<W>(g.ws, ticket, g.G, g.n_chunks, c, tag, s_adj, s_suf, s_tc, w, lane);
         __syncthreads();
 
         // ---- replay the wave's rows last to first, writing the gradients ----
         if (nr > 0) {
-            double cl = s_carry[w][0][lane], ce = s_carry[w][1][lane];
+            double cl, ce;
+            wave_carry<W>(s_suf, s_tc, w, lane, cl, ce);
             char* oa = reinterpret_cast<char*>(g.g_a) + lm.e0 * 4;
             char* op = reinterpret_cast<char*>(g.g_p) + lm.e0 * 4;
             char* of = reinterpret_cast<char*>(g.g_phi) + lm.e0 * 4;
@@ -329,7 +363,8 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(4)))
 void kla_mixer_bwd_kernel(MixerBwdArgs g) {
     static_assert(L == kMixBwdRows, "the recompute keeps a state every kMixBwdRows rows");
     __shared__ double s_adj[W][6][kWave];
-    __shared__ double s_carry[W][2][kWave];
+    __shared__ double s_suf[W][6][kWave];  // the maps tile_carry leaves
+    __shared__ double s_tc[2][kWave];       // the tile's carry
     __shared__ double s_part[W][2][kWave];
 
     const int lane = threadIdx.x & (kWave - 1);
@@ -452,13 +487,14 @@ void kla_mixer_bwd_kernel(MixerBwdArgs g) {
         s_adj[w][5][lane] = m.s;
         __syncthreads();
 
-        if (w == 0) tile_carry<W>(g.ws, ticket, g.G, g.n_chunks, c, tag, s_adj, s_carry, lane);
+        tile_carry<W>(g.ws, ticket, g.G, g.n_chunks, c, tag, s_adj, s_suf, s_tc, w, lane);
         __syncthreads();
 
         // ---- replay last to first: token-input gradients, gate sums ----
         double sa = 0.0, sp = 0.0;
         if (nr > 0) {
-            double cl = s_carry[w][0][lane], ce = s_carry[w][1][lane];
+            double cl, ce;
+            wave_carry<W>(s_suf, s_tc, w, lane, cl, ce);
             char* ok = reinterpret_cast<char*>(g.g_k) + lm.e0 * 4;
             char* ov = reinterpret_cast<char*>(g.g_v) + lm.e0 * 4;
             char* olv = reinterpret_cast<char*>(g.g_lam_v) + lm.e0 * 4;

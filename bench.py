@@ -3,8 +3,9 @@
 The headline (default) is the forward scan: a step is one kla_scan_fwd call
 over one batch of synthetic gates, the whole scan (chunk matrices, carry
 look-back, replay and output writes) in a single kernel launch.  --direction
-selects the backward scan, the fused mixer (forward, backward, or a training
-step of both), the time-invariant form or the decode step instead.  The K timed steps are
+selects the backward scan, the fused mixer (forward, backward, a training
+step of both, or its decode step), the time-invariant form or the scan's
+decode step instead.  The K timed steps are
 captured once into a HIP graph and replayed (--no-graph launches them one by
 one).  Inputs are generated on the GPU and are resident in HBM before timing;
 two input/output sets alternate so that the 256 MB Infinity Cache cannot
@@ -35,18 +36,21 @@ CSRC = os.path.join(ROOT, "linear_attention_sequence_kla_amd", "csrc")
 KERNEL_SOURCES = {"fwd": ("kla_scan_fwd.hip", "kla_lookback.h", "kla_internal.h"),
                   "bwd": ("kla_scan_bwd.hip", "kla_lookback.h", "kla_internal.h"),
                   "decode": ("kla_decode.hip", "kla_lookback.h", "kla_internal.h"),
+                  "mixer_decode": ("kla_decode.hip", "kla_lookback.h", "kla_internal.h"),
                   "mixer": ("kla_scan_fwd.hip", "kla_lookback.h", "kla_internal.h"),
                   "lti": ("kla_scan_fwd.hip", "kla_lookback.h", "kla_internal.h"),
                   "mixer_bwd": ("kla_scan_bwd.hip", "kla_lookback.h", "kla_internal.h"),
                   "mixer_train": ("kla_scan_bwd.hip", "kla_lookback.h", "kla_internal.h")}
 KERNEL_NAMES = {"fwd": "kla_scan_kernel", "bwd": "kla_scan_bwd_kernel",
-                "decode": "kla_decode_kernel", "mixer": "kla_scan_kernel",
+                "decode": "kla_decode_kernel", "mixer_decode": "kla_mixer_decode_kernel",
+                "mixer": "kla_scan_kernel",
                 "lti": "kla_scan_kernel", "mixer_bwd": "kla_mixer_bwd_kernel",
                 "mixer_train": "kla_mixer_bwd_kernel"}
 # the forward kernel template's last parameter is its mode (scan, mixer, LTI)
 KERNEL_SUFFIX = {"fwd": "Mode)0>", "mixer": "Mode)1>", "lti": "Mode)2>"}
 PROFILE_NAMES = {"fwd": "kla_scan_kernel", "bwd": "kla_scan_bwd_kernel",
-                 "decode": "kla_decode_kernel", "mixer": "kla_scan_kernel_mixer",
+                 "decode": "kla_decode_kernel", "mixer_decode": "kla_mixer_decode_kernel",
+                 "mixer": "kla_scan_kernel_mixer",
                  "lti": "kla_scan_kernel_lti", "mixer_bwd": "kla_mixer_bwd_kernel",
                  "mixer_train": "kla_mixer_bwd_kernel"}
 
@@ -84,6 +88,8 @@ def bytes_per_element(dtype: str, direction: str = "fwd") -> int:
         return 4 * gate + 2 * 4
     if direction == "decode":  # 4 gates, state read and written in place
         return 4 * gate + 2 * 4 + 2 * 4
+    if direction == "mixer_decode":  # 4 token inputs, state in place, readout and variance
+        return 4 * gate + 2 * 4 + 2 * 4 + 2 * 4
     if direction == "mixer":  # k, v, lam_v, q read; readout and variance written
         return 4 * gate + 2 * 4
     if direction == "lti":  # b read (gates once per channel); lam, eta written
@@ -208,7 +214,8 @@ def summarize_counters(args):
 def workloads_for(direction: str):
     from kla_inputs import LTI_WORKLOADS, MIXER_WORKLOADS, WORKLOADS
     return {"mixer": MIXER_WORKLOADS, "mixer_bwd": MIXER_WORKLOADS,
-            "mixer_train": MIXER_WORKLOADS, "lti": LTI_WORKLOADS}.get(direction, WORKLOADS)
+            "mixer_train": MIXER_WORKLOADS, "mixer_decode": MIXER_WORKLOADS,
+            "lti": LTI_WORKLOADS}.get(direction, WORKLOADS)
 
 
 def cpu_baseline(w, g_dev, budget_s: float = 10.0):
@@ -262,14 +269,16 @@ def main(argv=None):
                     help="0..4; the headline is 1 (small-LM layer)")
     ap.add_argument("--sets", type=int, default=2, help="input/output sets to rotate")
     ap.add_argument("--direction",
-                    choices=("fwd", "bwd", "decode", "mixer", "mixer_bwd", "mixer_train", "lti"),
+                    choices=("fwd", "bwd", "decode", "mixer", "mixer_bwd", "mixer_train",
+                             "mixer_decode", "lti"),
                     default="fwd",
                     help="fwd: kla_scan_fwd (the headline); bwd: kla_scan_bwd; decode: "
                          "kla_decode_step on one token of every channel of the workload; "
                          "mixer: kla_mixer_fwd on the mixer workload of the same key; "
                          "mixer_bwd: kla_mixer_bwd on the mixer workload; "
                          "mixer_train: kla_mixer_fwd keeping its states, then kla_mixer_bwd "
-                         "from them (one training step of the layer); "
+                         "from them (one training step of the layer); mixer_decode: "
+                         "kla_mixer_decode_step on one token of every channel; "
                          "lti: kla_scan_lti_fwd on the time-invariant workload of that key")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
@@ -311,8 +320,8 @@ def main(argv=None):
     from kla_inputs import make_lti_workload, make_mixer_workload, make_workload
     from linear_attention_sequence_kla_amd import (
         bwd_workspace_size, decode_step, get_workspace, lti_workspace_size, mixer_bwd,
-        mixer_bwd_workspace_size, mixer_fwd, mixer_states_shape, scan_bwd, scan_fwd,
-        scan_lti_fwd, workspace_health, workspace_size)
+        mixer_bwd_workspace_size, mixer_decode_step, mixer_fwd, mixer_states_shape, scan_bwd,
+        scan_fwd, scan_lti_fwd, workspace_health, workspace_size)
 
     d = args.direction
     if args.workload not in workloads_for(d):
@@ -329,7 +338,8 @@ def main(argv=None):
                            lti_workspace_size(*w.shape, TORCH_DTYPE[w.dtype]),
                            mixer_bwd_workspace_size(*w.shape, TORCH_DTYPE[w.dtype])), dev, stream)
     sets = []
-    for k in range(args.sets if d != "decode" else 0):
+    decoding = d in ("decode", "mixer_decode")
+    for k in range(args.sets if not decoding else 0):
         make = {"mixer": make_mixer_workload, "mixer_bwd": make_mixer_workload,
                 "mixer_train": make_mixer_workload, "lti": make_lti_workload}.get(d, make_workload)
         g = make(args.workload, device=dev, seed=w.seed + 1000 * k)
@@ -360,6 +370,16 @@ def main(argv=None):
             g = {n: v[:, :, 0].contiguous() for n, v in g.items()}
             sets.append((g, tuple(x.clone() for x in make_initial_state(
                 w.B, w.H, w.D, random=True, seed=k, device=dev))))
+    if d == "mixer_decode":
+        # one mixer token per channel; the state is updated in place each step
+        from kla_inputs import make_initial_state, make_mixer_inputs
+        for k in range(args.sets):
+            g = make_mixer_inputs((w.B, w.H, 1, w.D), w.dtype, w.seed + 1000 * k, dev)
+            g = {n: (v[:, :, 0] if v.dim() == 4 else v).contiguous() for n, v in g.items()}
+            g["out"] = torch.empty((w.B, w.H, w.D), dtype=torch.float32, device=dev)
+            g["var"] = torch.empty((w.B, w.H, w.D), dtype=torch.float32, device=dev)
+            sets.append((g, tuple(x.clone() for x in make_initial_state(
+                w.B, w.H, w.D, random=True, seed=k, device=dev))))
     grads = None
     if d == "bwd":
         grads = tuple(torch.empty(w.shape, dtype=torch.float32, device=dev) for _ in range(4))
@@ -372,6 +392,9 @@ def main(argv=None):
         g, out = sets[i % len(sets)]
         if d == "decode":
             decode_step(g["a"], g["p"], g["phi"], g["b"], out[0], out[1])
+        elif d == "mixer_decode":
+            mixer_decode_step(g["k"], g["v"], g["lam_v"], g["q"], g["a"], g["p"], out[0], out[1],
+                              out=g["out"], var=g["var"])
         elif d == "fwd":
             scan_fwd(g["a"], g["p"], g["phi"], g["b"], g["lam0"], g["eta0"], out=out,
                      workspace=ws)
@@ -442,7 +465,7 @@ def main(argv=None):
     if health != 0:
         print("warning: workspace health word %#x" % health, file=sys.stderr)
 
-    n = w.elements if d != "decode" else w.channels
+    n = w.elements if not decoding else w.channels
     ms_step = wall * 1e3 / args.steps
     k_avg = sum(kernel_ms) / len(kernel_ms)
     bpe = bytes_per_element(w.dtype, d)
@@ -494,6 +517,10 @@ def main(argv=None):
                          "(gates, scan, readout and variance in one pass)")
     if d == "decode":
         rec["metric"] = "KLA decode step channel updates (B*H*D)/s, one token per step"
+        rec["config"]["elements"] = n
+    if d == "mixer_decode":
+        rec["metric"] = ("KLA fused mixer decode step channel updates (B*H*D)/s, one token "
+                         "per step (readout and variance written)")
         rec["config"]["elements"] = n
     if not args.no_cpu_baseline and d == "fwd":
         rec["cpu_baseline"] = cpu_baseline(w, sets[0][0])

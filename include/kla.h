@@ -2,7 +2,7 @@
  * kla.h -- C ABI of libkla: the Kalman Linear Attention (KLA) scan on AMD
  * Instinct MI355X (gfx950) -- forward pass, its backward pass, the fused
  * mixer (forward and backward), the time-invariant-gate form and the
- * one-token decode step.
+ * one-token decode steps of the scan and of the mixer.
  *
  * The operation (Pith review of arXiv 2602.10743, "What carries the
  * argument" and "Circularity check"; "KLA Part 1" primer, sections 2 and
@@ -170,6 +170,32 @@ KLA_API kla_status kla_scan_bwd(const void *a, const void *p, kla_dtype in_dtype
 KLA_API kla_status kla_decode_step(const void *a, const void *p, const void *phi,
                                    const void *b, kla_dtype in_dtype,
                                    float *lam, float *eta, int64_t n_channels, void *stream);
+
+/*
+ * One decode step of the fused mixer: the token step of kla_mixer_fwd for
+ * every channel of one token, on a running state, in place.
+ *
+ * Channel i (i < n_channels = B*H*D, laid out as [B, H, D]) forms
+ * phi = k^2 lam_v and b = k lam_v v from its token inputs, takes the gates
+ * a, p of channel i % hd (hd = H*D), applies the step of kla_decode_step to
+ * (lam, eta), and writes the readout out = q eta / lam and the variance
+ * var = 1 / lam of the new state (computed in float64; the state is stored
+ * back in float32).  Passing kla_mixer_fwd's lam_T, eta_T as the state
+ * continues a sequence whose prefix went through kla_mixer_fwd.
+ *
+ *   k, v, lam_v, q  device pointers, [n_channels] of in_dtype.
+ *   a, p            device pointers, [hd] float32.
+ *   lam, eta        device pointers, [n_channels] float32, read and written.
+ *   out             device pointer, [n_channels] float32, written.
+ *   var             device pointer, [n_channels] float32, written; may be NULL.
+ *   n_channels      a multiple of hd (0: no-op).
+ * No workspace; asynchronous on `stream`; errors as for kla_scan_fwd.
+ */
+KLA_API kla_status kla_mixer_decode_step(const void *k, const void *v, const void *lam_v,
+                                         const void *q, kla_dtype in_dtype,
+                                         const float *a, const float *p,
+                                         float *lam, float *eta, float *out, float *var,
+                                         int64_t n_channels, int64_t hd, void *stream);
 
 /*
  * Forward KLA scan for time-invariant gates (the linear time-invariant case

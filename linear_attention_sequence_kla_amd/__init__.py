@@ -1,6 +1,6 @@
 """libkla: the Kalman Linear Attention (KLA) scan on AMD MI355X (gfx950):
 forward and backward scan, time-invariant-gate scan, fused mixer (forward
-and backward), decode step.
+and backward), decode steps of the scan and of the mixer.
 
 The work happens in ``libkla.so`` (HIP kernels behind a C ABI declared in
 ``include/kla.h``); ``kla`` is its ctypes binding.
@@ -9,5 +9,5 @@ The work happens in ``libkla.so`` (HIP kernels behind a C ABI declared in
 from .kla import (  # noqa: F401
     KLAMixer, KLAScan, KlaError, LIBRARY, bwd_workspace_size, decode_step, get_workspace,
     kla_mixer, kla_scan, library, lti_workspace_size, mixer_bwd, mixer_bwd_workspace_size,
-    mixer_fwd, mixer_states_shape, mixer_workspace_size, scan_bwd, scan_fwd, scan_lti_fwd,
-    workspace_health, workspace_size)
+    mixer_decode_step, mixer_fwd, mixer_states_shape, mixer_workspace_size, scan_bwd, scan_fwd,
+    scan_lti_fwd, workspace_health, workspace_size)

@@ -624,6 +624,54 @@ kla_status kla_decode_step(const void* a, const void* p, const void* phi, const 
     return KLA_OK;
 }
 
+kla_status kla_mixer_decode_step(const void* k, const void* v, const void* lam_v, const void* q,
+                                 kla_dtype in_dtype, const float* a, const float* p, float* lam,
+                                 float* eta, float* out, float* var, int64_t n_channels,
+                                 int64_t hd, void* stream) {
+    t_detail[0] = '\0';
+    if (n_channels < 0 || hd < 0)
+        return fail(KLA_ERR_INVALID_ARG, "negative size n_channels=%lld hd=%lld",
+                    (long long)n_channels, (long long)hd);
+    if (in_dtype != KLA_DTYPE_F32 && in_dtype != KLA_DTYPE_BF16)
+        return fail(KLA_ERR_UNSUPPORTED, "unknown input dtype %d", int(in_dtype));
+    if (n_channels == 0) return KLA_OK;
+    if (hd == 0 || n_channels % hd != 0)
+        return fail(KLA_ERR_INVALID_ARG, "n_channels=%lld is not a multiple of hd=%lld",
+                    (long long)n_channels, (long long)hd);
+    if (n_channels > INT64_MAX / 8)
+        return fail(KLA_ERR_INVALID_ARG, "channel count overflows");
+    const void* ins[4] = {k, v, lam_v, q};
+    const char* names[4] = {"k", "v", "lam_v", "q"};
+    const size_t esz = in_dtype == KLA_DTYPE_F32 ? 4 : 2;
+    for (int i = 0; i < 4; ++i) {
+        if (!ins[i]) return fail(KLA_ERR_INVALID_ARG, "%s is NULL", names[i]);
+        if (misaligned(ins[i], esz))
+            return fail(KLA_ERR_UNSUPPORTED, "%s is not %zu-byte aligned", names[i], esz);
+    }
+    const void* req[5] = {a, p, lam, eta, out};
+    const char* rnames[5] = {"a", "p", "lam", "eta", "out"};
+    for (int i = 0; i < 5; ++i)
+        if (!req[i]) return fail(KLA_ERR_INVALID_ARG, "%s is NULL", rnames[i]);
+    const void* f32s[6] = {a, p, lam, eta, out, var};
+    for (int i = 0; i < 6; ++i)
+        if (f32s[i] && misaligned(f32s[i], 4))
+            return fail(KLA_ERR_UNSUPPORTED, "float32 arguments must be 4-byte aligned");
+    const size_t in_bytes = size_t(n_channels) * esz, f_bytes = size_t(n_channels) * 4;
+    const size_t ch_bytes = size_t(hd) * 4;
+    const Buffer bufs[10] = {{k, in_bytes, "k", false},         {v, in_bytes, "v", false},
+                             {lam_v, in_bytes, "lam_v", false}, {q, in_bytes, "q", false},
+                             {a, ch_bytes, "a", false},         {p, ch_bytes, "p", false},
+                             {lam, f_bytes, "lam", true},       {eta, f_bytes, "eta", true},
+                             {out, f_bytes, "out", true},       {var, f_bytes, "var", true}};
+    kla_status st = check_overlaps(bufs, 10);
+    if (st != KLA_OK) return st;
+    const hipError_t err =
+        kla::launch_mixer_decode(k, v, lam_v, q, in_dtype, a, p, lam, eta, out, var, n_channels,
+                                 hd, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(KLA_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
+    return KLA_OK;
+}
+
 kla_status kla_workspace_health(void* workspace, uint32_t* flags_out, void* stream) {
     t_detail[0] = '\0';
     if (!workspace) return fail(KLA_ERR_WORKSPACE, "workspace is NULL");

@@ -9,7 +9,8 @@
 // It is computed in float64 as the homogeneous step of the scan kernel
 // (Z' = p lam + a^2, lam' = (lam + phi Z') / Z', eta' = (a eta + b Z') / Z')
 // and stored back in float32.  Channels are independent: one thread each,
-// consecutive threads on consecutive channels (coalesced).
+// consecutive threads on consecutive channels (coalesced).  The fused mixer
+// has a decode step of its own (kla_mixer_decode_kernel).
 
 #include "kla_internal.h"
 
@@ -48,7 +49,56 @@ __global__ __launch_bounds__(256) void kla_decode_kernel(const In* __restrict__ 
     }
 }
 
+// One token of the fused mixer (the decode form of the forward kernel's
+// mixer mode): gates phi = k^2 lam_v and b = k lam_v v, channel gates a, p
+// from the [H*D] arrays (channel i uses i % hd), the same float64 step as
+// above, the state stored back in float32, and the readout q eta' / lam'
+// and variance 1 / lam' from the float64 state.
+template <typename In>
+__global__ __launch_bounds__(256) void kla_mixer_decode_kernel(
+    const In* __restrict__ k, const In* __restrict__ v, const In* __restrict__ lam_v,
+    const In* __restrict__ q, const float* __restrict__ a, const float* __restrict__ p,
+    float* __restrict__ lam, float* __restrict__ eta, float* __restrict__ out,
+    float* __restrict__ var, int64_t n, int64_t hd) {
+    const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+        const double kv = load_one<In>(k, i), vv = load_one<In>(v, i);
+        const double lv = load_one<In>(lam_v, i), qv = load_one<In>(q, i);
+        const int64_t c = i % hd;
+        const double av = a[c], pv = p[c];
+        const double l = lam[i], e = eta[i];
+        const double z = fma(pv, l, av * av);
+        const double r = recip(z);
+        const double nl = fma(kv * kv * lv, z, l) * r;
+        const double ne = fma(kv * lv * vv, z, av * e) * r;
+        const double rl = recip(nl);
+        lam[i] = float(nl);
+        eta[i] = float(ne);
+        out[i] = float(qv * (ne * rl));
+        if (var) var[i] = float(rl);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_mixer_decode(const void* k, const void* v, const void* lam_v, const void* q,
+                               kla_dtype dtype, const float* a, const float* p, float* lam,
+                               float* eta, float* out, float* var, int64_t n, int64_t hd,
+                               hipStream_t stream) {
+    const int64_t blocks = (n + 255) / 256;
+    const dim3 grid(unsigned(blocks < 65536 ? blocks : 65536)), block(256);
+    if (dtype == KLA_DTYPE_F32)
+        hipLaunchKernelGGL(kla_mixer_decode_kernel<float>, grid, block, 0, stream,
+                           static_cast<const float*>(k), static_cast<const float*>(v),
+                           static_cast<const float*>(lam_v), static_cast<const float*>(q), a, p,
+                           lam, eta, out, var, n, hd);
+    else
+        hipLaunchKernelGGL(kla_mixer_decode_kernel<uint16_t>, grid, block, 0, stream,
+                           static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                           static_cast<const uint16_t*>(lam_v), static_cast<const uint16_t*>(q),
+                           a, p, lam, eta, out, var, n, hd);
+    return hipGetLastError();
+}
 
 hipError_t launch_decode(const void* a, const void* p, const void* phi, const void* b,
                          kla_dtype dtype, float* lam, float* eta, int64_t n, hipStream_t stream) {

@@ -120,5 +120,12 @@ hipError_t launch_mixer_grad_reduce(const double* partial, float* g_a, float* g_
                                     hipStream_t stream);
 hipError_t launch_decode(const void* a, const void* p, const void* phi, const void* b,
                          kla_dtype dtype, float* lam, float* eta, int64_t n, hipStream_t stream);
+// One mixer token per channel: k, v, lam_v, q [n] of dtype; a, p [hd] float32
+// (channel i uses i % hd); lam, eta updated in place; out (and var unless
+// NULL) written.
+hipError_t launch_mixer_decode(const void* k, const void* v, const void* lam_v, const void* q,
+                               kla_dtype dtype, const float* a, const float* p, float* lam,
+                               float* eta, float* out, float* var, int64_t n, int64_t hd,
+                               hipStream_t stream);
 
 }  // namespace kla

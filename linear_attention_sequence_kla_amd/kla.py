@@ -80,6 +80,9 @@ def load_library(path: str) -> ctypes.CDLL:
     lib.kla_mixer_bwd.restype = ctypes.c_int
     lib.kla_decode_step.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, vp, i64, vp]
     lib.kla_decode_step.restype = ctypes.c_int
+    lib.kla_mixer_decode_step.argtypes = [vp, vp, vp, vp, ctypes.c_int] + [vp] * 6 + [
+        i64, i64, vp]
+    lib.kla_mixer_decode_step.restype = ctypes.c_int
     lib.kla_workspace_health.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), vp]
     lib.kla_workspace_health.restype = ctypes.c_int
     lib.kla_status_string.argtypes = [ctypes.c_int]
@@ -523,6 +526,49 @@ def decode_step(a: torch.Tensor, p: torch.Tensor, phi: torch.Tensor, b: torch.Te
                                      _ptr(lam), _ptr(eta), a.numel(),
                                      ctypes.c_void_p(stream.cuda_stream)))
     return lam, eta
+
+
+def mixer_decode_step(k: torch.Tensor, v: torch.Tensor, lam_v: torch.Tensor, q: torch.Tensor,
+                      a: torch.Tensor, p: torch.Tensor, lam: torch.Tensor, eta: torch.Tensor,
+                      want_var: bool = True, out: torch.Tensor | None = None,
+                      var: torch.Tensor | None = None):
+    """One token of the fused mixer on the running state (lam, eta), in place,
+    on the current stream (kla_mixer_decode_step).  k, v, lam_v, q: [B, H, D]
+    contiguous, all float32 or all bfloat16; a, p: [H, D] float32; lam, eta:
+    [B, H, D] float32.  Returns (out, var, lam, eta): the readout q eta / lam
+    and the variance 1 / lam of the new state (var None unless want_var)."""
+    if k.dim() != 3:
+        raise ValueError("token inputs must be [B, H, D], got shape %s" % (tuple(k.shape),))
+    for name, t in zip(("k", "v", "lam_v", "q"), (k, v, lam_v, q)):
+        if t.shape != k.shape or t.dtype != k.dtype:
+            raise ValueError("%s must match k in shape and dtype" % name)
+        if not t.is_cuda or t.device != k.device or not t.is_contiguous():
+            raise ValueError("%s must be contiguous on k's GPU" % name)
+    if k.dtype not in _DTYPES:
+        raise ValueError("token dtype must be float32 or bfloat16, got %s" % k.dtype)
+    B, H, D = k.shape
+    dev = k.device
+    for name, t in (("a", a), ("p", p)):
+        if t is None:
+            raise ValueError("%s is required" % name)
+        _check_f32(name, t, (H, D), dev)
+    for name, t in (("lam", lam), ("eta", eta)):
+        if t is None:
+            raise ValueError("%s is required" % name)
+        _check_f32(name, t, k.shape, dev)
+    if out is None:
+        out = torch.empty(k.shape, dtype=torch.float32, device=dev)
+    _check_f32("out", out, k.shape, dev)
+    if want_var and var is None:
+        var = torch.empty(k.shape, dtype=torch.float32, device=dev)
+    if not want_var:
+        var = None
+    _check_f32("var", var, k.shape, dev)
+    stream = torch.cuda.current_stream(dev)
+    _check(library().kla_mixer_decode_step(
+        _ptr(k), _ptr(v), _ptr(lam_v), _ptr(q), _DTYPES[k.dtype], _ptr(a), _ptr(p), _ptr(lam),
+        _ptr(eta), _ptr(out), _ptr(var), k.numel(), H * D, ctypes.c_void_p(stream.cuda_stream)))
+    return out, var, lam, eta
 
 
 def workspace_health(workspace: torch.Tensor) -> int:

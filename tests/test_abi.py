@@ -232,3 +232,32 @@ def test_mixer_bwd_argument_errors_before_launch(lib):
     assert st == 2 and "16-byte" in msg
     st, msg = call(states=0x1000000 - 64)  # g_k is written over the states
     assert st == 1 and "overlaps" in msg
+
+
+def test_mixer_decode_argument_errors_before_launch(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("uses fake device pointers; argument errors are tested on GPUs elsewhere")
+    vp = ctypes.c_void_p
+
+    def call(k=0x100000, n=24, hd=12, out=0x1000000, lam=0x800000, var=0):
+        st = lib.kla_mixer_decode_step(vp(k), vp(0x200000), vp(0x300000), vp(0x400000), 0,
+                                       vp(0x500000), vp(0x600000), vp(lam), vp(0x900000),
+                                       vp(out), vp(var), n, hd, None)
+        return st, lib.kla_last_error_detail().decode()
+    st, msg = call(k=0)
+    assert st == 1 and "k is NULL" in msg
+    st, msg = call(out=0)
+    assert st == 1 and "out is NULL" in msg
+    st, msg = call(n=25)
+    assert st == 1 and "multiple" in msg
+    st, msg = call(hd=0)
+    assert st == 1
+    st, msg = call(n=-1)
+    assert st == 1
+    st, msg = call(out=0x800000 + 16)  # the readout runs into the state
+    assert st == 1 and "overlaps" in msg
+    st, msg = call(var=0x100000 + 8)   # the variance would overwrite k
+    assert st == 1 and "overlaps" in msg
+    st, _ = call(k=0, n=0)
+    assert st == 0

@@ -100,3 +100,54 @@ def test_graph_replays_mixer_and_lti():
         scan_lti_fwd(lt["a"], lt["p"], lt["phi"], lt["b"], workspace=ws)
         torch.cuda.synchronize(DEV)
     assert workspace_health(ws) == 0
+
+
+def test_graph_replays_mixer_training_step():
+    """A mixer training step -- kla_mixer_fwd keeping its states, kla_mixer_bwd
+    from them -- and a recomputing kla_mixer_bwd, captured in one graph on one
+    workspace and replayed three times with eager calls in between; every
+    replay equals the eager results bit for bit."""
+    from linear_attention_sequence_kla_amd import (mixer_bwd, mixer_bwd_workspace_size,
+                                                   mixer_fwd, mixer_states_shape,
+                                                   workspace_health)
+    from kla_inputs import make_initial_state, make_mixer_inputs
+    shape = (2, 2, 700, 48)
+    mx = {n: v.to(DEV) for n, v in make_mixer_inputs(shape, "f32", seed=43).items()}
+    lam0, eta0 = (x.to(DEV) for x in make_initial_state(2, 2, 48, random=True, seed=43))
+    gen = torch.Generator(device=DEV).manual_seed(44)
+    g_out = torch.randn(shape, generator=gen, device=DEV)
+    g_var = torch.randn(shape, generator=gen, device=DEV)
+    ws = torch.zeros(mixer_bwd_workspace_size(*shape), dtype=torch.uint8, device=DEV)
+    tok = (mx["k"], mx["v"], mx["lam_v"], mx["q"], mx["a"], mx["p"])
+
+    def grads_out():
+        return tuple(torch.empty(shape, device=DEV) for _ in range(4)) + tuple(
+            torch.empty((2, 48), device=DEV) for _ in range(2))
+
+    states = torch.empty(mixer_states_shape(*shape), dtype=torch.float64, device=DEV)
+    e_out, e_var, _, _ = mixer_fwd(*tok, lam0, eta0, workspace=ws, states=states)
+    e_kept = mixer_bwd(*tok, g_out, g_var, lam0, eta0, workspace=ws, states=states,
+                       need_state_grads=False)
+    e_again = mixer_bwd(*tok, g_out, g_var, lam0, eta0, workspace=ws, need_state_grads=False)
+    torch.cuda.synchronize(DEV)
+    fo, fv = torch.empty(shape, device=DEV), torch.empty(shape, device=DEV)
+    kept, again = grads_out(), grads_out()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        mixer_fwd(*tok, lam0, eta0, out=fo, var=fv, workspace=ws, states=states)
+        mixer_bwd(*tok, g_out, g_var, lam0, eta0, workspace=ws, states=states, out=kept,
+                  need_state_grads=False)
+        mixer_bwd(*tok, g_out, g_var, lam0, eta0, workspace=ws, out=again,
+                  need_state_grads=False)
+    torch.cuda.synchronize(DEV)
+    for replay in range(3):
+        for t in (fo, fv, states) + kept + again:
+            t.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize(DEV)
+        assert torch.equal(fo, e_out) and torch.equal(fv, e_var), replay
+        for got, want in zip(kept + again, e_kept[:6] + e_again[:6]):
+            assert torch.equal(got, want), replay
+        mixer_fwd(*tok, workspace=ws)  # eager work on the same workspace
+        torch.cuda.synchronize(DEV)
+    assert workspace_health(ws) == 0

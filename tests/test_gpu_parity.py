@@ -100,6 +100,34 @@ def test_workload_full_size_sampled(key):
     assert bool((lam > 0).all())
 
 
+def test_largest_offsets():
+    """The largest per-wave address span the library accepts: D = 1, so the
+    64 channels of a wave lie in 64 slabs of T elements, and T just under the
+    limit of 32-bit per-wave byte offsets (63 T < 2^30; 4.35 GB per float32
+    tensor).  The oracle checks whole channels, including the first and the
+    last (the farthest slab)."""
+    from linear_attention_sequence_kla_amd import scan_fwd
+    B, H, T, D = 8, 8, 17_000_000, 1
+    _say("largest offsets %s" % ((B, H, T, D),))
+    g = make_gates((B, H, T, D), "std", "f32", seed=77, device=DEV)
+    lam0, eta0 = make_initial_state(B, H, D, random=True, seed=77, device=DEV)
+    lam, eta = scan_fwd(g["a"], g["p"], g["phi"], g["b"], lam0, eta0)
+    torch.cuda.synchronize(DEV)
+    assert health() == 0
+    q = _sample_channels(B * H * D, 3, seed=77)
+    gs = {k: _gather(g[k], D, q).cpu() for k in ("a", "p", "phi", "b")}
+    qd = torch.as_tensor(q, device=DEV)
+    ref = oracle_scan(gs["a"], gs["p"], gs["phi"], gs["b"],
+                      lam0.reshape(-1)[qd].reshape(1, 1, -1).cpu(),
+                      eta0.reshape(-1)[qd].reshape(1, 1, -1).cpu())
+    rep = compare(_gather(lam, D, q).cpu(), _gather(eta, D, q).cpu(), *ref)
+    _say("largest offsets: %s" % rep)
+    assert_parity(rep, TOL_F32, "largest offsets")
+    assert bool(torch.isfinite(lam).all()) and bool(torch.isfinite(eta).all())
+    del g, lam, eta
+    torch.cuda.empty_cache()
+
+
 SHAPES = [
     # (B, H, T, D, gates, dtype)
     (1, 1, 1, 1, "std", "f32"),          # a single token, a single channel

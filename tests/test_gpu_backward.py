@@ -150,6 +150,36 @@ def test_backward_workload_sampled(key):
     assert_grad_parity(rep, TOL_BF16 if w.dtype == "bf16" else TOL_F32, w.describe())
 
 
+def test_backward_largest_offsets():
+    """The backward pass at the largest per-wave address span the library
+    accepts (D = 1: a wave's 64 channels in 64 slabs of T tokens, 63 T just
+    under 2^30); the oracle checks whole channels including the farthest."""
+    from linear_attention_sequence_kla_amd import scan_bwd, scan_fwd
+    B, H, T, D = 8, 8, 17_000_000, 1
+    _say("backward, largest offsets %s" % ((B, H, T, D),))
+    g = make_gates((B, H, T, D), "std", "f32", seed=78, device=DEV)
+    g["lam0"], g["eta0"] = make_initial_state(B, H, D, random=True, seed=78, device=DEV)
+    g_lam, g_eta = upstream((B, H, T, D), 78, device=DEV)
+    lam, eta = scan_fwd(g["a"], g["p"], g["phi"], g["b"], g["lam0"], g["eta0"])
+    out = scan_bwd(g["a"], g["p"], lam, eta, g_lam, g_eta, g["lam0"], g["eta0"])
+    torch.cuda.synchronize(DEV)
+    assert health() == 0
+    q = np.array([0, 1, 31, 62, 63])
+    gs = {k: _gather(g[k], D, q).cpu() for k in ("a", "p", "phi", "b")}
+    sel = torch.as_tensor(q, device=DEV)
+    gs["lam0"] = g["lam0"].reshape(-1)[sel].reshape(1, 1, -1).cpu()
+    gs["eta0"] = g["eta0"].reshape(-1)[sel].reshape(1, 1, -1).cpu()
+    grads, mags = oracle_grads(gs, _gather(g_lam, D, q).cpu(), _gather(g_eta, D, q).cpu())
+    got = {k: _gather(v, D, q).cpu() for k, v in zip(("a", "p", "phi", "b"), out[:4])}
+    got["lam0"] = out[4].reshape(-1)[sel].reshape(1, 1, -1).cpu()
+    got["eta0"] = out[5].reshape(-1)[sel].reshape(1, 1, -1).cpu()
+    rep = compare_grads(got, grads, mags)
+    _say("backward, largest offsets: %s" % rep)
+    assert_grad_parity(rep, TOL_F32, "backward, largest offsets")
+    del g, g_lam, g_eta, lam, eta, out
+    torch.cuda.empty_cache()
+
+
 def test_null_upstream_and_no_state_grads():
     """g_eta = NULL means zero; g_lam0/g_eta0 may be skipped."""
     from linear_attention_sequence_kla_amd import scan_bwd, scan_fwd

@@ -65,6 +65,24 @@ def test_scan_forward_and_backward(debug_build, shape):
     assert_grad_parity(compare_grads(got, grads, mags), TOL_F32, "backward %s" % (shape,))
 
 
+@pytest.mark.parametrize("shape", [(1, 2, 9000, 128), (3, 3, 2000, 256)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_scan_forward_bf16(debug_build, shape):
+    """bfloat16 gates on whole rows (D = 128) and on paired quarter rows."""
+    from kla_metric import TOL_BF16
+    from linear_attention_sequence_kla_amd import scan_fwd
+    B, H, T, D = shape
+    g = make_gates(shape, "std", "bf16", seed=T + 1)
+    g["lam0"], g["eta0"] = make_initial_state(B, H, D, random=True, seed=T + 1)
+    d = {n: v.to(DEV) for n, v in g.items()}
+    for _ in range(2):
+        lam, eta = scan_fwd(d["a"], d["p"], d["phi"], d["b"], d["lam0"], d["eta0"])
+        torch.cuda.synchronize(DEV)
+    assert _health() == 0
+    ref = oracle_scan(g["a"], g["p"], g["phi"], g["b"], g["lam0"], g["eta0"])
+    assert_parity(compare(lam.cpu(), eta.cpu(), *ref), TOL_BF16, "bf16 forward %s" % (shape,))
+
+
 @pytest.mark.parametrize("shape", [(1, 2, 6000, 64), (2, 4, 1500, 128)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_mixer_forward_and_backward(debug_build, shape):

@@ -142,6 +142,8 @@ SHAPES = [
     (5, 1, 64, 13, "hard", "f32"),       # T below one wave's rows
     (3, 3, 1000, 128, "hard", "f32"),    # row halves paired per XCD, partial last block
     (2, 5, 400, 256, "std", "bf16"),     # paired quarter rows, bf16
+    (3, 1, 777, 6, "hard", "bf16"),      # bf16, small even D, hard gates
+    (2, 3, 250, 2, "slow", "bf16"),      # bf16, D = 2
 ]
 
 

@@ -75,7 +75,7 @@ struct BwdArgs {
 constexpr int kFwdRows = 28, kFwdWaves = 4, kFwdMatrixWords = 7, kFwdStateWords = 2;
 constexpr int kLtiRows = 64, kLtiWaves = 4;
 constexpr int kMixBwdRows = 8, kMixBwdWaves = 8;
-constexpr int kBwdRows = 20, kBwdWaves = 4, kBwdMatrixWords = 6, kBwdStateWords = 2;
+constexpr int kBwdRows = 14, kBwdWaves = 8, kBwdMatrixWords = 6, kBwdStateWords = 2;
 
 // kMixerState: the mixer's gates; writes the float64 states (lam, eta) after
 // every kMixBwdRows-th row into FwdArgs::bstate, for the mixer's backward

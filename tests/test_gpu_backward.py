@@ -60,7 +60,7 @@ def health():
 
 SHAPES = [
     (1, 1, 1, 1, "std", "f32"),
-    (1, 1, 81, 1, "std", "f32"),        # one row past one backward tile
+    (1, 1, 113, 1, "std", "f32"),       # one row past one backward tile
     (2, 3, 1000, 7, "std", "f32"),
     (3, 2, 517, 100, "slow", "f32"),
     (1, 2, 333, 64, "hard", "f32"),

@@ -72,6 +72,23 @@ bool overlaps(const void* x, size_t nx, const void* y, size_t ny) {
 
 bool misaligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a != 0; }
 
+// dtype and status codes come from C callers (or ctypes) as plain ints.  C++
+// may not even read an enum object whose value lies outside the enum's range,
+// so an argument is validated through its object representation before it is
+// used as the enum.
+static_assert(sizeof(kla_dtype) == sizeof(int32_t) && sizeof(kla_status) == sizeof(int32_t),
+              "the ABI's enums are int-sized");
+template <typename E>
+int32_t raw_bits(const E& e) {
+    int32_t r;
+    memcpy(&r, &e, sizeof(r));
+    return r;
+}
+bool known_dtype(const kla_dtype& d) {
+    const int32_t r = raw_bits(d);
+    return r == KLA_DTYPE_F32 || r == KLA_DTYPE_BF16;
+}
+
 struct Buffer {
     const void* p;
     size_t bytes;
@@ -92,14 +109,14 @@ kla_status check_overlaps(const Buffer* bufs, int n) {
 
 // Sizes, dtype and the plan shared by both directions.  Sets *empty when some
 // size is 0 (nothing to do).
-kla_status common_checks(int64_t B, int64_t H, int64_t T, int64_t D, kla_dtype dt, int rows,
-                         int waves, int mw, int sw, Plan* pl, bool* empty) {
+kla_status common_checks(int64_t B, int64_t H, int64_t T, int64_t D, const kla_dtype& dt,
+                         int rows, int waves, int mw, int sw, Plan* pl, bool* empty) {
     t_detail[0] = '\0';
     if (B < 0 || H < 0 || T < 0 || D < 0)
         return fail(KLA_ERR_INVALID_ARG, "negative size B=%lld H=%lld T=%lld D=%lld",
                     (long long)B, (long long)H, (long long)T, (long long)D);
-    if (dt != KLA_DTYPE_F32 && dt != KLA_DTYPE_BF16)
-        return fail(KLA_ERR_UNSUPPORTED, "unknown input dtype %d", int(dt));
+    if (!known_dtype(dt))
+        return fail(KLA_ERR_UNSUPPORTED, "unknown input dtype %d", int(raw_bits(dt)));
     if (!kla::make_plan(B, H, T, D, rows, waves, mw, sw, pl))
         return fail(KLA_ERR_INVALID_ARG, "sizes overflow: B=%lld H=%lld T=%lld D=%lld",
                     (long long)B, (long long)H, (long long)T, (long long)D);
@@ -157,7 +174,7 @@ extern "C" {
 
 size_t kla_scan_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int64_t D,
                                    kla_dtype in_dtype) {
-    if (in_dtype != KLA_DTYPE_F32 && in_dtype != KLA_DTYPE_BF16) return 0;
+    if (!known_dtype(in_dtype)) return 0;
     Plan pl;
     if (!kla::make_plan(B, H, T, D, kla::kFwdRows, kla::kFwdWaves, kla::kFwdMatrixWords,
                         kla::kFwdStateWords, &pl) || pl.N == 0)
@@ -167,7 +184,7 @@ size_t kla_scan_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int64_t D,
 
 size_t kla_scan_bwd_workspace_size(int64_t B, int64_t H, int64_t T, int64_t D,
                                    kla_dtype in_dtype) {
-    if (in_dtype != KLA_DTYPE_F32 && in_dtype != KLA_DTYPE_BF16) return 0;
+    if (!known_dtype(in_dtype)) return 0;
     Plan pl;
     if (!kla::make_plan(B, H, T, D, kla::kBwdRows, kla::kBwdWaves, kla::kBwdMatrixWords,
                         kla::kBwdStateWords, &pl) || pl.N == 0)
@@ -234,7 +251,7 @@ kla_status kla_scan_fwd(const void* a, const void* p, const void* phi, const voi
 
 size_t kla_scan_lti_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int64_t D,
                                        kla_dtype in_dtype) {
-    if (in_dtype != KLA_DTYPE_F32 && in_dtype != KLA_DTYPE_BF16) return 0;
+    if (!known_dtype(in_dtype)) return 0;
     Plan pl;
     if (!kla::make_plan(B, H, T, D, kla::kLtiRows, kla::kLtiWaves, kla::kFwdMatrixWords,
                         kla::kFwdStateWords, &pl) || pl.N == 0)
@@ -303,7 +320,7 @@ kla_status kla_scan_lti_fwd(const float* a, const float* p, const float* phi, co
 
 size_t kla_mixer_bwd_workspace_size(int64_t B, int64_t H, int64_t T, int64_t D,
                                     kla_dtype in_dtype) {
-    if (in_dtype != KLA_DTYPE_F32 && in_dtype != KLA_DTYPE_BF16) return 0;
+    if (!known_dtype(in_dtype)) return 0;
     MixerBwdLayout l;
     if (!mixer_bwd_layout(B, H, T, D, &l) || l.fwd.N == 0) return 0;
     return l.bytes;
@@ -596,8 +613,8 @@ kla_status kla_decode_step(const void* a, const void* p, const void* phi, const 
     t_detail[0] = '\0';
     if (n_channels < 0)
         return fail(KLA_ERR_INVALID_ARG, "negative channel count %lld", (long long)n_channels);
-    if (in_dtype != KLA_DTYPE_F32 && in_dtype != KLA_DTYPE_BF16)
-        return fail(KLA_ERR_UNSUPPORTED, "unknown input dtype %d", int(in_dtype));
+    if (!known_dtype(in_dtype))
+        return fail(KLA_ERR_UNSUPPORTED, "unknown input dtype %d", int(raw_bits(in_dtype)));
     if (n_channels == 0) return KLA_OK;
     if (n_channels > INT64_MAX / 8)
         return fail(KLA_ERR_INVALID_ARG, "channel count overflows");
@@ -632,8 +649,8 @@ kla_status kla_mixer_decode_step(const void* k, const void* v, const void* lam_v
     if (n_channels < 0 || hd < 0)
         return fail(KLA_ERR_INVALID_ARG, "negative size n_channels=%lld hd=%lld",
                     (long long)n_channels, (long long)hd);
-    if (in_dtype != KLA_DTYPE_F32 && in_dtype != KLA_DTYPE_BF16)
-        return fail(KLA_ERR_UNSUPPORTED, "unknown input dtype %d", int(in_dtype));
+    if (!known_dtype(in_dtype))
+        return fail(KLA_ERR_UNSUPPORTED, "unknown input dtype %d", int(raw_bits(in_dtype)));
     if (n_channels == 0) return KLA_OK;
     if (hd == 0 || n_channels % hd != 0)
         return fail(KLA_ERR_INVALID_ARG, "n_channels=%lld is not a multiple of hd=%lld",
@@ -692,7 +709,7 @@ kla_status kla_workspace_health(void* workspace, uint32_t* flags_out, void* stre
 }
 
 const char* kla_status_string(kla_status s) {
-    switch (s) {
+    switch (raw_bits(s)) {
         case KLA_OK: return "KLA_OK";
         case KLA_ERR_INVALID_ARG: return "KLA_ERR_INVALID_ARG";
         case KLA_ERR_UNSUPPORTED: return "KLA_ERR_UNSUPPORTED";

@@ -35,7 +35,8 @@ def test_abi_host_side_is_sanitizer_clean(tmp_path):
            "-I", os.path.join(ROOT, "include"), "-I", CSRC,
            os.path.join(ROOT, "tests", "abi_host_check.cpp"), os.path.join(CSRC, "kla_api.cpp"),
            "-o", exe]
-    subprocess.run(cmd, check=True, capture_output=True, timeout=300)
+    c = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
+    assert c.returncode == 0, c.stderr[-4000:]
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0",
                UBSAN_OPTIONS="print_stacktrace=1")
     r = subprocess.run([exe], capture_output=True, text=True, timeout=120, env=env)

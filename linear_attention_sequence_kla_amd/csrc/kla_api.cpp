@@ -88,6 +88,12 @@ bool known_dtype(const kla_dtype& d) {
     const int32_t r = raw_bits(d);
     return r == KLA_DTYPE_F32 || r == KLA_DTYPE_BF16;
 }
+// Rows per wave of the forward kernel for the argument's dtype, in the scan
+// or the mixer modes (any value for an unknown dtype, which common_checks
+// then rejects).
+int fwd_rows(const kla_dtype& d, bool mixer) {
+    return known_dtype(d) ? kla::fwd_rows(d, mixer) : kla::kFwdRows;
+}
 
 struct Buffer {
     const void* p;
@@ -155,8 +161,9 @@ size_t mixer_states_bytes(const Plan& pl, int64_t T) {
     return size_t(blocks) * size_t(pl.C) * 2 * sizeof(double);
 }
 
-bool mixer_bwd_layout(int64_t B, int64_t H, int64_t T, int64_t D, MixerBwdLayout* l) {
-    if (!kla::make_plan(B, H, T, D, kla::kFwdRows, kla::kFwdWaves, kla::kFwdMatrixWords,
+bool mixer_bwd_layout(int64_t B, int64_t H, int64_t T, int64_t D, const kla_dtype& dt,
+                      MixerBwdLayout* l) {
+    if (!kla::make_plan(B, H, T, D, fwd_rows(dt, true), kla::kFwdWaves, kla::kFwdMatrixWords,
                         kla::kFwdStateWords, &l->fwd) ||
         !kla::make_plan(B, H, T, D, kla::kMixBwdRows, kla::kMixBwdWaves, kla::kBwdMatrixWords,
                         kla::kBwdStateWords, &l->bwd))
@@ -176,8 +183,8 @@ size_t kla_scan_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int64_t D,
                                    kla_dtype in_dtype) {
     if (!known_dtype(in_dtype)) return 0;
     Plan pl;
-    if (!kla::make_plan(B, H, T, D, kla::kFwdRows, kla::kFwdWaves, kla::kFwdMatrixWords,
-                        kla::kFwdStateWords, &pl) || pl.N == 0)
+    if (!kla::make_plan(B, H, T, D, fwd_rows(in_dtype, false), kla::kFwdWaves,
+                        kla::kFwdMatrixWords, kla::kFwdStateWords, &pl) || pl.N == 0)
         return 0;
     return pl.ws.bytes;
 }
@@ -198,8 +205,9 @@ kla_status kla_scan_fwd(const void* a, const void* p, const void* phi, const voi
                         void* workspace, size_t workspace_bytes, void* stream) {
     Plan pl;
     bool empty = false;
-    kla_status st = common_checks(B, H, T, D, in_dtype, kla::kFwdRows, kla::kFwdWaves,
-                                  kla::kFwdMatrixWords, kla::kFwdStateWords, &pl, &empty);
+    kla_status st = common_checks(B, H, T, D, in_dtype, fwd_rows(in_dtype, false),
+                                  kla::kFwdWaves, kla::kFwdMatrixWords, kla::kFwdStateWords,
+                                  &pl, &empty);
     if (st != KLA_OK || empty) return st;
 
     const void* ins[4] = {a, p, phi, b};
@@ -322,7 +330,7 @@ size_t kla_mixer_bwd_workspace_size(int64_t B, int64_t H, int64_t T, int64_t D,
                                     kla_dtype in_dtype) {
     if (!known_dtype(in_dtype)) return 0;
     MixerBwdLayout l;
-    if (!mixer_bwd_layout(B, H, T, D, &l) || l.fwd.N == 0) return 0;
+    if (!mixer_bwd_layout(B, H, T, D, in_dtype, &l) || l.fwd.N == 0) return 0;
     return l.bytes;
 }
 
@@ -339,7 +347,7 @@ kla_status kla_mixer_bwd(const void* k, const void* v, const void* lam_v, const 
                                   kla::kBwdMatrixWords, kla::kBwdStateWords, &pl, &empty);
     if (st != KLA_OK || empty) return st;
     MixerBwdLayout lay;
-    if (!mixer_bwd_layout(B, H, T, D, &lay) || !lay.fwd.offsets_fit)
+    if (!mixer_bwd_layout(B, H, T, D, in_dtype, &lay) || !lay.fwd.offsets_fit)
         return fail(KLA_ERR_UNSUPPORTED, "sizes not supported: B=%lld H=%lld T=%lld D=%lld",
                     (long long)B, (long long)H, (long long)T, (long long)D);
 
@@ -456,7 +464,12 @@ kla_status kla_mixer_bwd(const void* k, const void* v, const void* lam_v, const 
 
 size_t kla_mixer_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int64_t D,
                                     kla_dtype in_dtype) {
-    return kla_scan_fwd_workspace_size(B, H, T, D, in_dtype);
+    if (!known_dtype(in_dtype)) return 0;
+    Plan pl;
+    if (!kla::make_plan(B, H, T, D, fwd_rows(in_dtype, true), kla::kFwdWaves,
+                        kla::kFwdMatrixWords, kla::kFwdStateWords, &pl) || pl.N == 0)
+        return 0;
+    return pl.ws.bytes;
 }
 
 size_t kla_mixer_states_size(int64_t B, int64_t H, int64_t T, int64_t D) {
@@ -474,8 +487,9 @@ kla_status kla_mixer_fwd(const void* k, const void* v, const void* lam_v, const 
                          void* workspace, size_t workspace_bytes, void* stream) {
     Plan pl;
     bool empty = false;
-    kla_status st = common_checks(B, H, T, D, in_dtype, kla::kFwdRows, kla::kFwdWaves,
-                                  kla::kFwdMatrixWords, kla::kFwdStateWords, &pl, &empty);
+    kla_status st = common_checks(B, H, T, D, in_dtype, fwd_rows(in_dtype, true),
+                                  kla::kFwdWaves, kla::kFwdMatrixWords, kla::kFwdStateWords,
+                                  &pl, &empty);
     if (st != KLA_OK || empty) return st;
 
     const void* ins[4] = {k, v, lam_v, q};

@@ -73,6 +73,15 @@ struct BwdArgs {
 
 // Tile shapes (rows per wave, waves per workgroup) and record sizes.
 constexpr int kFwdRows = 28, kFwdWaves = 4, kFwdMatrixWords = 7, kFwdStateWords = 2;
+// bfloat16 rows take half the registers (two rows to a register), so their
+// tiles are sized on their own: 24 rows per wave let the scan run 4 waves per
+// SIMD, and the mixer modes, which need more registers per row, take 36.
+constexpr int kScanRowsBf16 = 24, kMixerRowsBf16 = 36;
+// Rows per wave of the forward kernel for an input type, in the scan and LTI
+// modes or in the mixer modes.
+inline int fwd_rows(kla_dtype dt, bool mixer) {
+    return dt == KLA_DTYPE_F32 ? kFwdRows : mixer ? kMixerRowsBf16 : kScanRowsBf16;
+}
 constexpr int kLtiRows = 64, kLtiWaves = 4;
 constexpr int kMixBwdRows = 8, kMixBwdWaves = 8;
 constexpr int kBwdRows = 14, kBwdWaves = 8, kBwdMatrixWords = 6, kBwdStateWords = 2;

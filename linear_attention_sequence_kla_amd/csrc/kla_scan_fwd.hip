@@ -182,6 +182,49 @@ __device__ inline void token_gates(float x0, float x1, float x2, float x3, doubl
     }
 }
 
+// One token input of a wave's L rows, held in registers across both passes.
+// float32 values are kept as loaded; bfloat16 values stay packed, two rows
+// per register (row 2j in the low half), and widen when read, which halves
+// the registers the rows take.
+template <typename In, int L>
+struct GateRows {
+    float v[L];
+    __device__ void load(int i, const char* base, uint32_t off) {
+        v[i] = __builtin_nontemporal_load(reinterpret_cast<const float*>(base + off));
+    }
+    __device__ void set(int i, float x) { v[i] = x; }
+    __device__ float operator[](int i) const { return v[i]; }
+    // pins the values in registers (see the first pass)
+    __device__ void keep() {
+#pragma unroll
+        for (int i = 0; i < L; ++i) asm volatile("" : "+v"(v[i]));
+    }
+};
+
+template <int L>
+struct GateRows<uint16_t, L> {
+    uint32_t v[(L + 1) / 2];
+    __device__ void put(int i, uint32_t bits) {
+        if (i & 1)
+            v[i >> 1] |= bits << 16;
+        else
+            v[i >> 1] = bits;
+    }
+    __device__ void load(int i, const char* base, uint32_t off) {
+        put(i, __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(base + off)));
+    }
+    // (x exact in bfloat16)
+    __device__ void set(int i, float x) { put(i, __float_as_uint(x) >> 16); }
+    __device__ float operator[](int i) const {
+        const uint32_t x = v[i >> 1];
+        return __uint_as_float((i & 1) ? (x & 0xffff0000u) : (x << 16));
+    }
+    __device__ void keep() {
+#pragma unroll
+        for (int i = 0; i < (L + 1) / 2; ++i) asm volatile("" : "+v"(v[i]));
+    }
+};
+
 template <typename In, int L, int W, Mode M>
 __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(3)))
 void kla_scan_kernel(FwdArgs g) {
@@ -225,28 +268,33 @@ void kla_scan_kernel(FwdArgs g) {
 
         // ---- load the wave's rows; rows past T repeat the last row ----
         // (their values only reach chunk matrices that no valid row uses)
-        float ra[L], rp[L], rf[L], rb[L];
+        GateRows<In, L> ra, rp, rf, rb;
         if (nr > 0) {
 #pragma unroll
             for (int i = 0; i < L; ++i) {
                 const uint32_t off =
                     lm.lane_el * uint32_t(sizeof(In)) + uint32_t(min(i, nr - 1)) * in_row;
                 if constexpr (kAll) {
-                    ra[i] = load_gate<In>(pa, off);
-                    rp[i] = load_gate<In>(pp, off);
-                    rf[i] = load_gate<In>(pf, off);
+                    ra.load(i, pa, off);
+                    rp.load(i, pp, off);
+                    rf.load(i, pf, off);
                 } else {
-                    ra[i] = rp[i] = rf[i] = 0.0f;
+                    ra.set(i, 0.0f);
+                    rp.set(i, 0.0f);
+                    rf.set(i, 0.0f);
                 }
-                rb[i] = kFourth ? load_gate<In>(pb, off) : 0.0f;
+                if constexpr (kFourth)
+                    rb.load(i, pb, off);
+                else
+                    rb.set(i, 0.0f);
             }
         } else {
 #pragma unroll
             for (int i = 0; i < L; ++i) {
-                ra[i] = 1.0f;
-                rp[i] = 0.0f;
-                rf[i] = 0.0f;
-                rb[i] = 0.0f;
+                ra.set(i, 1.0f);
+                rp.set(i, 0.0f);
+                rf.set(i, 0.0f);
+                rb.set(i, 0.0f);
             }
         }
         if (w == 0) tag = read_tag(g.ws);
@@ -281,11 +329,12 @@ void kla_scan_kernel(FwdArgs g) {
         // Keep only the 32-bit gates live across the carry exchange: without
         // this barrier the compiler reuses the float64 conversions of the
         // first pass in the second, doubling the registers a tile needs.
-#pragma unroll
-        for (int i = 0; i < L; ++i) {
-            if constexpr (kAll) asm volatile("" : "+v"(ra[i]), "+v"(rp[i]), "+v"(rf[i]));
-            if constexpr (kFourth) asm volatile("" : "+v"(rb[i]));
+        if constexpr (kAll) {
+            ra.keep();
+            rp.keep();
+            rf.keep();
         }
+        if constexpr (kFourth) rb.keep();
         s_lift[w][0][lane] = m.A;
         s_lift[w][1][lane] = m.B;
         s_lift[w][2][lane] = m.C;
@@ -411,13 +460,13 @@ void kla_scan_kernel(FwdArgs g) {
         advance_epoch(g.ws, tag, (g.n_chunks - 1) * g.G, g.n_tiles, lane);
 }
 
-template <int L, int W, Mode M>
+template <int L32, int L16, int W, Mode M>
 void launch(const FwdArgs& args, kla_dtype dtype, hipStream_t stream) {
     const dim3 grid(unsigned(args.n_tiles)), block(W * kWave);
     if (dtype == KLA_DTYPE_F32)
-        hipLaunchKernelGGL((kla_scan_kernel<float, L, W, M>), grid, block, 0, stream, args);
+        hipLaunchKernelGGL((kla_scan_kernel<float, L32, W, M>), grid, block, 0, stream, args);
     else
-        hipLaunchKernelGGL((kla_scan_kernel<uint16_t, L, W, M>), grid, block, 0, stream, args);
+        hipLaunchKernelGGL((kla_scan_kernel<uint16_t, L16, W, M>), grid, block, 0, stream, args);
 }
 
 }  // namespace
@@ -425,15 +474,15 @@ void launch(const FwdArgs& args, kla_dtype dtype, hipStream_t stream) {
 hipError_t launch_scan_fwd(const FwdArgs& args, kla_dtype dtype, FwdMode mode,
                            hipStream_t stream) {
     if (mode == FwdMode::kScan)
-        launch<kFwdRows, kFwdWaves, Mode::Scan>(args, dtype, stream);
+        launch<kFwdRows, kScanRowsBf16, kFwdWaves, Mode::Scan>(args, dtype, stream);
     else if (mode == FwdMode::kMixer)
-        launch<kFwdRows, kFwdWaves, Mode::Mixer>(args, dtype, stream);
+        launch<kFwdRows, kMixerRowsBf16, kFwdWaves, Mode::Mixer>(args, dtype, stream);
     else if (mode == FwdMode::kMixerTrain)
-        launch<kFwdRows, kFwdWaves, Mode::MixerTrain>(args, dtype, stream);
+        launch<kFwdRows, kMixerRowsBf16, kFwdWaves, Mode::MixerTrain>(args, dtype, stream);
     else if (mode == FwdMode::kMixerState)
-        launch<kFwdRows, kFwdWaves, Mode::MixerState>(args, dtype, stream);
+        launch<kFwdRows, kMixerRowsBf16, kFwdWaves, Mode::MixerState>(args, dtype, stream);
     else
-        launch<kLtiRows, kLtiWaves, Mode::Lti>(args, dtype, stream);
+        launch<kLtiRows, kLtiRows, kLtiWaves, Mode::Lti>(args, dtype, stream);
     return hipGetLastError();
 }
 

@@ -48,9 +48,11 @@ def test_workspace_size(lib):
     assert ws(2 ** 40, 2 ** 40, 1, 1, 0) == 0  # overflow
     small = ws(1, 1, 256, 16, 0)
     assert small > 256 and small % 8 == 0
-    # grows with the number of tiles, same for both dtypes
+    # grows with the number of tiles: bfloat16 tiles are shorter (96 rows
+    # against 112), so the same problem has more of them
     assert ws(8, 16, 2048, 64, 0) > small
-    assert ws(8, 16, 2048, 64, 0) == ws(8, 16, 2048, 64, 1)
+    assert ws(8, 16, 2048, 64, 1) > ws(8, 16, 2048, 64, 0)
+    assert ws(8, 16, 96 * 22, 64, 1) == ws(8, 16, 112 * 22, 64, 0)
 
 
 def _call(lib, a=1, p=1, phi=1, b=1, dtype=0, lam=0x1000000, eta=0x2000000,
@@ -118,11 +120,20 @@ def _mixer_call(lib, k=1, a=0x500000, out=0x1000000, var=0x2000000, lam_T=0, eta
     return st, lib.kla_last_error_detail().decode()
 
 
-def test_mixer_workspace_matches_scan(lib):
+def test_mixer_workspace_size(lib):
+    """float32 mixer tiles equal the scan's (28 rows x 4 waves); bfloat16
+    mixer tiles hold 36 rows per wave against the scan's 24, so a bfloat16
+    mixer over 144 * n rows needs what a bfloat16 scan over 96 * n rows does."""
     for shape in ((1, 1, 256, 16), (8, 16, 2048, 64), (3, 5, 77, 9)):
-        for dt in (0, 1):
-            assert (lib.kla_mixer_fwd_workspace_size(*shape, dt)
-                    == lib.kla_scan_fwd_workspace_size(*shape, dt))
+        assert (lib.kla_mixer_fwd_workspace_size(*shape, 0)
+                == lib.kla_scan_fwd_workspace_size(*shape, 0))
+        assert 0 < lib.kla_mixer_fwd_workspace_size(*shape, 1) <= \
+            lib.kla_scan_fwd_workspace_size(*shape, 1)
+    for n in (1, 7, 30):
+        assert (lib.kla_mixer_fwd_workspace_size(2, 3, 144 * n, 40, 1)
+                == lib.kla_scan_fwd_workspace_size(2, 3, 96 * n, 40, 1))
+    assert lib.kla_mixer_fwd_workspace_size(0, 3, 144, 40, 1) == 0
+    assert lib.kla_mixer_fwd_workspace_size(1, 3, 144, 40, 5) == 0
 
 
 def test_mixer_argument_errors_before_launch(lib):

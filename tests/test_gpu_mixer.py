@@ -120,10 +120,16 @@ def test_mixer_shapes(shape):
     full_parity(g, TOL_F32, "shape %s" % (shape,))
 
 
-def test_mixer_bf16_shape():
-    shape = (2, 2, 700, 48)
-    g = make_mixer_inputs(shape, "bf16", seed=5)
-    g["lam0"], g["eta0"] = make_initial_state(2, 2, 48, random=True, seed=5)
+# bfloat16 mixer tiles hold 36 rows x 4 waves
+BF16_SHAPES = [(2, 2, 700, 48), (1, 2, 144, 64), (2, 1, 145, 33), (1, 1, 35, 7),
+               (2, 3, 1001, 128)]
+
+
+@pytest.mark.parametrize("shape", BF16_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_mixer_bf16_shape(shape):
+    g = make_mixer_inputs(shape, "bf16", seed=5 + sum(shape))
+    g["lam0"], g["eta0"] = make_initial_state(shape[0], shape[1], shape[3], random=True,
+                                              seed=5 + sum(shape))
     full_parity(g, TOL_BF16, "bf16 %s" % (shape,))
 
 

@@ -138,7 +138,8 @@ def test_kla_mixer_autograd():
 
 
 @pytest.mark.parametrize("shape,dtype", [((2, 3, 500, 24), "f32"), ((3, 3, 300, 128), "f32"),
-                                         ((2, 2, 601, 48), "bf16"), ((1, 1, 7, 3), "f32")],
+                                         ((2, 2, 601, 48), "bf16"), ((1, 1, 7, 3), "f32"),
+                                         ((2, 1, 289, 40), "bf16")],
                          ids=lambda x: "x".join(map(str, x)) if isinstance(x, tuple) else x)
 def test_saved_states_equal_recompute(shape, dtype):
     """States kept by kla_mixer_fwd give the backward bitwise the gradients of

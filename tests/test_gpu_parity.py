@@ -144,6 +144,10 @@ SHAPES = [
     (2, 5, 400, 256, "std", "bf16"),     # paired quarter rows, bf16
     (3, 1, 777, 6, "hard", "bf16"),      # bf16, small even D, hard gates
     (2, 3, 250, 2, "slow", "bf16"),      # bf16, D = 2
+    (1, 2, 96, 64, "std", "bf16"),       # exactly one bf16 tile (24 rows x 4 waves)
+    (2, 1, 97, 64, "slow", "bf16"),      # one row into a second bf16 tile
+    (1, 1, 23, 5, "hard", "bf16"),       # bf16, T below one wave's rows (odd)
+    (2, 2, 1153, 70, "std", "bf16"),     # bf16, many tiles, odd rows in the last wave
 ]
 
 

@@ -59,9 +59,9 @@ static void expect(const char* what, int got, int want, int launched, int want_l
     }
 }
 
-// This driver stands in for a C caller, for which a dtype or status argument
+// This program stands in for a C caller, for which a dtype or status argument
 // is a plain int: out-of-range codes are passed through their object
-// representation, so the enum checker is off where the driver handles them.
+// representation, so the enum checker is off where the program handles them.
 #define C_CALLER __attribute__((no_sanitize("enum")))
 C_CALLER static kla_dtype dtype_code(int32_t v) {
     kla_dtype d;

@@ -326,9 +326,10 @@ void kla_scan_kernel(FwdArgs g) {
                 }
             }
         }
-        // Keep only the 32-bit gates live across the carry exchange: without
-        // this barrier the compiler reuses the float64 conversions of the
-        // first pass in the second, doubling the registers a tile needs.
+        // Keep only the loaded gates (float32, or packed bfloat16) live across
+        // the carry exchange: without this barrier the compiler reuses the
+        // float64 conversions of the first pass in the second, doubling the
+        // registers a tile needs.
         if constexpr (kAll) {
             ra.keep();
             rp.keep();

@@ -104,7 +104,8 @@ def test_lti_bf16_and_default_state():
 
 # LTI tiles hold 64 rows x 4 waves; bfloat16 rows are packed two to a register
 @pytest.mark.parametrize("shape", [(1, 2, 256, 64), (2, 1, 257, 33), (1, 1, 63, 5),
-                                   (2, 3, 1001, 128)], ids=lambda s: "x".join(map(str, s)))
+                                   (2, 3, 1001, 128), (2, 2, 1, 9)],
+                         ids=lambda s: "x".join(map(str, s)))
 def test_lti_bf16_tile_boundaries(shape):
     g = make_lti_inputs(shape, "slow", "bf16", seed=sum(shape))
     g["lam0"], g["eta0"] = make_initial_state(shape[0], shape[1], shape[3], random=True,

@@ -122,7 +122,7 @@ def test_mixer_shapes(shape):
 
 # bfloat16 mixer tiles hold 36 rows x 4 waves
 BF16_SHAPES = [(2, 2, 700, 48), (1, 2, 144, 64), (2, 1, 145, 33), (1, 1, 35, 7),
-               (2, 3, 1001, 128)]
+               (2, 3, 1001, 128), (3, 2, 1, 24), (1, 1, 3, 1)]
 
 
 @pytest.mark.parametrize("shape", BF16_SHAPES, ids=lambda s: "x".join(map(str, s)))

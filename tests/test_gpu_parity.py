@@ -148,6 +148,8 @@ SHAPES = [
     (2, 1, 97, 64, "slow", "bf16"),      # one row into a second bf16 tile
     (1, 1, 23, 5, "hard", "bf16"),       # bf16, T below one wave's rows (odd)
     (2, 2, 1153, 70, "std", "bf16"),     # bf16, many tiles, odd rows in the last wave
+    (2, 3, 1, 40, "hard", "bf16"),       # bf16, a single token
+    (1, 1, 2, 1, "std", "bf16"),         # bf16, two tokens, one channel
 ]
 
 

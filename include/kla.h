@@ -264,7 +264,8 @@ KLA_API kla_status kla_scan_lti_fwd(const float *a, const float *p, const float 
  *                   and hands it to kla_mixer_bwd, which then skips its
  *                   recompute of the forward states.
  *   workspace       kla_mixer_fwd_workspace_size bytes, same contract as for
- *                   kla_scan_fwd (one workspace serves both entry points).
+ *                   kla_scan_fwd; one workspace large enough for each call
+ *                   serves both entry points in turn.
  * Errors, stream semantics and the overflow rule as for kla_scan_fwd.
  */
 KLA_API size_t kla_mixer_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int64_t D,

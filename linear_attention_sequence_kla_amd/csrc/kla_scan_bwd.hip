@@ -565,14 +565,37 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void kla_mixer_grad_reduce_ke
     const int64_t n = B * n_chunks;
     double sa = 0.0, sp = 0.0;
     if (hd < HD) {
-#pragma unroll 4
-        for (int64_t j = w; j < n; j += kReduceWaves) {
-            const int64_t b = j / n_chunks, cc = j - b * n_chunks;
-            const int64_t q = b * HD + hd;
-            const int64_t grp = q / kWave, ln = q - grp * kWave;
-            const size_t t = size_t(cc * G + grp);
-            sa += partial[(t * 2) * kWave + ln];
-            sp += partial[(t * 2 + 1) * kWave + ln];
+        // pair j = b * n_chunks + cc; (b, cc) advance with j, so the loop
+        // divides once, and a batch of kBatch pairs' loads is in flight
+        // before the first one is added
+        constexpr int kBatch = 16;
+        int64_t j = w, b = j / n_chunks, cc = j - b * n_chunks;
+        while (j < n) {
+            size_t off[kBatch];
+            bool in[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                in[u] = j < n;
+                const uint64_t q = uint64_t(b * HD + hd);
+                off[u] = size_t(cc * G + int64_t(q / kWave)) * 2 * kWave + size_t(q % kWave);
+                j += kReduceWaves;
+                cc += kReduceWaves;
+                while (cc >= n_chunks) {
+                    cc -= n_chunks;
+                    ++b;
+                }
+            }
+            double va[kBatch], vp[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                va[u] = in[u] ? partial[off[u]] : 0.0;
+                vp[u] = in[u] ? partial[off[u] + kWave] : 0.0;
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                sa += va[u];
+                sp += vp[u];
+            }
         }
     }
     s_sum[w][0][lane] = sa;

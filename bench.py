@@ -252,7 +252,7 @@ def cpu_baseline(w, g_dev, budget_s: float = 10.0):
                     nthreads=1)
         t1 += time.perf_counter() - t0
         reps1 += 1
-    return {"value": elems * reps / t_total, "unit": "elements/s", "cores": used,
+    return {"value": elems * reps / t_total, "unit": "elements/sec", "cores": used,
             "kind": "oracle",
             "sample": "%d of %d slabs (all %d channels, full T=%d), %d runs, %.1f s"
                       % (n_slabs, slabs_total, w.D, w.T, reps, t_total),
@@ -472,9 +472,9 @@ def main(argv=None):
     achieved = n * bpe / (k_avg * 1e-3) / 1e9
     traffic = load_traffic(args.workload, d)
     rec = {
-        "metric": "KLA scan elements (B*H*T*D)/s and achieved HBM GB/s vs peak, 1 MI355X",
+        "metric": "KLA scan elements (B·H·T·D)/sec and achieved HBM GB/s vs peak, 1 MI355X",
         "value": n / (ms_step * 1e-3),
-        "unit": "elements/s",
+        "unit": "elements/sec",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -497,29 +497,29 @@ def main(argv=None):
                             "max": eager_ms[-1], "launches": n_eager},
     }
     if d == "bwd":
-        rec["metric"] = "KLA backward scan elements (B*H*T*D)/s and achieved HBM GB/s vs peak"
+        rec["metric"] = "KLA backward scan elements (B·H·T·D)/sec and achieved HBM GB/s vs peak"
     if d == "lti":
-        rec["metric"] = ("KLA scan with time-invariant gates, elements (B*H*T*D)/s and "
+        rec["metric"] = ("KLA scan with time-invariant gates, elements (B·H·T·D)/sec and "
                          "achieved HBM GB/s vs peak")
     if d == "mixer_bwd":
         rec["roofline"]["scope"] = ("the whole call (state recompute, backward kernel, "
                                     "reduction); traffic is the backward kernel's alone")
-        rec["metric"] = ("KLA fused mixer backward elements (B*H*T*D)/s and achieved HBM GB/s "
+        rec["metric"] = ("KLA fused mixer backward elements (B·H·T·D)/sec and achieved HBM GB/s "
                          "vs peak (the whole call: state recompute, adjoint scan, reduction)")
     if d == "mixer_train":
         rec["roofline"]["scope"] = ("the whole step (mixer forward keeping the states, "
                                     "backward kernel, reduction); traffic is the backward "
                                     "kernel's alone")
         rec["metric"] = ("KLA fused mixer training step (forward + backward) elements "
-                         "(B*H*T*D)/s and achieved HBM GB/s vs peak")
+                         "(B·H·T·D)/sec and achieved HBM GB/s vs peak")
     if d == "mixer":
-        rec["metric"] = ("KLA fused mixer elements (B*H*T*D)/s and achieved HBM GB/s vs peak "
+        rec["metric"] = ("KLA fused mixer elements (B·H·T·D)/sec and achieved HBM GB/s vs peak "
                          "(gates, scan, readout and variance in one pass)")
     if d == "decode":
-        rec["metric"] = "KLA decode step channel updates (B*H*D)/s, one token per step"
+        rec["metric"] = "KLA decode step channel updates (B·H·D)/sec, one token per step"
         rec["config"]["elements"] = n
     if d == "mixer_decode":
-        rec["metric"] = ("KLA fused mixer decode step channel updates (B*H*D)/s, one token "
+        rec["metric"] = ("KLA fused mixer decode step channel updates (B·H·D)/sec, one token "
                          "per step (readout and variance written)")
         rec["config"]["elements"] = n
     if not args.no_cpu_baseline and d == "fwd":

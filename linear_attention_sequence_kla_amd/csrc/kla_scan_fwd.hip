@@ -33,7 +33,7 @@
 //     matrices of the waves before it, then replays its rows sequentially from
 //     on-chip data, writing lam and eta.
 //
-// The kernel has four modes (template parameter Mode):
+// The kernel has five modes (template parameter Mode):
 //   * Scan: the four token inputs are the gates a, p, phi, b; writes lam, eta.
 //   * Mixer: the fused KLA mixer.  The inputs are the token tensors k, v,
 //     lam_v, q and per-channel gates (a, p); phi = k^2 lam_v and b = k lam_v v
@@ -53,8 +53,8 @@
 // Arithmetic is float64 for everything carried (chunk matrices, states): the
 // exact precision can reach 1e88 and the information mean 1e-51 on hard gates,
 // beyond float32's exponent range, and on gfx950 a float64 FMA issues at the
-// same rate as an unpacked float32 FMA.  Inputs are float32 or bfloat16 and
-// outputs float32.
+// same rate as an unpacked float32 FMA.  Inputs are float32 or bfloat16 (held
+// two rows to a register, with tiles sized for that) and outputs float32.
 
 #include "kla_internal.h"
 

@@ -67,7 +67,9 @@ def test_mixer_bwd_workload(key):
 
 
 SHAPES = [(1, 1, 1, 1), (1, 1, 7, 3), (2, 3, 113, 7), (1, 2, 337, 64), (3, 1, 450, 65),
-          (2, 2, 1000, 33), (1, 1, 2049, 128), (3, 3, 300, 128)]
+          (2, 2, 1000, 33), (1, 1, 2049, 128), (3, 3, 300, 128),
+          # a state is kept after every 8th token; a tile holds 64 rows
+          (2, 3, 8, 5), (1, 2, 9, 7), (2, 1, 64, 9), (2, 1, 65, 9), (1, 3, 129, 40)]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))

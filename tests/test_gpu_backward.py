@@ -68,6 +68,10 @@ SHAPES = [
     (1, 1, 2500, 65, "slow", "bf16"),
     (3, 3, 700, 128, "std", "f32"),     # row halves paired per XCD, partial last block
     (2, 5, 300, 256, "slow", "bf16"),
+    (2, 1, 112, 40, "std", "f32"),      # exactly one backward tile (14 rows x 8 waves)
+    (1, 3, 14, 9, "hard", "f32"),       # exactly one wave's rows
+    (2, 2, 15, 3, "std", "bf16"),       # one row into a second wave, bf16
+    (1, 1, 225, 64, "slow", "f32"),     # one row into a third tile
 ]
 
 

@@ -131,9 +131,11 @@ def test_largest_offsets():
 SHAPES = [
     # (B, H, T, D, gates, dtype)
     (1, 1, 1, 1, "std", "f32"),          # a single token, a single channel
-    (1, 1, 127, 1, "std", "f32"),        # T below one tile, D below a wave
-    (1, 1, 128, 64, "std", "f32"),       # exactly one tile
-    (1, 1, 129, 64, "std", "f32"),       # one row into a second tile
+    (1, 1, 111, 1, "std", "f32"),        # T below one tile (28 rows x 4 waves), D below a wave
+    (1, 1, 112, 64, "std", "f32"),       # exactly one tile
+    (1, 1, 113, 64, "std", "f32"),       # one row into a second tile
+    (1, 2, 28, 3, "hard", "f32"),        # exactly one wave's rows
+    (2, 1, 29, 3, "slow", "f32"),        # one row into a second wave
     (2, 3, 1000, 7, "std", "f32"),       # ragged everything
     (3, 2, 517, 100, "slow", "f32"),     # column groups straddle slabs
     (1, 2, 4099, 33, "hard", "f32"),     # long ragged T with hard gates

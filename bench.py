@@ -1,8 +1,11 @@
 """Benchmark of the KLA scan (libkla) on one MI355X.
 
-The headline (default) is the forward scan: a step is one kla_scan_fwd call
-over one batch of synthetic gates, the whole scan (chunk matrices, carry
-look-back, replay and output writes) in a single kernel launch.  --direction
+The headline (default) is the forward scan on the long-context workload
+(B=1, H=32, T=131072, D=128, float32 gates; the largest one): a step is one
+kla_scan_fwd call over one batch of synthetic gates, the whole scan (chunk
+matrices, carry look-back, replay and output writes) in a single kernel
+launch.  The small-LM-layer and 1B-scale-layer workloads are measured the
+same way in the same process and reported under per_config.  --direction
 selects the backward scan, the fused mixer (forward, backward, a training
 step of both, or its decode step), the time-invariant form or the scan's
 decode step instead.  The K timed steps are
@@ -211,6 +214,23 @@ def summarize_counters(args):
     return 0
 
 
+def per_config_entry(m, direction: str) -> dict:
+    """One workload's line of the per-config table: the timed step and the
+    kernel time per launch (HIP events on the launch stream), with the
+    algorithmic bandwidth and its fraction of the HBM peak."""
+    w = m["w"]
+    k_avg = sum(m["kernel_ms"]) / len(m["kernel_ms"])
+    steps = len(m["kernel_ms"])
+    gbs = w.elements * bytes_per_element(w.dtype, direction) / (k_avg * 1e-3) / 1e9
+    return {"workload": w.describe(), "elements": w.elements,
+            "bytes_per_element": bytes_per_element(w.dtype, direction),
+            "ms_per_step": m["wall"] * 1e3 / steps, "kernel_ms_avg": k_avg,
+            "kernel_ms_min": min(m["kernel_ms"]), "achieved_GBps": gbs,
+            "frac": gbs / HBM_PEAK_GBS, "elements_per_sec": w.elements / (k_avg * 1e-3),
+            "eager_launch_ms_median": m["eager_ms"][len(m["eager_ms"]) // 2],
+            "health": m["health"]}
+
+
 def workloads_for(direction: str):
     from kla_inputs import LTI_WORKLOADS, MIXER_WORKLOADS, WORKLOADS
     return {"mixer": MIXER_WORKLOADS, "mixer_bwd": MIXER_WORKLOADS,
@@ -265,8 +285,12 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=1,
-                    help="0..4; the headline is 1 (small-LM layer)")
+    ap.add_argument("--workload", type=int, default=3,
+                    help="0..4; the headline is 3 (long context, the largest)")
+    ap.add_argument("--per-config", type=lambda x: [int(v) for v in x.split(",") if v],
+                    default=[1, 2, 3],
+                    help="forward only: workloads measured the same way after the "
+                         "headline and reported in per_config (comma list; empty: none)")
     ap.add_argument("--sets", type=int, default=2, help="input/output sets to rotate")
     ap.add_argument("--direction",
                     choices=("fwd", "bwd", "decode", "mixer", "mixer_bwd", "mixer_train",
@@ -329,142 +353,151 @@ def main(argv=None):
               % (args.workload, d, ", ".join(map(str, sorted(workloads_for(d))))),
               file=sys.stderr)
         return 2
-    w = workloads_for(d)[args.workload]
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    stream = torch.cuda.current_stream(dev)
-    ws = get_workspace(max(workspace_size(*w.shape, TORCH_DTYPE[w.dtype]),
-                           bwd_workspace_size(*w.shape, TORCH_DTYPE[w.dtype]),
-                           lti_workspace_size(*w.shape, TORCH_DTYPE[w.dtype]),
-                           mixer_bwd_workspace_size(*w.shape, TORCH_DTYPE[w.dtype])), dev, stream)
-    sets = []
-    decoding = d in ("decode", "mixer_decode")
-    for k in range(args.sets if not decoding else 0):
-        make = {"mixer": make_mixer_workload, "mixer_bwd": make_mixer_workload,
-                "mixer_train": make_mixer_workload, "lti": make_lti_workload}.get(d, make_workload)
-        g = make(args.workload, device=dev, seed=w.seed + 1000 * k)
-        lam = torch.empty(w.shape, dtype=torch.float32, device=dev)
-        eta = torch.empty(w.shape, dtype=torch.float32, device=dev)
-        if d == "bwd":
-            # the forward outputs are the saved states; upstream gradients ~ N(0, 1)
-            scan_fwd(g["a"], g["p"], g["phi"], g["b"], g["lam0"], g["eta0"], out=(lam, eta))
-            gen = torch.Generator(device=dev)
-            gen.manual_seed(w.seed + 77 + k)
-            g["g_lam"] = torch.randn(w.shape, generator=gen, device=dev)
-            g["g_eta"] = torch.randn(w.shape, generator=gen, device=dev)
-        if d in ("mixer_bwd", "mixer_train"):
-            # upstream gradients of the readout and the variance ~ N(0, 1)
-            gen = torch.Generator(device=dev)
-            gen.manual_seed(w.seed + 77 + k)
-            g["g_out"] = torch.randn(w.shape, generator=gen, device=dev)
-            g["g_var"] = torch.randn(w.shape, generator=gen, device=dev)
-        if d == "mixer_train":
-            g["states"] = torch.empty(mixer_states_shape(*w.shape), dtype=torch.float64,
-                                      device=dev)
-        sets.append((g, (lam, eta)))
-    if d == "decode":
-        # one token per channel; the state is updated in place each step
-        from kla_inputs import make_gates, make_initial_state
-        for k in range(args.sets):
-            g = make_gates((w.B, w.H, 1, w.D), w.gates, w.dtype, w.seed + 1000 * k, dev)
-            g = {n: v[:, :, 0].contiguous() for n, v in g.items()}
-            sets.append((g, tuple(x.clone() for x in make_initial_state(
-                w.B, w.H, w.D, random=True, seed=k, device=dev))))
-    if d == "mixer_decode":
-        # one mixer token per channel; the state is updated in place each step
-        from kla_inputs import make_initial_state, make_mixer_inputs
-        for k in range(args.sets):
-            g = make_mixer_inputs((w.B, w.H, 1, w.D), w.dtype, w.seed + 1000 * k, dev)
-            g = {n: (v[:, :, 0] if v.dim() == 4 else v).contiguous() for n, v in g.items()}
-            g["out"] = torch.empty((w.B, w.H, w.D), dtype=torch.float32, device=dev)
-            g["var"] = torch.empty((w.B, w.H, w.D), dtype=torch.float32, device=dev)
-            sets.append((g, tuple(x.clone() for x in make_initial_state(
-                w.B, w.H, w.D, random=True, seed=k, device=dev))))
-    grads = None
-    if d == "bwd":
-        grads = tuple(torch.empty(w.shape, dtype=torch.float32, device=dev) for _ in range(4))
-    if d in ("mixer_bwd", "mixer_train"):
-        grads = tuple(torch.empty(w.shape, dtype=torch.float32, device=dev) for _ in range(4)) + \
-            tuple(torch.empty((w.H, w.D), dtype=torch.float32, device=dev) for _ in range(2))
-    torch.cuda.synchronize(dev)
-
-    def step(i):
-        g, out = sets[i % len(sets)]
+    def run_one(key):
+        """Times K launches of direction d on workload `key` (warm-up first);
+        returns the timings and the first input set."""
+        w = workloads_for(d)[key]
+        dev = torch.device("cuda:0")
+        torch.cuda.set_device(dev)
+        stream = torch.cuda.current_stream(dev)
+        ws = get_workspace(max(workspace_size(*w.shape, TORCH_DTYPE[w.dtype]),
+                               bwd_workspace_size(*w.shape, TORCH_DTYPE[w.dtype]),
+                               lti_workspace_size(*w.shape, TORCH_DTYPE[w.dtype]),
+                               mixer_bwd_workspace_size(*w.shape, TORCH_DTYPE[w.dtype])), dev, stream)
+        sets = []
+        decoding = d in ("decode", "mixer_decode")
+        for k in range(args.sets if not decoding else 0):
+            make = {"mixer": make_mixer_workload, "mixer_bwd": make_mixer_workload,
+                    "mixer_train": make_mixer_workload, "lti": make_lti_workload}.get(d, make_workload)
+            g = make(key, device=dev, seed=w.seed + 1000 * k)
+            lam = torch.empty(w.shape, dtype=torch.float32, device=dev)
+            eta = torch.empty(w.shape, dtype=torch.float32, device=dev)
+            if d == "bwd":
+                # the forward outputs are the saved states; upstream gradients ~ N(0, 1)
+                scan_fwd(g["a"], g["p"], g["phi"], g["b"], g["lam0"], g["eta0"], out=(lam, eta))
+                gen = torch.Generator(device=dev)
+                gen.manual_seed(w.seed + 77 + k)
+                g["g_lam"] = torch.randn(w.shape, generator=gen, device=dev)
+                g["g_eta"] = torch.randn(w.shape, generator=gen, device=dev)
+            if d in ("mixer_bwd", "mixer_train"):
+                # upstream gradients of the readout and the variance ~ N(0, 1)
+                gen = torch.Generator(device=dev)
+                gen.manual_seed(w.seed + 77 + k)
+                g["g_out"] = torch.randn(w.shape, generator=gen, device=dev)
+                g["g_var"] = torch.randn(w.shape, generator=gen, device=dev)
+            if d == "mixer_train":
+                g["states"] = torch.empty(mixer_states_shape(*w.shape), dtype=torch.float64,
+                                          device=dev)
+            sets.append((g, (lam, eta)))
         if d == "decode":
-            decode_step(g["a"], g["p"], g["phi"], g["b"], out[0], out[1])
-        elif d == "mixer_decode":
-            mixer_decode_step(g["k"], g["v"], g["lam_v"], g["q"], g["a"], g["p"], out[0], out[1],
-                              out=g["out"], var=g["var"])
-        elif d == "fwd":
-            scan_fwd(g["a"], g["p"], g["phi"], g["b"], g["lam0"], g["eta0"], out=out,
-                     workspace=ws)
-        elif d == "lti":
-            scan_lti_fwd(g["a"], g["p"], g["phi"], g["b"], g["lam0"], g["eta0"], out=out,
+            # one token per channel; the state is updated in place each step
+            from kla_inputs import make_gates, make_initial_state
+            for k in range(args.sets):
+                g = make_gates((w.B, w.H, 1, w.D), w.gates, w.dtype, w.seed + 1000 * k, dev)
+                g = {n: v[:, :, 0].contiguous() for n, v in g.items()}
+                sets.append((g, tuple(x.clone() for x in make_initial_state(
+                    w.B, w.H, w.D, random=True, seed=k, device=dev))))
+        if d == "mixer_decode":
+            # one mixer token per channel; the state is updated in place each step
+            from kla_inputs import make_initial_state, make_mixer_inputs
+            for k in range(args.sets):
+                g = make_mixer_inputs((w.B, w.H, 1, w.D), w.dtype, w.seed + 1000 * k, dev)
+                g = {n: (v[:, :, 0] if v.dim() == 4 else v).contiguous() for n, v in g.items()}
+                g["out"] = torch.empty((w.B, w.H, w.D), dtype=torch.float32, device=dev)
+                g["var"] = torch.empty((w.B, w.H, w.D), dtype=torch.float32, device=dev)
+                sets.append((g, tuple(x.clone() for x in make_initial_state(
+                    w.B, w.H, w.D, random=True, seed=k, device=dev))))
+        grads = None
+        if d == "bwd":
+            grads = tuple(torch.empty(w.shape, dtype=torch.float32, device=dev) for _ in range(4))
+        if d in ("mixer_bwd", "mixer_train"):
+            grads = tuple(torch.empty(w.shape, dtype=torch.float32, device=dev) for _ in range(4)) + \
+                tuple(torch.empty((w.H, w.D), dtype=torch.float32, device=dev) for _ in range(2))
+        torch.cuda.synchronize(dev)
+
+        def step(i):
+            g, out = sets[i % len(sets)]
+            if d == "decode":
+                decode_step(g["a"], g["p"], g["phi"], g["b"], out[0], out[1])
+            elif d == "mixer_decode":
+                mixer_decode_step(g["k"], g["v"], g["lam_v"], g["q"], g["a"], g["p"], out[0], out[1],
+                                  out=g["out"], var=g["var"])
+            elif d == "fwd":
+                scan_fwd(g["a"], g["p"], g["phi"], g["b"], g["lam0"], g["eta0"], out=out,
                          workspace=ws)
-        elif d == "mixer_bwd":
-            mixer_bwd(g["k"], g["v"], g["lam_v"], g["q"], g["a"], g["p"], g["g_out"], g["g_var"],
-                      g["lam0"], g["eta0"], need_state_grads=False, workspace=ws, out=grads)
-        elif d == "mixer":
-            mixer_fwd(g["k"], g["v"], g["lam_v"], g["q"], g["a"], g["p"], g["lam0"], g["eta0"],
-                      out=out[0], var=out[1], workspace=ws)
-        elif d == "mixer_train":
-            mixer_fwd(g["k"], g["v"], g["lam_v"], g["q"], g["a"], g["p"], g["lam0"], g["eta0"],
-                      out=out[0], var=out[1], workspace=ws, states=g["states"])
-            mixer_bwd(g["k"], g["v"], g["lam_v"], g["q"], g["a"], g["p"], g["g_out"], g["g_var"],
-                      g["lam0"], g["eta0"], need_state_grads=False, workspace=ws, out=grads,
-                      states=g["states"])
-        else:
-            scan_bwd(g["a"], g["p"], out[0], out[1], g["g_lam"], g["g_eta"], g["lam0"],
-                     g["eta0"], workspace=ws, out=grads)
+            elif d == "lti":
+                scan_lti_fwd(g["a"], g["p"], g["phi"], g["b"], g["lam0"], g["eta0"], out=out,
+                             workspace=ws)
+            elif d == "mixer_bwd":
+                mixer_bwd(g["k"], g["v"], g["lam_v"], g["q"], g["a"], g["p"], g["g_out"], g["g_var"],
+                          g["lam0"], g["eta0"], need_state_grads=False, workspace=ws, out=grads)
+            elif d == "mixer":
+                mixer_fwd(g["k"], g["v"], g["lam_v"], g["q"], g["a"], g["p"], g["lam0"], g["eta0"],
+                          out=out[0], var=out[1], workspace=ws)
+            elif d == "mixer_train":
+                mixer_fwd(g["k"], g["v"], g["lam_v"], g["q"], g["a"], g["p"], g["lam0"], g["eta0"],
+                          out=out[0], var=out[1], workspace=ws, states=g["states"])
+                mixer_bwd(g["k"], g["v"], g["lam_v"], g["q"], g["a"], g["p"], g["g_out"], g["g_var"],
+                          g["lam0"], g["eta0"], need_state_grads=False, workspace=ws, out=grads,
+                          states=g["states"])
+            else:
+                scan_bwd(g["a"], g["p"], out[0], out[1], g["g_lam"], g["g_eta"], g["lam0"],
+                         g["eta0"], workspace=ws, out=grads)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize(dev)
-
-    if args.graph:
-        # The K timed launches are captured once into a HIP graph and replayed:
-        # the kernels read their epoch from the workspace, so replays need no
-        # host work (and the graph holds no memset).
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for i in range(args.steps):
-                step(i)
-        torch.cuda.synchronize(dev)
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        start.record(stream)
-        graph.replay()
-        end.record(stream)
-        torch.cuda.synchronize(dev)
-        wall = time.perf_counter() - t0
-        kernel_ms = [start.elapsed_time(end) / args.steps] * args.steps
-    else:
-        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-        torch.cuda.synchronize(dev)
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            starts[i].record(stream)
+        for i in range(args.warmup):
             step(i)
-            ends[i].record(stream)
         torch.cuda.synchronize(dev)
-        wall = time.perf_counter() - t0
-        kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    # outside the timed region: the per-launch distribution of eager launches
-    n_eager = min(20, max(1, args.steps))
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(n_eager)]
-    for i, (e0, e1) in enumerate(ev):
-        e0.record(stream)
-        step(i)
-        e1.record(stream)
-    torch.cuda.synchronize(dev)
-    eager_ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
-    health = workspace_health(ws)
-    if health != 0:
-        print("warning: workspace health word %#x" % health, file=sys.stderr)
 
+        if args.graph:
+            # The K timed launches are captured once into a HIP graph and replayed:
+            # the kernels read their epoch from the workspace, so replays need no
+            # host work (and the graph holds no memset).
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for i in range(args.steps):
+                    step(i)
+            torch.cuda.synchronize(dev)
+            start = torch.cuda.Event(enable_timing=True)
+            end = torch.cuda.Event(enable_timing=True)
+            t0 = time.perf_counter()
+            start.record(stream)
+            graph.replay()
+            end.record(stream)
+            torch.cuda.synchronize(dev)
+            wall = time.perf_counter() - t0
+            kernel_ms = [start.elapsed_time(end) / args.steps] * args.steps
+        else:
+            starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+            ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+            torch.cuda.synchronize(dev)
+            t0 = time.perf_counter()
+            for i in range(args.steps):
+                starts[i].record(stream)
+                step(i)
+                ends[i].record(stream)
+            torch.cuda.synchronize(dev)
+            wall = time.perf_counter() - t0
+            kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+        # outside the timed region: the per-launch distribution of eager launches
+        n_eager = min(20, max(1, args.steps))
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n_eager)]
+        for i, (e0, e1) in enumerate(ev):
+            e0.record(stream)
+            step(i)
+            e1.record(stream)
+        torch.cuda.synchronize(dev)
+        eager_ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+        health = workspace_health(ws)
+        if health != 0:
+            print("warning: workspace health word %#x" % health, file=sys.stderr)
+        return {"w": w, "kernel_ms": kernel_ms, "wall": wall, "eager_ms": eager_ms,
+                "n_eager": n_eager, "health": health, "decoding": decoding,
+                "first_set": sets[0][0] if sets else None}
+
+    m = run_one(args.workload)
+    w, kernel_ms, wall, eager_ms = m["w"], m["kernel_ms"], m["wall"], m["eager_ms"]
+    n_eager, health, decoding = m["n_eager"], m["health"], m["decoding"]
     n = w.elements if not decoding else w.channels
     ms_step = wall * 1e3 / args.steps
     k_avg = sum(kernel_ms) / len(kernel_ms)
@@ -522,8 +555,14 @@ def main(argv=None):
         rec["metric"] = ("KLA fused mixer decode step channel updates (B·H·D)/sec, one token "
                          "per step (readout and variance written)")
         rec["config"]["elements"] = n
+    if d == "fwd" and args.per_config:
+        # the other target workloads, each measured the same way in this process
+        rec["per_config"] = [per_config_entry(m, d)]
+        for key in args.per_config:
+            if key != args.workload:
+                rec["per_config"].append(per_config_entry(run_one(key), d))
     if not args.no_cpu_baseline and d == "fwd":
-        rec["cpu_baseline"] = cpu_baseline(w, sets[0][0])
+        rec["cpu_baseline"] = cpu_baseline(w, m["first_set"])
     print(json.dumps(rec), flush=True)
     return 0
 

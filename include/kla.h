@@ -35,6 +35,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <hip/hip_runtime_api.h> /* hipStream_t */
+
 #if defined(__GNUC__) || defined(__clang__)
 #define KLA_API __attribute__((visibility("default")))
 #else
@@ -88,7 +90,7 @@ KLA_API size_t kla_scan_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int6
  *                 zero-filled before its first use; every call leaves it ready
  *                 for the next one, so it is zeroed once, not per call.  Calls
  *                 that run at the same time must use different workspaces.
- *   stream        the hipStream_t to enqueue on (NULL: the null stream).
+ *   stream        the HIP stream to enqueue on (NULL: the null stream).
  *
  * The call validates its arguments on the host and returns an error before
  * enqueueing anything (no partial writes).  On KLA_OK the work is enqueued
@@ -102,7 +104,7 @@ KLA_API kla_status kla_scan_fwd(const void *a, const void *p, const void *phi,
                         float *lam, float *eta,
                         int64_t B, int64_t H, int64_t T, int64_t D,
                         void *workspace, size_t workspace_bytes,
-                        void *stream);
+                        hipStream_t stream);
 
 /*
  * Bytes of device workspace kla_scan_bwd needs (0 for invalid sizes or an
@@ -149,7 +151,7 @@ KLA_API kla_status kla_scan_bwd(const void *a, const void *p, kla_dtype in_dtype
                                 float *g_a, float *g_p, float *g_phi, float *g_b,
                                 float *g_lam0, float *g_eta0,
                                 int64_t B, int64_t H, int64_t T, int64_t D,
-                                void *workspace, size_t workspace_bytes, void *stream);
+                                void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * One decode step: advances a running filter state by one token, in place.
@@ -169,7 +171,7 @@ KLA_API kla_status kla_scan_bwd(const void *a, const void *p, kla_dtype in_dtype
  */
 KLA_API kla_status kla_decode_step(const void *a, const void *p, const void *phi,
                                    const void *b, kla_dtype in_dtype,
-                                   float *lam, float *eta, int64_t n_channels, void *stream);
+                                   float *lam, float *eta, int64_t n_channels, hipStream_t stream);
 
 /*
  * One decode step of the fused mixer: the token step of kla_mixer_fwd for
@@ -195,7 +197,7 @@ KLA_API kla_status kla_mixer_decode_step(const void *k, const void *v, const voi
                                          const void *q, kla_dtype in_dtype,
                                          const float *a, const float *p,
                                          float *lam, float *eta, float *out, float *var,
-                                         int64_t n_channels, int64_t hd, void *stream);
+                                         int64_t n_channels, int64_t hd, hipStream_t stream);
 
 /*
  * Forward KLA scan for time-invariant gates (the linear time-invariant case
@@ -225,7 +227,7 @@ KLA_API kla_status kla_scan_lti_fwd(const float *a, const float *p, const float 
                                     const float *lam0, const float *eta0,
                                     float *lam, float *eta,
                                     int64_t B, int64_t H, int64_t T, int64_t D,
-                                    void *workspace, size_t workspace_bytes, void *stream);
+                                    void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Fused KLA mixer forward: gate production, scan and readout in one pass.
@@ -277,7 +279,7 @@ KLA_API kla_status kla_mixer_fwd(const void *k, const void *v, const void *lam_v
                                  float *out, float *var, float *lam_T, float *eta_T,
                                  double *states,
                                  int64_t B, int64_t H, int64_t T, int64_t D,
-                                 void *workspace, size_t workspace_bytes, void *stream);
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream);
 /* Bytes of kla_mixer_fwd's `states` output (0 for an empty or overflowing
  * problem): 16 bytes per channel per 8 tokens, about 2 bytes per element. */
 KLA_API size_t kla_mixer_states_size(int64_t B, int64_t H, int64_t T, int64_t D);
@@ -325,16 +327,19 @@ KLA_API kla_status kla_mixer_bwd(const void *k, const void *v, const void *lam_v
                                  float *g_k, float *g_v, float *g_lam_v, float *g_q,
                                  float *g_a, float *g_p, float *g_lam0, float *g_eta0,
                                  int64_t B, int64_t H, int64_t T, int64_t D,
-                                 void *workspace, size_t workspace_bytes, void *stream);
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Reads the workspace's health word after the calls that used it have
  * completed (it synchronizes `stream`).  *flags_out is 0 when every call so
  * far ran normally; bit 0 is set if a chunk gave up waiting for the carry of
- * its predecessor (its outputs are then wrong).  The word is cleared by the
- * read.  Returns KLA_ERR_WORKSPACE for a NULL workspace.
+ * its predecessor (the outputs of that call are then wrong).  Every wait is
+ * bounded (about 2^20 polls), so a kernel always terminates; once one wait
+ * of a call gives up, the other waits of the same call give up early, while
+ * later calls wait normally.  The word is cleared by the read.  Returns
+ * KLA_ERR_WORKSPACE for a NULL workspace.
  */
-KLA_API kla_status kla_workspace_health(void *workspace, uint32_t *flags_out, void *stream);
+KLA_API kla_status kla_workspace_health(void *workspace, uint32_t *flags_out, hipStream_t stream);
 
 /* Static text for a status code. */
 KLA_API const char *kla_status_string(kla_status s);

@@ -202,7 +202,7 @@ size_t kla_scan_bwd_workspace_size(int64_t B, int64_t H, int64_t T, int64_t D,
 kla_status kla_scan_fwd(const void* a, const void* p, const void* phi, const void* b,
                         kla_dtype in_dtype, const float* lam0, const float* eta0,
                         float* lam, float* eta, int64_t B, int64_t H, int64_t T, int64_t D,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
     Plan pl;
     bool empty = false;
     kla_status st = common_checks(B, H, T, D, in_dtype, fwd_rows(in_dtype, false),
@@ -252,7 +252,7 @@ kla_status kla_scan_fwd(const void* a, const void* p, const void* phi, const voi
     args.HD = H * D;
     args.ws = kla::workspace_view(workspace, pl.ws);
     const hipError_t err =
-        kla::launch_scan_fwd(args, in_dtype, kla::FwdMode::kScan, static_cast<hipStream_t>(stream));
+        kla::launch_scan_fwd(args, in_dtype, kla::FwdMode::kScan, stream);
     if (err != hipSuccess) return fail(KLA_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
     return KLA_OK;
 }
@@ -270,7 +270,7 @@ size_t kla_scan_lti_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int64_t 
 kla_status kla_scan_lti_fwd(const float* a, const float* p, const float* phi, const void* b,
                             kla_dtype in_dtype, const float* lam0, const float* eta0,
                             float* lam, float* eta, int64_t B, int64_t H, int64_t T, int64_t D,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
     Plan pl;
     bool empty = false;
     kla_status st = common_checks(B, H, T, D, in_dtype, kla::kLtiRows, kla::kLtiWaves,
@@ -321,7 +321,7 @@ kla_status kla_scan_lti_fwd(const float* a, const float* p, const float* phi, co
     args.HD = H * D;
     args.ws = kla::workspace_view(workspace, pl.ws);
     const hipError_t err = kla::launch_scan_fwd(args, in_dtype, kla::FwdMode::kLti,
-                                                static_cast<hipStream_t>(stream));
+                                                stream);
     if (err != hipSuccess) return fail(KLA_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
     return KLA_OK;
 }
@@ -340,7 +340,7 @@ kla_status kla_mixer_bwd(const void* k, const void* v, const void* lam_v, const 
                          const float* g_var, float* g_k,
                          float* g_v, float* g_lam_v, float* g_q, float* g_a, float* g_p,
                          float* g_lam0, float* g_eta0, int64_t B, int64_t H, int64_t T,
-                         int64_t D, void* workspace, size_t workspace_bytes, void* stream) {
+                         int64_t D, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     Plan pl;
     bool empty = false;
     kla_status st = common_checks(B, H, T, D, in_dtype, kla::kMixBwdRows, kla::kMixBwdWaves,
@@ -394,7 +394,7 @@ kla_status kla_mixer_bwd(const void* k, const void* v, const void* lam_v, const 
     if ((st = check_overlaps(bufs, 20)) != KLA_OK) return st;
 
     char* ws = static_cast<char*>(workspace);
-    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipStream_t s = stream;
     hipError_t err = hipSuccess;
     const double* bstate = states;
     if (!bstate) {
@@ -484,7 +484,7 @@ kla_status kla_mixer_fwd(const void* k, const void* v, const void* lam_v, const 
                          kla_dtype in_dtype, const float* a, const float* p, const float* lam0,
                          const float* eta0, float* out, float* var, float* lam_T, float* eta_T,
                          double* states, int64_t B, int64_t H, int64_t T, int64_t D,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
     Plan pl;
     bool empty = false;
     kla_status st = common_checks(B, H, T, D, in_dtype, fwd_rows(in_dtype, true),
@@ -548,7 +548,7 @@ kla_status kla_mixer_fwd(const void* k, const void* v, const void* lam_v, const 
     args.ws = kla::workspace_view(workspace, pl.ws);
     const hipError_t err = kla::launch_scan_fwd(
         args, in_dtype, states ? kla::FwdMode::kMixerTrain : kla::FwdMode::kMixer,
-        static_cast<hipStream_t>(stream));
+        stream);
     if (err != hipSuccess) return fail(KLA_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
     return KLA_OK;
 }
@@ -558,7 +558,7 @@ kla_status kla_scan_bwd(const void* a, const void* p, kla_dtype in_dtype,
                         const float* eta, const float* g_lam, const float* g_eta,
                         float* g_a, float* g_p, float* g_phi, float* g_b, float* g_lam0,
                         float* g_eta0, int64_t B, int64_t H, int64_t T, int64_t D,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
     Plan pl;
     bool empty = false;
     kla_status st = common_checks(B, H, T, D, in_dtype, kla::kBwdRows, kla::kBwdWaves,
@@ -616,14 +616,14 @@ kla_status kla_scan_bwd(const void* a, const void* p, kla_dtype in_dtype,
     args.n_tiles = pl.n_tiles;
     args.ws = kla::workspace_view(workspace, pl.ws);
     const hipError_t err =
-        kla::launch_scan_bwd(args, in_dtype, static_cast<hipStream_t>(stream));
+        kla::launch_scan_bwd(args, in_dtype, stream);
     if (err != hipSuccess) return fail(KLA_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
     return KLA_OK;
 }
 
 kla_status kla_decode_step(const void* a, const void* p, const void* phi, const void* b,
                            kla_dtype in_dtype, float* lam, float* eta, int64_t n_channels,
-                           void* stream) {
+                           hipStream_t stream) {
     t_detail[0] = '\0';
     if (n_channels < 0)
         return fail(KLA_ERR_INVALID_ARG, "negative channel count %lld", (long long)n_channels);
@@ -650,7 +650,7 @@ kla_status kla_decode_step(const void* a, const void* p, const void* phi, const 
     kla_status st = check_overlaps(bufs, 6);
     if (st != KLA_OK) return st;
     const hipError_t err = kla::launch_decode(a, p, phi, b, in_dtype, lam, eta, n_channels,
-                                              static_cast<hipStream_t>(stream));
+                                              stream);
     if (err != hipSuccess) return fail(KLA_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
     return KLA_OK;
 }
@@ -658,7 +658,7 @@ kla_status kla_decode_step(const void* a, const void* p, const void* phi, const 
 kla_status kla_mixer_decode_step(const void* k, const void* v, const void* lam_v, const void* q,
                                  kla_dtype in_dtype, const float* a, const float* p, float* lam,
                                  float* eta, float* out, float* var, int64_t n_channels,
-                                 int64_t hd, void* stream) {
+                                 int64_t hd, hipStream_t stream) {
     t_detail[0] = '\0';
     if (n_channels < 0 || hd < 0)
         return fail(KLA_ERR_INVALID_ARG, "negative size n_channels=%lld hd=%lld",
@@ -698,16 +698,16 @@ kla_status kla_mixer_decode_step(const void* k, const void* v, const void* lam_v
     if (st != KLA_OK) return st;
     const hipError_t err =
         kla::launch_mixer_decode(k, v, lam_v, q, in_dtype, a, p, lam, eta, out, var, n_channels,
-                                 hd, static_cast<hipStream_t>(stream));
+                                 hd, stream);
     if (err != hipSuccess) return fail(KLA_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
     return KLA_OK;
 }
 
-kla_status kla_workspace_health(void* workspace, uint32_t* flags_out, void* stream) {
+kla_status kla_workspace_health(void* workspace, uint32_t* flags_out, hipStream_t stream) {
     t_detail[0] = '\0';
     if (!workspace) return fail(KLA_ERR_WORKSPACE, "workspace is NULL");
     if (!flags_out) return fail(KLA_ERR_INVALID_ARG, "flags_out is NULL");
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStream_t s = stream;
     uint32_t* word = static_cast<uint32_t*>(workspace) + 3;
     uint32_t host = 0;
     hipError_t err = hipMemcpyAsync(&host, word, sizeof(host), hipMemcpyDeviceToHost, s);

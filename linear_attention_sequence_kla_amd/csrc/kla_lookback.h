@@ -11,7 +11,9 @@
 // workgroup already running.
 //
 // Workspace (caller-owned, zero-filled before first use, self-resetting):
-//   [0, 256)        header: u32 reserved[2], u32 epoch, u32 health
+//   [0, 256)        header: u32 reserved, u32 gave_up, u32 epoch, u32 health
+//                   (gave_up: the tag of the last call whose waits gave up;
+//                   health: sticky bit 0, set by any give-up until it is read)
 //   flags           u64 per tile: (tag << 32) | status, tag = epoch + 1
 //   matrix records  per tile: kMatrixWords x 64 float64 (the tile's own map)
 //   state records   per tile: kStateWords x 64 float64 (its inclusive carry)
@@ -120,12 +122,17 @@ __device__ inline void publish(uint64_t* flag, int lane, uint64_t value) {
     if (lane == 0) __hip_atomic_store(flag, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Records health bit 0 and tells whether a wait should give up: after
-// kSpinLimit polls, or as soon as another wait has given up.
-__device__ inline bool give_up(uint32_t spins, uint32_t* header) {
+// Tells whether a wait of the call tagged `tag` should give up: after
+// kSpinLimit polls, or as soon as another wait of the SAME call has given up
+// (header[1] holds the tag of the last call that gave up, so a give-up never
+// shortens the waits of later calls).  A give-up records the call's tag and
+// sets the sticky health bit 0, which stays set until kla_workspace_health
+// reads it.
+__device__ inline bool give_up(uint32_t spins, uint32_t* header, uint32_t tag) {
     if ((spins & 255) != 0) return false;
-    const uint32_t h = __hip_atomic_load(&header[3], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (__builtin_amdgcn_readfirstlane(h) != 0 || spins >= kSpinLimit) {
+    const uint32_t g = __hip_atomic_load(&header[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__builtin_amdgcn_readfirstlane(g) == tag || spins >= kSpinLimit) {
+        __hip_atomic_store(&header[1], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_fetch_or(&header[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return true;
     }
@@ -146,7 +153,7 @@ __device__ inline uint32_t wait_flag(uint64_t* flag, uint32_t tag, uint32_t* hea
             asm volatile("" ::: "memory");
             return lo;
         }
-        if (give_up(spins, header)) return 0;
+        if (give_up(spins, header, tag)) return 0;
         __builtin_amdgcn_s_sleep(1);
     }
 }
@@ -164,7 +171,7 @@ __device__ inline void advance_epoch(const Workspace& ws, uint32_t tag, int64_t 
             const uint64_t v =
                 __hip_atomic_load(&ws.flags[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (v == flag_word(tag, kStatusFinished)) break;
-            if (give_up(spins, ws.header)) break;
+            if (give_up(spins, ws.header, tag)) break;
             __builtin_amdgcn_s_sleep(1);
         }
     }

@@ -17,6 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libkla.so")
 
 KLA_OK = 0
+KLA_ERR_HIP_HEALTH = 4  # reported with the status of a HIP error
 KLA_DTYPE_F32 = 0
 KLA_DTYPE_BF16 = 1
 _DTYPES = {torch.float32: KLA_DTYPE_F32, torch.bfloat16: KLA_DTYPE_BF16}
@@ -99,6 +100,47 @@ def _check(status: int):
                        lib.kla_last_error_detail().decode())
 
 
+class KlaHealthError(KlaError):
+    """A kernel gave up waiting for a predecessor's carry (its outputs are
+    wrong); raised only when health checks are on."""
+
+
+# Health checks: off by default.  When on, every call that uses a workspace
+# is followed by kla_workspace_health on it, which synchronizes the stream
+# and copies 4 bytes to the host (a few microseconds plus the wait for the
+# call to finish, so launches no longer overlap the host); a nonzero word
+# raises KlaHealthError.  A give-up needs a predecessor tile that never
+# publishes its carry for about 2^20 polls, which only a fault elsewhere
+# causes; the kernels still terminate and the word records it either way.
+_health_checks = os.environ.get("KLA_CHECK_HEALTH", "0") not in ("", "0")
+
+
+def set_health_checks(enabled: bool) -> bool:
+    """Turns the per-call health check on or off; returns the previous
+    setting.  The environment variable KLA_CHECK_HEALTH=1 turns it on at
+    import."""
+    global _health_checks
+    prev = _health_checks
+    _health_checks = bool(enabled)
+    return prev
+
+
+def health_checks_enabled() -> bool:
+    return _health_checks
+
+
+def _after_call(name: str, workspace: torch.Tensor):
+    """With health checks on: reads and clears the workspace's health word
+    after the call and raises if a wait gave up."""
+    if not _health_checks:
+        return
+    word = workspace_health(workspace)
+    if word != 0:
+        raise KlaHealthError(KLA_ERR_HIP_HEALTH, name,
+                             "a chunk gave up waiting for its predecessor's carry "
+                             "(health word 0x%x); the outputs of this call are wrong" % word)
+
+
 def workspace_size(B: int, H: int, T: int, D: int, dtype=torch.float32) -> int:
     """Bytes of workspace kla_scan_fwd needs (0 for an empty problem)."""
     return int(library().kla_scan_fwd_workspace_size(B, H, T, D, _DTYPES[dtype]))
@@ -176,6 +218,7 @@ def scan_fwd(a: torch.Tensor, p: torch.Tensor, phi: torch.Tensor, b: torch.Tenso
         _ptr(a), _ptr(p), _ptr(phi), _ptr(b), _DTYPES[a.dtype], _ptr(lam0), _ptr(eta0),
         _ptr(lam), _ptr(eta), B, H, T, D, _ptr(workspace), workspace.numel(),
         ctypes.c_void_p(stream.cuda_stream)))
+    _after_call("kla_scan_fwd", workspace)
     return lam, eta
 
 
@@ -238,6 +281,7 @@ def scan_bwd(a: torch.Tensor, p: torch.Tensor, lam: torch.Tensor, eta: torch.Ten
         _ptr(g_lam), _ptr(g_eta), _ptr(g_a), _ptr(g_p), _ptr(g_phi), _ptr(g_b),
         _ptr(g_lam0), _ptr(g_eta0), B, H, T, D, _ptr(workspace), workspace.numel(),
         ctypes.c_void_p(stream.cuda_stream)))
+    _after_call("kla_scan_bwd", workspace)
     return g_a, g_p, g_phi, g_b, g_lam0, g_eta0
 
 
@@ -316,6 +360,7 @@ def scan_lti_fwd(a: torch.Tensor, p: torch.Tensor, phi: torch.Tensor, b: torch.T
         _ptr(a), _ptr(p), _ptr(phi), _ptr(b), _DTYPES[b.dtype], _ptr(lam0), _ptr(eta0),
         _ptr(lam), _ptr(eta), B, H, T, D, _ptr(workspace), workspace.numel(),
         ctypes.c_void_p(stream.cuda_stream)))
+    _after_call("kla_scan_lti_fwd", workspace)
     return lam, eta
 
 
@@ -379,6 +424,7 @@ def mixer_fwd(k: torch.Tensor, v: torch.Tensor, lam_v: torch.Tensor, q: torch.Te
         _ptr(k), _ptr(v), _ptr(lam_v), _ptr(q), _DTYPES[k.dtype], _ptr(a), _ptr(p), _ptr(lam0),
         _ptr(eta0), _ptr(out), _ptr(var), _ptr(lam_T), _ptr(eta_T), _ptr(states), B, H, T, D,
         _ptr(workspace), workspace.numel(), ctypes.c_void_p(stream.cuda_stream)))
+    _after_call("kla_mixer_fwd", workspace)
     return out, var, lam_T, eta_T
 
 
@@ -466,6 +512,7 @@ def mixer_bwd(k: torch.Tensor, v: torch.Tensor, lam_v: torch.Tensor, q: torch.Te
         _ptr(eta0), _ptr(states), _ptr(g_out), _ptr(g_var), _ptr(g_k), _ptr(g_v), _ptr(g_lam_v), _ptr(g_q),
         _ptr(g_a), _ptr(g_p), _ptr(g_lam0), _ptr(g_eta0), B, H, T, D, _ptr(workspace),
         workspace.numel(), ctypes.c_void_p(stream.cuda_stream)))
+    _after_call("kla_mixer_bwd", workspace)
     return g_k, g_v, g_lam_v, g_q, g_a, g_p, g_lam0, g_eta0
 
 

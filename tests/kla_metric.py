@@ -26,6 +26,11 @@ TINY = 2.0 ** -126
 
 TOL_F32 = 1e-4   # fp32 gate inputs
 TOL_BF16 = 2e-2  # bf16 gate inputs (oracle runs on the same bf16 values)
+# Regression bound of the forward paths, checked next to the bars above: the
+# kernels carry float64 from the very input values the oracle reads, so their
+# only error of note is the final float32 rounding (~6e-8).  A slip that moves
+# a gate by one token or one channel shows up far above it.
+TOL_REGRESSION = 1e-5
 
 
 def _np(x):
@@ -70,6 +75,23 @@ def compare(lam_hat, eta_hat, lam, eta, eta_abs) -> dict:
         rel = np.abs(eta_hat - eta) / np.abs(eta)
         rep["eta_max_rel_noncancel"] = float(rel[plain].max()) if plain.any() else 0.0
     return rep
+
+
+_MAX_KEYS = ("lam_max_rel", "eta_max_scaled", "eta_max_rel_noncancel")
+_SUM_KEYS = ("n", "nan", "range_violations", "lam_overflow", "eta_overflow")
+
+
+def merge_reports(reps) -> dict:
+    """One report for the union of the elements of several reports (counts
+    add, maxima take the largest)."""
+    out = {k: 0 for k in _SUM_KEYS}
+    out.update({k: 0.0 for k in _MAX_KEYS})
+    for r in reps:
+        for k in _SUM_KEYS:
+            out[k] += r[k]
+        for k in _MAX_KEYS:
+            out[k] = max(out[k], r[k])
+    return out
 
 
 def assert_parity(rep: dict, tol: float, what: str = ""):

@@ -95,8 +95,8 @@ KLA_API size_t kla_scan_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int6
  * The call validates its arguments on the host and returns an error before
  * enqueueing anything (no partial writes).  On KLA_OK the work is enqueued
  * and runs asynchronously on `stream`; the caller keeps every buffer alive
- * until it completes.  The library allocates and frees nothing and holds no
- * global state; it is re-entrant and thread-safe.
+ * until it completes.  The call allocates and frees nothing and uses no
+ * library-held state; it is re-entrant and thread-safe.
  */
 KLA_API kla_status kla_scan_fwd(const void *a, const void *p, const void *phi,
                         const void *b, kla_dtype in_dtype,
@@ -105,6 +105,33 @@ KLA_API kla_status kla_scan_fwd(const void *a, const void *p, const void *phi,
                         int64_t B, int64_t H, int64_t T, int64_t D,
                         void *workspace, size_t workspace_bytes,
                         hipStream_t stream);
+
+/*
+ * kla_scan_fwd without a caller-owned workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, results, errors and
+ * stream semantics as kla_scan_fwd, with the same kernels; the workspace is a
+ * device array inside the library, kla_scan_fwd_noalloc_max_workspace()
+ * bytes (32 MiB) per GPU, which each GPU holds from its first call until the
+ * process ends (its address is resolved once per device on that device's
+ * first call, with that device current).  The call itself allocates and
+ * frees nothing and clears nothing: the array starts zero-filled and every
+ * call leaves it ready for the next one.
+ *
+ * Limit: a problem whose kla_scan_fwd_workspace_size exceeds the array is
+ * rejected with KLA_ERR_WORKSPACE before anything is enqueued (about 7,000
+ * tiles of 64 channels by 112 float32 rows, e.g. 52M float32 elements at
+ * D = 64).  All calls on one GPU share its array: calls that may overlap in
+ * time on one GPU (different streams or threads) race and must be serialised
+ * by the caller.
+ */
+KLA_API size_t kla_scan_fwd_noalloc_max_workspace(void);
+KLA_API kla_status kla_scan_fwd_noalloc(const void *a, const void *p, const void *phi,
+                                        const void *b, kla_dtype in_dtype,
+                                        const float *lam0, const float *eta0,
+                                        float *lam, float *eta,
+                                        int64_t B, int64_t H, int64_t T, int64_t D,
+                                        hipStream_t stream);
 
 /*
  * Bytes of device workspace kla_scan_bwd needs (0 for invalid sizes or an

@@ -15,7 +15,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = [os.path.join(HERE, "csrc", f)
-           for f in ("kla_api.cpp", "kla_scan_fwd.hip", "kla_scan_bwd.hip", "kla_decode.hip")]
+           for f in ("kla_api.cpp", "kla_scan_fwd.hip", "kla_scan_bwd.hip", "kla_decode.hip",
+                     "kla_noalloc.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "libkla.so")
 DEBUG_LIBRARY = os.path.join(HERE, "libkla_debug.so")

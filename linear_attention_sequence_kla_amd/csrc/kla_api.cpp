@@ -47,15 +47,10 @@ bool make_plan(int64_t B, int64_t H, int64_t T, int64_t D, int rows_per_wave, in
     return true;
 }
 
-}  // namespace kla
-
 namespace {
-
-using kla::Plan;
-
 thread_local char t_detail[512];
+}  // namespace
 
-kla_status fail(kla_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 kla_status fail(kla_status s, const char* fmt, ...) {
     va_list ap;
     va_start(ap, fmt);
@@ -63,6 +58,14 @@ kla_status fail(kla_status s, const char* fmt, ...) {
     va_end(ap);
     return s;
 }
+
+}  // namespace kla
+
+namespace {
+
+using kla::Plan;
+using kla::fail;
+using kla::t_detail;
 
 bool overlaps(const void* x, size_t nx, const void* y, size_t ny) {
     if (!x || !y || nx == 0 || ny == 0) return false;

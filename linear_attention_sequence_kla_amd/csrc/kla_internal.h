@@ -25,6 +25,10 @@ struct Plan {
     WorkspaceLayout ws;
 };
 
+// Records the calling thread's error text (kla_last_error_detail) and
+// returns `s`.
+kla_status fail(kla_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
 // Returns false on negative or overflowing sizes.
 bool make_plan(int64_t B, int64_t H, int64_t T, int64_t D, int rows_per_wave,
                int waves, int matrix_words, int state_words, Plan* pl);

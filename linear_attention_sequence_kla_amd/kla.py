@@ -58,6 +58,11 @@ def load_library(path: str) -> ctypes.CDLL:
     lib.kla_scan_fwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, vp,
                                  i64, i64, i64, i64, vp, sz, vp]
     lib.kla_scan_fwd.restype = ctypes.c_int
+    lib.kla_scan_fwd_noalloc.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, vp,
+                                         i64, i64, i64, i64, vp]
+    lib.kla_scan_fwd_noalloc.restype = ctypes.c_int
+    lib.kla_scan_fwd_noalloc_max_workspace.argtypes = []
+    lib.kla_scan_fwd_noalloc_max_workspace.restype = sz
     lib.kla_scan_bwd_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int]
     lib.kla_scan_bwd_workspace_size.restype = sz
     lib.kla_scan_bwd.argtypes = [vp, vp, ctypes.c_int] + [vp] * 12 + [i64] * 4 + [vp, sz, vp]
@@ -219,6 +224,40 @@ def scan_fwd(a: torch.Tensor, p: torch.Tensor, phi: torch.Tensor, b: torch.Tenso
         _ptr(lam), _ptr(eta), B, H, T, D, _ptr(workspace), workspace.numel(),
         ctypes.c_void_p(stream.cuda_stream)))
     _after_call("kla_scan_fwd", workspace)
+    return lam, eta
+
+
+def scan_fwd_noalloc(a: torch.Tensor, p: torch.Tensor, phi: torch.Tensor, b: torch.Tensor,
+                     lam0: torch.Tensor | None = None, eta0: torch.Tensor | None = None,
+                     out: tuple | None = None):
+    """kla_scan_fwd_noalloc on the current stream: the forward scan with the
+    library's own per-GPU workspace (no workspace argument; calls that overlap
+    on one GPU race).  Arguments and results as for ``scan_fwd``; with ``out``
+    given nothing is allocated at all."""
+    if a.dim() != 4:
+        raise ValueError("gates must be [B, H, T, D], got shape %s" % (tuple(a.shape),))
+    for name, t in zip(("a", "p", "phi", "b"), (a, p, phi, b)):
+        if t.shape != a.shape or t.dtype != a.dtype:
+            raise ValueError("%s must match a in shape and dtype" % name)
+        if not t.is_cuda or t.device != a.device or not t.is_contiguous():
+            raise ValueError("%s must be contiguous on a's GPU" % name)
+    if a.dtype not in _DTYPES:
+        raise ValueError("gate dtype must be float32 or bfloat16, got %s" % a.dtype)
+    B, H, T, D = a.shape
+    for name, t in (("lam0", lam0), ("eta0", eta0)):
+        _check_f32(name, t, (B, H, D), a.device)
+    if out is None:
+        out = (torch.empty(a.shape, dtype=torch.float32, device=a.device),
+               torch.empty(a.shape, dtype=torch.float32, device=a.device))
+    lam, eta = out
+    for name, t in (("lam", lam), ("eta", eta)):
+        if t is None:
+            raise ValueError("%s output is required" % name)
+        _check_f32(name, t, a.shape, a.device)
+    stream = torch.cuda.current_stream(a.device)
+    _check(library().kla_scan_fwd_noalloc(
+        _ptr(a), _ptr(p), _ptr(phi), _ptr(b), _DTYPES[a.dtype], _ptr(lam0), _ptr(eta0),
+        _ptr(lam), _ptr(eta), B, H, T, D, ctypes.c_void_p(stream.cuda_stream)))
     return lam, eta
 
 

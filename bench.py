@@ -43,19 +43,25 @@ KERNEL_SOURCES = {"fwd": ("kla_scan_fwd.hip", "kla_lookback.h", "kla_internal.h"
                   "mixer": ("kla_scan_fwd.hip", "kla_lookback.h", "kla_internal.h"),
                   "lti": ("kla_scan_fwd.hip", "kla_lookback.h", "kla_internal.h"),
                   "mixer_bwd": ("kla_scan_bwd.hip", "kla_lookback.h", "kla_internal.h"),
+                  "bwd_states": ("kla_scan_bwd.hip", "kla_lookback.h", "kla_internal.h"),
+                  "scan_train": ("kla_scan_bwd.hip", "kla_lookback.h", "kla_internal.h"),
                   "mixer_train": ("kla_scan_bwd.hip", "kla_lookback.h", "kla_internal.h")}
 KERNEL_NAMES = {"fwd": "kla_scan_kernel", "bwd": "kla_scan_bwd_kernel",
                 "decode": "kla_decode_kernel", "mixer_decode": "kla_mixer_decode_kernel",
                 "mixer": "kla_scan_kernel",
-                "lti": "kla_scan_kernel", "mixer_bwd": "kla_mixer_bwd_kernel",
-                "mixer_train": "kla_mixer_bwd_kernel"}
+                "lti": "kla_scan_kernel", "mixer_bwd": "kla_state_bwd_kernel",
+                "mixer_train": "kla_state_bwd_kernel", "bwd_states": "kla_state_bwd_kernel",
+                "scan_train": "kla_state_bwd_kernel"}
 # the forward kernel template's last parameter is its mode (scan, mixer, LTI)
-KERNEL_SUFFIX = {"fwd": "Mode)0>", "mixer": "Mode)1>", "lti": "Mode)2>"}
+KERNEL_SUFFIX = {"fwd": "Mode)0>", "mixer": "Mode)1>", "lti": "Mode)2>",
+                 "mixer_bwd": "StateBwdMode)0>", "mixer_train": "StateBwdMode)0>",
+                 "bwd_states": "StateBwdMode)1>", "scan_train": "StateBwdMode)1>"}
 PROFILE_NAMES = {"fwd": "kla_scan_kernel", "bwd": "kla_scan_bwd_kernel",
                  "decode": "kla_decode_kernel", "mixer_decode": "kla_mixer_decode_kernel",
                  "mixer": "kla_scan_kernel_mixer",
-                 "lti": "kla_scan_kernel_lti", "mixer_bwd": "kla_mixer_bwd_kernel",
-                 "mixer_train": "kla_mixer_bwd_kernel"}
+                 "lti": "kla_scan_kernel_lti", "mixer_bwd": "kla_state_bwd_kernel_mixer",
+                 "mixer_train": "kla_state_bwd_kernel_mixer",
+                 "bwd_states": "kla_state_bwd_kernel_scan", "scan_train": "kla_state_bwd_kernel_scan"}
 
 
 def is_kernel(name: str, direction: str) -> bool:
@@ -103,6 +109,10 @@ def bytes_per_element(dtype: str, direction: str = "fwd") -> int:
     if direction == "mixer_train":  # forward keeping the boundary states, then the backward
         # from them (no recompute)
         return 4 * gate + 2 * 4 + 2 + kernel_bytes_per_element(dtype, "mixer_bwd")
+    if direction == "bwd_states":  # the backward kernel from kept states
+        return kernel_bytes_per_element(dtype, "bwd_states")
+    if direction == "scan_train":  # forward keeping the states, then the backward from them
+        return 4 * gate + 2 * 4 + 2 + kernel_bytes_per_element(dtype, "bwd_states")
     return 2 * gate + 4 * 4 + 4 * 4
 
 
@@ -111,7 +121,10 @@ def kernel_bytes_per_element(dtype: str, direction: str = "fwd") -> int:
     mixer_bwd that is the backward kernel alone: k, v, lam_v, q, the float64
     boundary state (16 bytes per 8 rows) and the upstream g_out, g_var read;
     g_k, g_v, g_lam_v, g_q written."""
-    if direction in ("mixer_bwd", "mixer_train"):
+    if direction in ("mixer_bwd", "mixer_train", "bwd_states", "scan_train"):
+        # mixer: k, v, lam_v, q, the states, g_out, g_var read; g_k, g_v,
+        # g_lam_v, g_q written.  scan: a, p, phi, b, the states, g_lam, g_eta
+        # read; g_a, g_p, g_phi, g_b written.
         gate = 4 if dtype == "f32" else 2
         return 4 * gate + 2 + 2 * 4 + 4 * 4
     return bytes_per_element(dtype, direction)
@@ -119,7 +132,7 @@ def kernel_bytes_per_element(dtype: str, direction: str = "fwd") -> int:
 
 def traffic_path(workload_key: int, direction: str) -> str:
     # a training step's dominant kernel is the mixer backward kernel
-    direction = {"mixer_train": "mixer_bwd"}.get(direction, direction)
+    direction = {"mixer_train": "mixer_bwd", "scan_train": "bwd_states"}.get(direction, direction)
     suffix = {"fwd": "", "bwd": "_bwd"}.get(direction, "_" + direction)
     return os.path.join(ROOT, "profiles", "traffic_workload%d%s.json" % (workload_key, suffix))
 
@@ -293,10 +306,13 @@ def main(argv=None):
                          "headline and reported in per_config (comma list; empty: none)")
     ap.add_argument("--sets", type=int, default=2, help="input/output sets to rotate")
     ap.add_argument("--direction",
-                    choices=("fwd", "bwd", "decode", "mixer", "mixer_bwd", "mixer_train",
-                             "mixer_decode", "lti"),
+                    choices=("fwd", "bwd", "bwd_states", "scan_train", "decode", "mixer",
+                             "mixer_bwd", "mixer_train", "mixer_decode", "lti"),
                     default="fwd",
-                    help="fwd: kla_scan_fwd (the headline); bwd: kla_scan_bwd; decode: "
+                    help="fwd: kla_scan_fwd (the headline); bwd: kla_scan_bwd; bwd_states: "
+                         "kla_scan_bwd_states from the states kla_scan_fwd_states kept; "
+                         "scan_train: kla_scan_fwd_states then kla_scan_bwd_states (one "
+                         "training step of the scan); decode: "
                          "kla_decode_step on one token of every channel of the workload; "
                          "mixer: kla_mixer_fwd on the mixer workload of the same key; "
                          "mixer_bwd: kla_mixer_bwd on the mixer workload; "
@@ -345,7 +361,8 @@ def main(argv=None):
     from linear_attention_sequence_kla_amd import (
         bwd_workspace_size, decode_step, get_workspace, lti_workspace_size, mixer_bwd,
         mixer_bwd_workspace_size, mixer_decode_step, mixer_fwd, mixer_states_shape, scan_bwd,
-        scan_fwd, scan_lti_fwd, workspace_health, workspace_size)
+        scan_fwd, scan_lti_fwd, workspace_health, workspace_size, bwd_states_workspace_size,
+        scan_bwd_states, scan_fwd_states, scan_states_shape)
 
     d = args.direction
     if args.workload not in workloads_for(d):
@@ -362,6 +379,7 @@ def main(argv=None):
         stream = torch.cuda.current_stream(dev)
         ws = get_workspace(max(workspace_size(*w.shape, TORCH_DTYPE[w.dtype]),
                                bwd_workspace_size(*w.shape, TORCH_DTYPE[w.dtype]),
+                               bwd_states_workspace_size(*w.shape, TORCH_DTYPE[w.dtype]),
                                lti_workspace_size(*w.shape, TORCH_DTYPE[w.dtype]),
                                mixer_bwd_workspace_size(*w.shape, TORCH_DTYPE[w.dtype])), dev, stream)
         sets = []
@@ -372,7 +390,12 @@ def main(argv=None):
             g = make(key, device=dev, seed=w.seed + 1000 * k)
             lam = torch.empty(w.shape, dtype=torch.float32, device=dev)
             eta = torch.empty(w.shape, dtype=torch.float32, device=dev)
-            if d == "bwd":
+            if d in ("bwd_states", "scan_train"):
+                g["states"] = torch.empty(scan_states_shape(*w.shape), dtype=torch.float64,
+                                          device=dev)
+                scan_fwd_states(g["a"], g["p"], g["phi"], g["b"], g["lam0"], g["eta0"],
+                                states=g["states"], out=(lam, eta))
+            if d in ("bwd", "bwd_states", "scan_train"):
                 # the forward outputs are the saved states; upstream gradients ~ N(0, 1)
                 scan_fwd(g["a"], g["p"], g["phi"], g["b"], g["lam0"], g["eta0"], out=(lam, eta))
                 gen = torch.Generator(device=dev)
@@ -408,7 +431,7 @@ def main(argv=None):
                 sets.append((g, tuple(x.clone() for x in make_initial_state(
                     w.B, w.H, w.D, random=True, seed=k, device=dev))))
         grads = None
-        if d == "bwd":
+        if d in ("bwd", "bwd_states", "scan_train"):
             grads = tuple(torch.empty(w.shape, dtype=torch.float32, device=dev) for _ in range(4))
         if d in ("mixer_bwd", "mixer_train"):
             grads = tuple(torch.empty(w.shape, dtype=torch.float32, device=dev) for _ in range(4)) + \
@@ -431,6 +454,16 @@ def main(argv=None):
             elif d == "mixer_bwd":
                 mixer_bwd(g["k"], g["v"], g["lam_v"], g["q"], g["a"], g["p"], g["g_out"], g["g_var"],
                           g["lam0"], g["eta0"], need_state_grads=False, workspace=ws, out=grads)
+            elif d == "bwd_states":
+                scan_bwd_states(g["a"], g["p"], g["phi"], g["b"], g["g_lam"], g["g_eta"],
+                                g["lam0"], g["eta0"], states=g["states"], need_state_grads=False,
+                                workspace=ws, out=grads)
+            elif d == "scan_train":
+                scan_fwd_states(g["a"], g["p"], g["phi"], g["b"], g["lam0"], g["eta0"],
+                                states=g["states"], out=out, workspace=ws)
+                scan_bwd_states(g["a"], g["p"], g["phi"], g["b"], g["g_lam"], g["g_eta"],
+                                g["lam0"], g["eta0"], states=g["states"], need_state_grads=False,
+                                workspace=ws, out=grads)
             elif d == "mixer":
                 mixer_fwd(g["k"], g["v"], g["lam_v"], g["q"], g["a"], g["p"], g["lam0"], g["eta0"],
                           out=out[0], var=out[1], workspace=ws)
@@ -531,6 +564,14 @@ def main(argv=None):
     }
     if d == "bwd":
         rec["metric"] = "KLA backward scan elements (B·H·T·D)/sec and achieved HBM GB/s vs peak"
+    if d == "bwd_states":
+        rec["metric"] = ("KLA backward scan from float64 states, elements (B·H·T·D)/sec and "
+                         "achieved HBM GB/s vs peak")
+    if d == "scan_train":
+        rec["roofline"]["scope"] = ("the whole step (forward keeping the states, backward "
+                                    "from them); traffic is the backward kernel's alone")
+        rec["metric"] = ("KLA scan training step (forward keeping states + backward) elements "
+                         "(B·H·T·D)/sec and achieved HBM GB/s vs peak")
     if d == "lti":
         rec["metric"] = ("KLA scan with time-invariant gates, elements (B·H·T·D)/sec and "
                          "achieved HBM GB/s vs peak")

@@ -164,7 +164,8 @@ KLA_API size_t kla_scan_bwd_workspace_size(int64_t B, int64_t H, int64_t T, int6
  *   lam, eta      the forward call's outputs, [B,H,T,D] float32: they are the
  *                 states lam_{t-1}, eta_{t-1} of the derivatives, so they must
  *                 be finite (where the forward outputs overflowed float32 the
- *                 gradients are unspecified).
+ *                 gradients are unspecified; kla_scan_bwd_states below has
+ *                 no such limit).
  *   g_lam, g_eta  upstream gradients, [B,H,T,D] float32; NULL means zero.
  *   g_a, g_p, g_phi, g_b   outputs, [B,H,T,D] float32 (also for bf16 gates).
  *   g_lam0, g_eta0         outputs, [B,H,D] float32; either may be NULL.
@@ -179,6 +180,64 @@ KLA_API kla_status kla_scan_bwd(const void *a, const void *p, kla_dtype in_dtype
                                 float *g_lam0, float *g_eta0,
                                 int64_t B, int64_t H, int64_t T, int64_t D,
                                 void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The backward pass from float64 states: the vector-Jacobian product of
+ * kla_scan_fwd (the same gradients as kla_scan_bwd), defined wherever the
+ * forward recursion is, also where lam or eta leave float32's range.
+ *
+ * kla_scan_bwd takes its states lam_{t-1}, eta_{t-1} from the forward
+ * outputs, which are float32: where those overflow (lam reaches 1e88 on
+ * hard gates) its gradients are unspecified.  These entry points keep the
+ * states in float64 instead: the forward call writes the state (lam, eta)
+ * of every channel after every 8th token, and the backward kernel replays
+ * each 8-token block from the state before it in float64.
+ *
+ * kla_scan_states_size: bytes of the `states` buffer, 16 per channel per 8
+ * tokens ([ceil(T / 8)][B * H * D][2] float64), about 2 bytes per element;
+ * 0 for an empty or overflowing problem.
+ *
+ * kla_scan_fwd_states: kla_scan_fwd (same arguments, outputs, workspace
+ * and errors) that also writes `states` (device pointer, 16-byte aligned,
+ * kla_scan_states_size bytes, not overlapping any other argument).
+ *
+ * kla_scan_bwd_states: the gradients of a scalar loss with respect to a, p,
+ * phi, b (per token) and lam0, eta0, given the upstream gradients g_lam,
+ * g_eta of the forward outputs (formulas as for kla_scan_bwd).
+ *   a, p, phi, b, lam0, eta0  the forward call's inputs.
+ *   states         kla_scan_fwd_states' `states` for these inputs, or NULL:
+ *                  the call then first recomputes them into the workspace
+ *                  (one more pass over the gates).  Read only.
+ *   g_lam, g_eta   [B, H, T, D] float32; NULL means zero.
+ *   g_a, g_p, g_phi, g_b   [B, H, T, D] float32 outputs.
+ *   g_lam0, g_eta0         [B, H, D] float32 outputs; either may be NULL.
+ *   workspace      kla_scan_bwd_states_workspace_size bytes (it holds the
+ *                  recomputed states), zero-filled once before first use as
+ *                  for kla_scan_fwd; it may serve the other entry points in
+ *                  turn.
+ * Outputs must not overlap any other argument.  Errors, stream semantics and
+ * the overflow rule as for kla_scan_fwd.
+ */
+KLA_API size_t kla_scan_states_size(int64_t B, int64_t H, int64_t T, int64_t D);
+KLA_API kla_status kla_scan_fwd_states(const void *a, const void *p, const void *phi,
+                                       const void *b, kla_dtype in_dtype,
+                                       const float *lam0, const float *eta0,
+                                       float *lam, float *eta, double *states,
+                                       int64_t B, int64_t H, int64_t T, int64_t D,
+                                       void *workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
+KLA_API size_t kla_scan_bwd_states_workspace_size(int64_t B, int64_t H, int64_t T, int64_t D,
+                                                  kla_dtype in_dtype);
+KLA_API kla_status kla_scan_bwd_states(const void *a, const void *p, const void *phi,
+                                       const void *b, kla_dtype in_dtype,
+                                       const float *lam0, const float *eta0,
+                                       const double *states,
+                                       const float *g_lam, const float *g_eta,
+                                       float *g_a, float *g_p, float *g_phi, float *g_b,
+                                       float *g_lam0, float *g_eta0,
+                                       int64_t B, int64_t H, int64_t T, int64_t D,
+                                       void *workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
 
 /*
  * One decode step: advances a running filter state by one token, in place.

@@ -11,4 +11,5 @@ from .kla import (  # noqa: F401
     get_workspace, health_checks_enabled, set_health_checks,
     kla_mixer, kla_scan, library, lti_workspace_size, mixer_bwd, mixer_bwd_workspace_size,
     mixer_decode_step, mixer_fwd, mixer_states_shape, mixer_workspace_size, scan_bwd, scan_fwd,
-    scan_fwd_noalloc, scan_lti_fwd, workspace_health, workspace_size)
+    scan_fwd_noalloc, scan_lti_fwd, workspace_health, workspace_size, scan_fwd_states,
+    scan_bwd_states, scan_states_shape, bwd_states_workspace_size)

@@ -178,6 +178,84 @@ bool mixer_bwd_layout(int64_t B, int64_t H, int64_t T, int64_t D, const kla_dtyp
     return true;
 }
 
+// Workspace of kla_scan_bwd_states: the look-back region (shared in turn by
+// the forward recompute and the backward kernel) and the recomputed float64
+// states after every kMixBwdRows-th row.
+bool scan_bwd_states_layout(int64_t B, int64_t H, int64_t T, int64_t D, const kla_dtype& dt,
+                            MixerBwdLayout* l) {
+    if (!kla::make_plan(B, H, T, D, fwd_rows(dt, false), kla::kFwdWaves, kla::kFwdMatrixWords,
+                        kla::kFwdStateWords, &l->fwd) ||
+        !kla::make_plan(B, H, T, D, kla::kMixBwdRows, kla::kMixBwdWaves, kla::kBwdMatrixWords,
+                        kla::kBwdStateWords, &l->bwd))
+        return false;
+    l->off_bstate = align256(l->fwd.ws.bytes > l->bwd.ws.bytes ? l->fwd.ws.bytes : l->bwd.ws.bytes);
+    l->off_partial = l->off_bstate + align256(mixer_states_bytes(l->fwd, T));
+    l->bytes = l->off_partial;
+    return true;
+}
+
+kla_status scan_fwd_impl(const void* a, const void* p, const void* phi, const void* b,
+                         const kla_dtype& in_dtype, const float* lam0, const float* eta0,
+                         float* lam, float* eta, double* states, int64_t B, int64_t H, int64_t T,
+                         int64_t D, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    Plan pl;
+    bool empty = false;
+    kla_status st = common_checks(B, H, T, D, in_dtype, fwd_rows(in_dtype, false),
+                                  kla::kFwdWaves, kla::kFwdMatrixWords, kla::kFwdStateWords,
+                                  &pl, &empty);
+    if (st != KLA_OK || empty) return st;
+
+    const void* ins[4] = {a, p, phi, b};
+    const char* names[4] = {"a", "p", "phi", "b"};
+    const size_t esz = in_dtype == KLA_DTYPE_F32 ? 4 : 2;
+    for (int i = 0; i < 4; ++i) {
+        if (!ins[i]) return fail(KLA_ERR_INVALID_ARG, "%s is NULL", names[i]);
+        if (misaligned(ins[i], esz))
+            return fail(KLA_ERR_UNSUPPORTED, "%s is not %zu-byte aligned", names[i], esz);
+    }
+    if (!lam || !eta) return fail(KLA_ERR_INVALID_ARG, "%s is NULL", lam ? "eta" : "lam");
+    if (misaligned(lam, 4) || misaligned(eta, 4))
+        return fail(KLA_ERR_UNSUPPORTED, "outputs must be 4-byte aligned");
+    if ((lam0 && misaligned(lam0, 4)) || (eta0 && misaligned(eta0, 4)))
+        return fail(KLA_ERR_UNSUPPORTED, "lam0/eta0 must be 4-byte aligned");
+    if (states && misaligned(states, 16))
+        return fail(KLA_ERR_UNSUPPORTED, "states is not 16-byte aligned");
+    if ((st = check_workspace(workspace, workspace_bytes, pl)) != KLA_OK) return st;
+
+    const size_t in_bytes = size_t(pl.N) * esz, out_bytes = size_t(pl.N) * 4;
+    const size_t st_bytes = size_t(pl.C) * 4;
+    const Buffer bufs[10] = {{a, in_bytes, "a", false},           {p, in_bytes, "p", false},
+                             {phi, in_bytes, "phi", false},       {b, in_bytes, "b", false},
+                             {lam0, st_bytes, "lam0", false},     {eta0, st_bytes, "eta0", false},
+                             {lam, out_bytes, "lam", true},       {eta, out_bytes, "eta", true},
+                             {workspace, pl.ws.bytes, "workspace", true},
+                             {states, mixer_states_bytes(pl, T), "states", true}};
+    if ((st = check_overlaps(bufs, 10)) != KLA_OK) return st;
+
+    kla::FwdArgs args = {};
+    args.in[0] = a;
+    args.in[1] = p;
+    args.in[2] = phi;
+    args.in[3] = b;
+    args.lam0 = lam0;
+    args.eta0 = eta0;
+    args.lam = lam;
+    args.eta = eta;
+    args.T = T;
+    args.D = D;
+    args.C = pl.C;
+    args.G = pl.G;
+    args.n_chunks = pl.n_chunks;
+    args.n_tiles = pl.n_tiles;
+    args.HD = H * D;
+    args.bstate = states;
+    args.ws = kla::workspace_view(workspace, pl.ws);
+    const hipError_t err = kla::launch_scan_fwd(
+        args, in_dtype, states ? kla::FwdMode::kScanTrain : kla::FwdMode::kScan, stream);
+    if (err != hipSuccess) return fail(KLA_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
+    return KLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -206,58 +284,24 @@ kla_status kla_scan_fwd(const void* a, const void* p, const void* phi, const voi
                         kla_dtype in_dtype, const float* lam0, const float* eta0,
                         float* lam, float* eta, int64_t B, int64_t H, int64_t T, int64_t D,
                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    Plan pl;
-    bool empty = false;
-    kla_status st = common_checks(B, H, T, D, in_dtype, fwd_rows(in_dtype, false),
-                                  kla::kFwdWaves, kla::kFwdMatrixWords, kla::kFwdStateWords,
-                                  &pl, &empty);
-    if (st != KLA_OK || empty) return st;
+    return scan_fwd_impl(a, p, phi, b, in_dtype, lam0, eta0, lam, eta, nullptr, B, H, T, D,
+                         workspace, workspace_bytes, stream);
+}
 
-    const void* ins[4] = {a, p, phi, b};
-    const char* names[4] = {"a", "p", "phi", "b"};
-    const size_t esz = in_dtype == KLA_DTYPE_F32 ? 4 : 2;
-    for (int i = 0; i < 4; ++i) {
-        if (!ins[i]) return fail(KLA_ERR_INVALID_ARG, "%s is NULL", names[i]);
-        if (misaligned(ins[i], esz))
-            return fail(KLA_ERR_UNSUPPORTED, "%s is not %zu-byte aligned", names[i], esz);
-    }
-    if (!lam || !eta) return fail(KLA_ERR_INVALID_ARG, "%s is NULL", lam ? "eta" : "lam");
-    if (misaligned(lam, 4) || misaligned(eta, 4))
-        return fail(KLA_ERR_UNSUPPORTED, "outputs must be 4-byte aligned");
-    if ((lam0 && misaligned(lam0, 4)) || (eta0 && misaligned(eta0, 4)))
-        return fail(KLA_ERR_UNSUPPORTED, "lam0/eta0 must be 4-byte aligned");
-    if ((st = check_workspace(workspace, workspace_bytes, pl)) != KLA_OK) return st;
+kla_status kla_scan_fwd_states(const void* a, const void* p, const void* phi, const void* b,
+                               kla_dtype in_dtype, const float* lam0, const float* eta0,
+                               float* lam, float* eta, double* states, int64_t B, int64_t H,
+                               int64_t T, int64_t D, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+    t_detail[0] = '\0';
+    if (!states && B > 0 && H > 0 && T > 0 && D > 0)
+        return fail(KLA_ERR_INVALID_ARG, "states is NULL");
+    return scan_fwd_impl(a, p, phi, b, in_dtype, lam0, eta0, lam, eta, states, B, H, T, D,
+                         workspace, workspace_bytes, stream);
+}
 
-    const size_t in_bytes = size_t(pl.N) * esz, out_bytes = size_t(pl.N) * 4;
-    const size_t st_bytes = size_t(pl.C) * 4;
-    const Buffer bufs[9] = {{a, in_bytes, "a", false},           {p, in_bytes, "p", false},
-                            {phi, in_bytes, "phi", false},       {b, in_bytes, "b", false},
-                            {lam0, st_bytes, "lam0", false},     {eta0, st_bytes, "eta0", false},
-                            {lam, out_bytes, "lam", true},       {eta, out_bytes, "eta", true},
-                            {workspace, pl.ws.bytes, "workspace", true}};
-    if ((st = check_overlaps(bufs, 9)) != KLA_OK) return st;
-
-    kla::FwdArgs args = {};
-    args.in[0] = a;
-    args.in[1] = p;
-    args.in[2] = phi;
-    args.in[3] = b;
-    args.lam0 = lam0;
-    args.eta0 = eta0;
-    args.lam = lam;
-    args.eta = eta;
-    args.T = T;
-    args.D = D;
-    args.C = pl.C;
-    args.G = pl.G;
-    args.n_chunks = pl.n_chunks;
-    args.n_tiles = pl.n_tiles;
-    args.HD = H * D;
-    args.ws = kla::workspace_view(workspace, pl.ws);
-    const hipError_t err =
-        kla::launch_scan_fwd(args, in_dtype, kla::FwdMode::kScan, stream);
-    if (err != hipSuccess) return fail(KLA_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
-    return KLA_OK;
+size_t kla_scan_states_size(int64_t B, int64_t H, int64_t T, int64_t D) {
+    return kla_mixer_states_size(B, H, T, D);
 }
 
 size_t kla_scan_lti_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int64_t D,
@@ -428,22 +472,22 @@ kla_status kla_mixer_bwd(const void* k, const void* v, const void* lam_v, const 
     }
 
     // 2. the adjoint scan with the mixer's front and back ends
-    kla::MixerBwdArgs ba;
-    ba.k = k;
-    ba.v = v;
-    ba.lam_v = lam_v;
-    ba.q = q;
+    kla::StateBwdArgs ba = {};
+    ba.in[0] = k;
+    ba.in[1] = v;
+    ba.in[2] = lam_v;
+    ba.in[3] = q;
     ba.a_ch = a;
     ba.p_ch = p;
     ba.lam0 = lam0;
     ba.eta0 = eta0;
     ba.bstate = bstate;
-    ba.g_out = g_out;
-    ba.g_var = g_var;
-    ba.g_k = g_k;
-    ba.g_v = g_v;
-    ba.g_lam_v = g_lam_v;
-    ba.g_q = g_q;
+    ba.g0 = g_out;
+    ba.g1 = g_var;
+    ba.out[0] = g_k;
+    ba.out[1] = g_v;
+    ba.out[2] = g_lam_v;
+    ba.out[3] = g_q;
     ba.g_lam0 = g_lam0;
     ba.g_eta0 = g_eta0;
     ba.partial = reinterpret_cast<double*>(ws + lay.off_partial);
@@ -455,7 +499,7 @@ kla_status kla_mixer_bwd(const void* k, const void* v, const void* lam_v, const 
     ba.n_tiles = lay.bwd.n_tiles;
     ba.HD = H * D;
     ba.ws = kla::workspace_view(workspace, lay.bwd.ws);
-    err = kla::launch_mixer_bwd(ba, in_dtype, s);
+    err = kla::launch_state_bwd(ba, in_dtype, kla::StateBwdMode::kMixer, s);
     if (err != hipSuccess) return fail(KLA_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
 
     // 3. channel-gate gradients
@@ -620,6 +664,128 @@ kla_status kla_scan_bwd(const void* a, const void* p, kla_dtype in_dtype,
     args.ws = kla::workspace_view(workspace, pl.ws);
     const hipError_t err =
         kla::launch_scan_bwd(args, in_dtype, stream);
+    if (err != hipSuccess) return fail(KLA_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
+    return KLA_OK;
+}
+
+size_t kla_scan_bwd_states_workspace_size(int64_t B, int64_t H, int64_t T, int64_t D,
+                                          kla_dtype in_dtype) {
+    if (!known_dtype(in_dtype)) return 0;
+    MixerBwdLayout lay;
+    if (!scan_bwd_states_layout(B, H, T, D, in_dtype, &lay) || lay.fwd.N == 0) return 0;
+    return lay.bytes;
+}
+
+kla_status kla_scan_bwd_states(const void* a, const void* p, const void* phi, const void* b,
+                               kla_dtype in_dtype, const float* lam0, const float* eta0,
+                               const double* states, const float* g_lam, const float* g_eta,
+                               float* g_a, float* g_p, float* g_phi, float* g_b, float* g_lam0,
+                               float* g_eta0, int64_t B, int64_t H, int64_t T, int64_t D,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    Plan pl;
+    bool empty = false;
+    kla_status st = common_checks(B, H, T, D, in_dtype, kla::kMixBwdRows, kla::kMixBwdWaves,
+                                  kla::kBwdMatrixWords, kla::kBwdStateWords, &pl, &empty);
+    if (st != KLA_OK || empty) return st;
+    MixerBwdLayout lay;
+    if (!scan_bwd_states_layout(B, H, T, D, in_dtype, &lay) || !lay.fwd.offsets_fit)
+        return fail(KLA_ERR_UNSUPPORTED, "sizes not supported: B=%lld H=%lld T=%lld D=%lld",
+                    (long long)B, (long long)H, (long long)T, (long long)D);
+
+    const void* ins[4] = {a, p, phi, b};
+    const char* names[4] = {"a", "p", "phi", "b"};
+    const size_t esz = in_dtype == KLA_DTYPE_F32 ? 4 : 2;
+    for (int i = 0; i < 4; ++i) {
+        if (!ins[i]) return fail(KLA_ERR_INVALID_ARG, "%s is NULL", names[i]);
+        if (misaligned(ins[i], esz))
+            return fail(KLA_ERR_UNSUPPORTED, "%s is not %zu-byte aligned", names[i], esz);
+    }
+    const void* req[4] = {g_a, g_p, g_phi, g_b};
+    const char* rnames[4] = {"g_a", "g_p", "g_phi", "g_b"};
+    for (int i = 0; i < 4; ++i)
+        if (!req[i]) return fail(KLA_ERR_INVALID_ARG, "%s is NULL", rnames[i]);
+    const void* f32s[10] = {lam0, eta0, g_lam, g_eta, g_a, g_p, g_phi, g_b, g_lam0, g_eta0};
+    for (int i = 0; i < 10; ++i)
+        if (f32s[i] && misaligned(f32s[i], 4))
+            return fail(KLA_ERR_UNSUPPORTED, "float32 arguments must be 4-byte aligned");
+    if (states && misaligned(states, 16))
+        return fail(KLA_ERR_UNSUPPORTED, "states is not 16-byte aligned");
+    if (!workspace) return fail(KLA_ERR_WORKSPACE, "workspace is NULL");
+    if (misaligned(workspace, 256))
+        return fail(KLA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    if (workspace_bytes < lay.bytes)
+        return fail(KLA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                    lay.bytes);
+
+    const size_t in_bytes = size_t(pl.N) * esz, f_bytes = size_t(pl.N) * 4;
+    const size_t st_bytes = size_t(pl.C) * 4;
+    const Buffer bufs[16] = {
+        {a, in_bytes, "a", false},           {p, in_bytes, "p", false},
+        {phi, in_bytes, "phi", false},       {b, in_bytes, "b", false},
+        {lam0, st_bytes, "lam0", false},     {eta0, st_bytes, "eta0", false},
+        {g_lam, f_bytes, "g_lam", false},    {g_eta, f_bytes, "g_eta", false},
+        {g_a, f_bytes, "g_a", true},         {g_p, f_bytes, "g_p", true},
+        {g_phi, f_bytes, "g_phi", true},     {g_b, f_bytes, "g_b", true},
+        {g_lam0, st_bytes, "g_lam0", true},  {g_eta0, st_bytes, "g_eta0", true},
+        {workspace, lay.bytes, "workspace", true},
+        {states, mixer_states_bytes(lay.fwd, T), "states", false}};
+    if ((st = check_overlaps(bufs, 16)) != KLA_OK) return st;
+
+    char* ws = static_cast<char*>(workspace);
+    hipError_t err = hipSuccess;
+    const double* bstate = states;
+    if (!bstate) {
+        // 1. recompute the forward states at every kMixBwdRows-th row (unless
+        //    the forward call kept them)
+        double* rec = reinterpret_cast<double*>(ws + lay.off_bstate);
+        bstate = rec;
+        kla::FwdArgs fa = {};
+        fa.in[0] = a;
+        fa.in[1] = p;
+        fa.in[2] = phi;
+        fa.in[3] = b;
+        fa.lam0 = lam0;
+        fa.eta0 = eta0;
+        fa.bstate = rec;
+        fa.T = T;
+        fa.D = D;
+        fa.C = lay.fwd.C;
+        fa.G = lay.fwd.G;
+        fa.n_chunks = lay.fwd.n_chunks;
+        fa.n_tiles = lay.fwd.n_tiles;
+        fa.HD = H * D;
+        fa.ws = kla::workspace_view(workspace, lay.fwd.ws);
+        err = kla::launch_scan_fwd(fa, in_dtype, kla::FwdMode::kScanState, stream);
+        if (err != hipSuccess)
+            return fail(KLA_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
+    }
+
+    // 2. the adjoint scan, replaying each wave's rows from the states
+    kla::StateBwdArgs ba = {};
+    ba.in[0] = a;
+    ba.in[1] = p;
+    ba.in[2] = phi;
+    ba.in[3] = b;
+    ba.lam0 = lam0;
+    ba.eta0 = eta0;
+    ba.bstate = bstate;
+    ba.g0 = g_lam;
+    ba.g1 = g_eta;
+    ba.out[0] = g_a;
+    ba.out[1] = g_p;
+    ba.out[2] = g_phi;
+    ba.out[3] = g_b;
+    ba.g_lam0 = g_lam0;
+    ba.g_eta0 = g_eta0;
+    ba.T = T;
+    ba.D = D;
+    ba.C = lay.bwd.C;
+    ba.G = lay.bwd.G;
+    ba.n_chunks = lay.bwd.n_chunks;
+    ba.n_tiles = lay.bwd.n_tiles;
+    ba.HD = H * D;
+    ba.ws = kla::workspace_view(workspace, lay.bwd.ws);
+    err = kla::launch_state_bwd(ba, in_dtype, kla::StateBwdMode::kScan, stream);
     if (err != hipSuccess) return fail(KLA_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
     return KLA_OK;
 }

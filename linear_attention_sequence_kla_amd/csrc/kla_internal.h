@@ -92,40 +92,43 @@ constexpr int kBwdRows = 14, kBwdWaves = 8, kBwdMatrixWords = 6, kBwdStateWords 
 
 // kMixerState: the mixer's gates; writes the float64 states (lam, eta) after
 // every kMixBwdRows-th row into FwdArgs::bstate, for the mixer's backward
-// pass.  kMixerTrain: kMixer that also writes those states.
-enum class FwdMode { kScan, kMixer, kLti, kMixerState, kMixerTrain };
+// pass.  kMixerTrain: kMixer that also writes those states.  kScanState and
+// kScanTrain: the same for the scan's gates (states only / lam, eta and the
+// states), for the scan's backward pass from states.
+enum class FwdMode { kScan, kMixer, kLti, kMixerState, kMixerTrain, kScanState, kScanTrain };
 hipError_t launch_scan_fwd(const FwdArgs& args, kla_dtype dtype, FwdMode mode, hipStream_t stream);
 hipError_t launch_scan_bwd(const BwdArgs& args, kla_dtype dtype, hipStream_t stream);
 
-// Fused-mixer backward: token inputs k, v, lam_v, q; channel gates a, p; the
-// forward boundary states (recomputed by the caller with kMixerState);
-// upstream g_out, g_var.
-// Writes g_k, g_v, g_lam_v, g_q, g_lam0, g_eta0 and, per tile and lane, the
-// tile's sums of the channel-gate gradients into `partial` ([tile][2][64]).
-struct MixerBwdArgs {
-    const void* k;
-    const void* v;
-    const void* lam_v;
-    const void* q;
-    const float* a_ch;
+// Backward pass from float64 boundary states (the state after every
+// kMixBwdRows-th row, written by a forward mode above): each wave replays its
+// rows forward from the state before them, then runs the adjoint scan.
+//   kMixer: in = k, v, lam_v, q; channel gates a_ch, p_ch; upstream
+//           g0 = g_out, g1 = g_var (may be NULL); writes out = g_k, g_v,
+//           g_lam_v, g_q and, per tile and lane, the tile's sums of the
+//           channel-gate gradients into `partial` ([tile][2][64]).
+//   kScan:  in = a, p, phi, b; upstream g0 = g_lam, g1 = g_eta (either may
+//           be NULL); writes out = g_a, g_p, g_phi, g_b per token.
+// Both write g_lam0, g_eta0 (either may be NULL).
+enum class StateBwdMode { kMixer, kScan };
+struct StateBwdArgs {
+    const void* in[4];
+    const float* a_ch;   // kMixer: [H, D]
     const float* p_ch;
     const float* lam0;   // may be NULL (1)
     const float* eta0;   // may be NULL (0)
-    const double* bstate;  // forward states after every kMixBwdRows-th row (kMixerState)
-    const float* g_out;
-    const float* g_var;  // may be NULL (0)
-    float* g_k;
-    float* g_v;
-    float* g_lam_v;
-    float* g_q;
+    const double* bstate;  // forward states after every kMixBwdRows-th row
+    const float* g0;
+    const float* g1;
+    float* out[4];
     float* g_lam0;  // may be NULL
     float* g_eta0;  // may be NULL
-    double* partial;
+    double* partial;  // kMixer only
     int64_t T, D, C, G, n_chunks, n_tiles, HD;
     Workspace ws;
 };
 
-hipError_t launch_mixer_bwd(const MixerBwdArgs& args, kla_dtype dtype, hipStream_t stream);
+hipError_t launch_state_bwd(const StateBwdArgs& args, kla_dtype dtype, StateBwdMode mode,
+                            hipStream_t stream);
 // g_a[h, d], g_p[h, d]: the per-tile sums added over the batch and the chunks
 // in a fixed order.
 hipError_t launch_mixer_grad_reduce(const double* partial, float* g_a, float* g_p, int64_t B,

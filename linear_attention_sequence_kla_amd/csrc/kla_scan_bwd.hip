@@ -336,9 +336,23 @@ __global__ __launch_bounds__(W * kWave) void kla_scan_bwd_kernel(BwdArgs g) {
         advance_epoch(g.ws, tag, (g.n_chunks - 1) * g.G, g.n_tiles, lane);
 }
 
-// Fused-mixer backward (the kernel above with the mixer's front and back
-// ends).  Per token the readout out = q eta / lam, var = 1 / lam feeds the
-// adjoint scan with
+// Backward pass from float64 boundary states: the adjoint scan of the
+// kernel above, with the states lam_{t-1}, eta_{t-1} replayed on chip in
+// float64 instead of read per row.  The forward pass keeps the float64 state
+// after every L-th row (FwdMode::kMixerState/kMixerTrain for the mixer,
+// kScanState/kScanTrain for the scan); each wave replays its L rows forward
+// from the state before its first row, which gives the states of its rows
+// and the wave's adjoint map, and after the tile's carry exchange runs the
+// rows last to first.  Float64 states make the gradients exact wherever the
+// forward recursion itself is, also where lam or eta leave float32's range
+// (lam reaches 1e88 on hard gates).
+//
+// Mode kScan: the inputs are the gates a, p, phi, b; the upstream gradients
+// g_lam, g_eta feed the adjoint scan directly, and each token writes
+// g_a, g_p, g_phi = Lam, g_b = Eta (the formulas above).
+//
+// Mode kMixer (the fused mixer's backward).  Per token the readout
+// out = q eta / lam, var = 1 / lam feeds the adjoint scan with
 //     g_lam[t] = -(g_out q eta + g_var) / lam^2,   g_eta[t] = g_out q / lam,
 // and writes g_q = g_out eta / lam; the gates phi = k^2 lam_v, b = k lam_v v
 // send the scan's adjoints Lam (of phi) and Eta (of b) to the token inputs:
@@ -346,26 +360,27 @@ __global__ __launch_bounds__(W * kWave) void kla_scan_bwd_kernel(BwdArgs g) {
 //     g_v = Eta k lam_v;
 // the channel gates a, p collect their per-token adjoints (as g_a, g_p of
 // the kernel above) into one sum per tile and lane, added over the batch and
-// the chunks by kla_mixer_grad_reduce_kernel.
-//
-// The forward states are not read per row: the recompute writes the float64
-// state after every L-th row (FwdMode::kMixerState), and each wave replays
-// its L rows forward from the state before its first row, which also yields
-// the readout adjoints; only float32 copies of the states stay in registers
-// for the reverse pass.
+// the chunks by kla_mixer_grad_reduce_kernel.  The mixer's states stay within
+// float32's range, so its rows keep float32 copies of them for the reverse
+// pass (fewer registers).
 //
 // Four waves per SIMD (two workgroups of eight waves per CU) are asked for
 // explicitly: left to itself the compiler gives the bfloat16 instance a few
 // registers more than 128, which halves the workgroups per CU and costs a
 // quarter of the bandwidth on bfloat16 inputs.
-template <typename In, int L, int W>
+template <StateBwdMode M> struct StateOf { typedef float T; };
+template <> struct StateOf<StateBwdMode::kScan> { typedef double T; };
+
+template <typename In, int L, int W, StateBwdMode M>
 __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(4)))
-void kla_mixer_bwd_kernel(MixerBwdArgs g) {
-    static_assert(L == kMixBwdRows, "the recompute keeps a state every kMixBwdRows rows");
+void kla_state_bwd_kernel(StateBwdArgs g) {
+    static_assert(L == kMixBwdRows, "the forward keeps a state every kMixBwdRows rows");
+    constexpr bool kMix = M == StateBwdMode::kMixer;
+    typedef typename StateOf<M>::T S;  // the per-row states kept for the reverse pass
     __shared__ double s_adj[W][6][kWave];
     __shared__ double s_suf[W][6][kWave];  // the maps tile_carry leaves
     __shared__ double s_tc[2][kWave];       // the tile's carry
-    __shared__ double s_part[W][2][kWave];
+    __shared__ double s_part[kMix ? W : 1][2][kWave];
 
     const int lane = threadIdx.x & (kWave - 1);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -385,19 +400,24 @@ void kla_mixer_bwd_kernel(MixerBwdArgs g) {
         const uint32_t in_off = lm.lane_el * uint32_t(sizeof(In));
         const uint32_t f_off = lm.lane_el * uint32_t(sizeof(float));
         const int64_t in_base = lm.e0 * int64_t(sizeof(In));
-        const char* pk = static_cast<const char*>(g.k) + in_base;
-        const char* pv = static_cast<const char*>(g.v) + in_base;
-        const char* plv = static_cast<const char*>(g.lam_v) + in_base;
-        const char* pq = static_cast<const char*>(g.q) + in_base;
-        const char* pgo = reinterpret_cast<const char*>(g.g_out) + lm.e0 * 4;
-        const char* pgv = reinterpret_cast<const char*>(g.g_var) + lm.e0 * 4;
-        const int64_t hd = lm.qc % g.HD;
-        const double ac = g.a_ch[hd], pc = g.p_ch[hd];
-        char* oq = reinterpret_cast<char*>(g.g_q) + lm.e0 * 4;
+        const char* p0 = static_cast<const char*>(g.in[0]) + in_base;
+        const char* p1 = static_cast<const char*>(g.in[1]) + in_base;
+        const char* p2 = static_cast<const char*>(g.in[2]) + in_base;
+        const char* p3 = static_cast<const char*>(g.in[3]) + in_base;
+        const char* pg0 = reinterpret_cast<const char*>(g.g0) + lm.e0 * 4;
+        const char* pg1 = reinterpret_cast<const char*>(g.g1) + lm.e0 * 4;
+        double ac = 0.0, pc = 0.0;
+        if constexpr (kMix) {
+            const int64_t hd = lm.qc % g.HD;
+            ac = g.a_ch[hd];
+            pc = g.p_ch[hd];
+        }
 
         // ---- load the rows and the state before the wave's first row ----
         // (row t0 - 1's boundary state, or the initial state at t0 = 0)
-        float rk[L], rv[L], rlv[L], rq[L], rgo[L], rgv[L];
+        // mixer: r0..r3 = k, v, lam_v, q; rg0, rg1 = g_out, g_var
+        // scan:  r0..r3 = a, p, phi, b;   rg0, rg1 = g_lam, g_eta
+        float r0[L], r1[L], r2[L], r3[L], rg0[L], rg1[L];
         double l_in = 1.0, e_in = 0.0;
         if (nr > 0) {
             if (t0 > 0) {
@@ -414,46 +434,66 @@ void kla_mixer_bwd_kernel(MixerBwdArgs g) {
                 const int ri = min(i, nr - 1);
                 const uint32_t io = in_off + uint32_t(ri) * in_row;
                 const uint32_t fo = f_off + uint32_t(ri) * f_row;
-                rk[i] = load_gate<In>(pk, io);
-                rv[i] = load_gate<In>(pv, io);
-                rlv[i] = load_gate<In>(plv, io);
-                rq[i] = load_gate<In>(pq, io);
-                rgo[i] = load_f32(pgo, fo);
-                rgv[i] = g.g_var ? load_f32(pgv, fo) : 0.0f;
+                r0[i] = load_gate<In>(p0, io);
+                r1[i] = load_gate<In>(p1, io);
+                r2[i] = load_gate<In>(p2, io);
+                r3[i] = load_gate<In>(p3, io);
+                rg0[i] = g.g0 ? load_f32(pg0, fo) : 0.0f;
+                rg1[i] = g.g1 ? load_f32(pg1, fo) : 0.0f;
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < L; ++i) rk[i] = rv[i] = rlv[i] = rq[i] = rgo[i] = rgv[i] = 0.0f;
+            for (int i = 0; i < L; ++i) r0[i] = r1[i] = r2[i] = r3[i] = rg0[i] = rg1[i] = 0.0f;
         }
         if (w == 0) tag = read_tag(g.ws);
 
         // ---- forward replay of the rows (float64): the states lam_t, eta_t,
-        // the readout's adjoints and g_q; and the wave's map, the per-token
-        // adjoint maps multiplied in time order ----
-        // rl[i], re[i]: the state after row i, kept as float32 for the
-        // reverse pass (which takes the state before row 0 from l_in, e_in).
-        float rl[L], re[L], rgl[L], rge[L];
+        // the adjoints fed in per token (the readout's for the mixer, the
+        // upstream gradients for the scan), g_q for the mixer; and the wave's
+        // map, the per-token adjoint maps multiplied in time order ----
+        // rl[i], re[i]: the state after row i, kept for the reverse pass
+        // (which takes the state before row 0 from l_in, e_in).
+        S rl[L], re[L];
+        float rgl[L], rge[L];
         Adj m{1.0, 0.0, 0.0, 1.0, 0.0, 1.0};
         {
             double lp = l_in, ep = e_in;
 #pragma unroll
             for (int i = 0; i < L; ++i) {
                 if (i < nr) {
-                    const double k = rk[i], lv = rlv[i];
-                    const double rd = recip(fma(pc, lp, ac * ac));
-                    const double f = ac * rd;
-                    const double lt = fma(lp, rd, k * k * lv);
-                    const double et = fma(f, ep, k * lv * double(rv[i]));
-                    const double rlt = recip(lt);
-                    const double go = rgo[i], gq = go * double(rq[i]);
-                    rgl[i] = float(-fma(gq, et, double(rgv[i])) * rlt * rlt);
-                    rge[i] = float(gq * rlt);
-                    if (lm.valid)
-                        __builtin_nontemporal_store(
-                            float(go * et * rlt),
-                            reinterpret_cast<float*>(oq + f_off + uint32_t(i) * f_row));
+                    double a, p, ph, bb;
+                    if constexpr (kMix) {
+                        const double k = r0[i], lv = r2[i];
+                        a = ac;
+                        p = pc;
+                        ph = k * k * lv;
+                        bb = k * lv * double(r1[i]);
+                    } else {
+                        a = r0[i];
+                        p = r1[i];
+                        ph = r2[i];
+                        bb = r3[i];
+                    }
+                    const double rd = recip(fma(p, lp, a * a));
+                    const double f = a * rd;
+                    const double lt = fma(lp, rd, ph);
+                    const double et = fma(f, ep, bb);
+                    if constexpr (kMix) {
+                        const double rlt = recip(lt);
+                        const double go = rg0[i], gq = go * double(r3[i]);
+                        rgl[i] = float(-fma(gq, et, double(rg1[i])) * rlt * rlt);
+                        rge[i] = float(gq * rlt);
+                        if (lm.valid)
+                            __builtin_nontemporal_store(
+                                float(go * et * rlt),
+                                reinterpret_cast<float*>(reinterpret_cast<char*>(g.out[3]) +
+                                                         lm.e0 * 4 + f_off + uint32_t(i) * f_row));
+                    } else {
+                        rgl[i] = rg0[i];
+                        rge[i] = rg1[i];
+                    }
                     const double al = f * f;
-                    const double be = -pc * f * ep * rd;
+                    const double be = -p * f * ep * rd;
                     const double ge = rge[i];
                     const double o1 = fma(al, double(rgl[i]), be * ge);
                     const double o2 = f * ge;
@@ -463,21 +503,25 @@ void kla_mixer_bwd_kernel(MixerBwdArgs g) {
                     m.y = fma(m.w, o2, m.y);
                     m.w = m.w * f;
                     m.x = nx;
-                    rl[i] = float(lt);
-                    re[i] = float(et);
+                    rl[i] = S(lt);
+                    re[i] = S(et);
                     lp = lt;
                     ep = et;
                 } else {
-                    rl[i] = 1.0f;
-                    re[i] = rgl[i] = rge[i] = 0.0f;
+                    rl[i] = S(1.0);
+                    re[i] = S(0.0);
+                    rgl[i] = rge[i] = 0.0f;
                 }
                 if ((i % kRenormEvery) == kRenormEvery - 1 || i == L - 1) renorm(m);
             }
         }
+        // keep the reverse pass's operands as they are (no recomputation)
 #pragma unroll
-        for (int i = 0; i < L; ++i)
-            asm volatile("" : "+v"(rk[i]), "+v"(rv[i]), "+v"(rlv[i]), "+v"(rl[i]), "+v"(re[i]),
-                         "+v"(rgl[i]), "+v"(rge[i]));
+        for (int i = 0; i < L; ++i) {
+            asm volatile("" : "+v"(r0[i]), "+v"(r1[i]), "+v"(rl[i]), "+v"(re[i]), "+v"(rgl[i]),
+                         "+v"(rge[i]));
+            if constexpr (kMix) asm volatile("" : "+v"(r2[i]));
+        }
         asm volatile("" : "+v"(l_in), "+v"(e_in));
         s_adj[w][0][lane] = m.u;
         s_adj[w][1][lane] = m.v;
@@ -490,36 +534,52 @@ void kla_mixer_bwd_kernel(MixerBwdArgs g) {
         tile_carry<W>(g.ws, ticket, g.G, g.n_chunks, c, tag, s_adj, s_suf, s_tc, w, lane);
         __syncthreads();
 
-        // ---- replay last to first: token-input gradients, gate sums ----
+        // ---- replay last to first: input gradients (and the mixer's gate
+        // sums) ----
         double sa = 0.0, sp = 0.0;
         if (nr > 0) {
             double cl, ce;
             wave_carry<W>(s_suf, s_tc, w, lane, cl, ce);
-            char* ok = reinterpret_cast<char*>(g.g_k) + lm.e0 * 4;
-            char* ov = reinterpret_cast<char*>(g.g_v) + lm.e0 * 4;
-            char* olv = reinterpret_cast<char*>(g.g_lam_v) + lm.e0 * 4;
+            char* o0 = reinterpret_cast<char*>(g.out[0]) + lm.e0 * 4;
+            char* o1 = reinterpret_cast<char*>(g.out[1]) + lm.e0 * 4;
+            char* o2 = reinterpret_cast<char*>(g.out[2]) + lm.e0 * 4;
+            char* o3 = reinterpret_cast<char*>(g.out[3]) + lm.e0 * 4;
 #pragma unroll
             for (int i = L - 1; i >= 0; --i) {
                 if (i >= nr) continue;
-                const double lp = i ? rl[i - 1] : l_in, ep = i ? re[i - 1] : e_in;
-                const double rd = recip(fma(pc, lp, ac * ac));
+                const double lp = i ? double(rl[i - 1]) : l_in;
+                const double ep = i ? double(re[i - 1]) : e_in;
+                const double a = kMix ? ac : double(r0[i]);
+                const double p = kMix ? pc : double(r1[i]);
+                const double rd = recip(fma(p, lp, a * a));
                 const double rd2 = rd * rd;
-                const double f = ac * rd;
+                const double f = a * rd;
                 const double Lam = double(rgl[i]) + cl;
                 const double Eta = double(rge[i]) + ce;
-                sa += (Lam * (-2.0 * ac * lp) + Eta * ep * fma(pc, lp, -ac * ac)) * rd2;
-                sp += -lp * (Lam * lp + Eta * ac * ep) * rd2;
-                const double k = rk[i], vv = rv[i], lv = rlv[i];
+                const double ga = (Lam * (-2.0 * a * lp) + Eta * ep * fma(p, lp, -a * a)) * rd2;
+                const double gp = -lp * (Lam * lp + Eta * a * ep) * rd2;
                 if (lm.valid) {
                     const uint32_t off = f_off + uint32_t(i) * f_row;
-                    __builtin_nontemporal_store(float(fma(Lam * 2.0 * k, lv, Eta * lv * vv)),
-                                                reinterpret_cast<float*>(ok + off));
-                    __builtin_nontemporal_store(float(Eta * k * lv),
-                                                reinterpret_cast<float*>(ov + off));
-                    __builtin_nontemporal_store(float(fma(Lam * k, k, Eta * k * vv)),
-                                                reinterpret_cast<float*>(olv + off));
+                    if constexpr (kMix) {
+                        const double k = r0[i], vv = r1[i], lv = r2[i];
+                        __builtin_nontemporal_store(float(fma(Lam * 2.0 * k, lv, Eta * lv * vv)),
+                                                    reinterpret_cast<float*>(o0 + off));
+                        __builtin_nontemporal_store(float(Eta * k * lv),
+                                                    reinterpret_cast<float*>(o1 + off));
+                        __builtin_nontemporal_store(float(fma(Lam * k, k, Eta * k * vv)),
+                                                    reinterpret_cast<float*>(o2 + off));
+                    } else {
+                        __builtin_nontemporal_store(float(ga), reinterpret_cast<float*>(o0 + off));
+                        __builtin_nontemporal_store(float(gp), reinterpret_cast<float*>(o1 + off));
+                        __builtin_nontemporal_store(float(Lam), reinterpret_cast<float*>(o2 + off));
+                        __builtin_nontemporal_store(float(Eta), reinterpret_cast<float*>(o3 + off));
+                    }
                 }
-                cl = fma(f * f, Lam, -pc * f * ep * rd * Eta);
+                if constexpr (kMix) {
+                    sa += ga;
+                    sp += gp;
+                }
+                cl = fma(f * f, Lam, -p * f * ep * rd * Eta);
                 ce = f * Eta;
             }
             if (t0 == 0 && lm.valid) {
@@ -527,19 +587,21 @@ void kla_mixer_bwd_kernel(MixerBwdArgs g) {
                 if (g.g_eta0) g.g_eta0[lm.q] = float(ce);
             }
         }
-        // ---- the tile's sums of the channel-gate gradients ----
-        s_part[w][0][lane] = sa;
-        s_part[w][1][lane] = sp;
-        __syncthreads();
-        if (w == 0) {
-            double ta = 0.0, tp = 0.0;
+        // ---- the mixer: the tile's sums of the channel-gate gradients ----
+        if constexpr (kMix) {
+            s_part[w][0][lane] = sa;
+            s_part[w][1][lane] = sp;
+            __syncthreads();
+            if (w == 0) {
+                double ta = 0.0, tp = 0.0;
 #pragma unroll
-            for (int j = 0; j < W; ++j) {
-                ta += s_part[j][0][lane];
-                tp += s_part[j][1][lane];
+                for (int j = 0; j < W; ++j) {
+                    ta += s_part[j][0][lane];
+                    tp += s_part[j][1][lane];
+                }
+                g.partial[(size_t(ticket) * 2) * kWave + lane] = ta;
+                g.partial[(size_t(ticket) * 2 + 1) * kWave + lane] = tp;
             }
-            g.partial[(size_t(ticket) * 2) * kWave + lane] = ta;
-            g.partial[(size_t(ticket) * 2 + 1) * kWave + lane] = tp;
         }
     }
 
@@ -625,14 +687,23 @@ hipError_t launch_scan_bwd(const BwdArgs& args, kla_dtype dtype, hipStream_t str
     return hipGetLastError();
 }
 
-hipError_t launch_mixer_bwd(const MixerBwdArgs& args, kla_dtype dtype, hipStream_t stream) {
+template <StateBwdMode M>
+void launch_state(const StateBwdArgs& args, kla_dtype dtype, hipStream_t stream) {
     const dim3 grid(unsigned(args.n_tiles)), block(kMixBwdWaves * kWave);
     if (dtype == KLA_DTYPE_F32)
-        hipLaunchKernelGGL((kla_mixer_bwd_kernel<float, kMixBwdRows, kMixBwdWaves>), grid, block,
-                           0, stream, args);
-    else
-        hipLaunchKernelGGL((kla_mixer_bwd_kernel<uint16_t, kMixBwdRows, kMixBwdWaves>), grid,
+        hipLaunchKernelGGL((kla_state_bwd_kernel<float, kMixBwdRows, kMixBwdWaves, M>), grid,
                            block, 0, stream, args);
+    else
+        hipLaunchKernelGGL((kla_state_bwd_kernel<uint16_t, kMixBwdRows, kMixBwdWaves, M>), grid,
+                           block, 0, stream, args);
+}
+
+hipError_t launch_state_bwd(const StateBwdArgs& args, kla_dtype dtype, StateBwdMode mode,
+                            hipStream_t stream) {
+    if (mode == StateBwdMode::kMixer)
+        launch_state<StateBwdMode::kMixer>(args, dtype, stream);
+    else
+        launch_state<StateBwdMode::kScan>(args, dtype, stream);
     return hipGetLastError();
 }
 

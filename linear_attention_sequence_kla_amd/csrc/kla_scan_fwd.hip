@@ -33,7 +33,7 @@
 //     matrices of the waves before it, then replays its rows sequentially from
 //     on-chip data, writing lam and eta.
 //
-// The kernel has five modes (template parameter Mode):
+// The kernel has seven modes (template parameter Mode):
 //   * Scan: the four token inputs are the gates a, p, phi, b; writes lam, eta.
 //   * Mixer: the fused KLA mixer.  The inputs are the token tensors k, v,
 //     lam_v, q and per-channel gates (a, p); phi = k^2 lam_v and b = k lam_v v
@@ -49,6 +49,9 @@
 //     read.
 //   * Lti: per-channel (a, p, phi) and the token's b only (time-invariant
 //     gates; one input row per token, so 64 rows per wave).
+//   * ScanState / ScanTrain: the scan's gates, writing the float64 boundary
+//     states of MixerState (only them / with lam and eta), from which the
+//     scan's backward pass from states recomputes its rows' states.
 //
 // Arithmetic is float64 for everything carried (chunk matrices, states): the
 // exact precision can reach 1e88 and the information mean 1e-51 on hard gates,
@@ -149,6 +152,8 @@ enum class Mode {
     Lti,    // b per token, (a, p, phi) per channel -> lam, eta
     MixerState,  // k, v, lam_v per token, (a, p) per channel -> boundary (lam, eta)
     MixerTrain,  // Mixer's inputs -> Mixer's outputs and MixerState's
+    ScanState,   // Scan's inputs -> boundary (lam, eta) only
+    ScanTrain,   // Scan's inputs -> lam, eta and the boundary states
 };
 
 // The float64 gates (a, p, phi, b) of one token.  Scan mode reads them from
@@ -412,7 +417,8 @@ void kla_scan_kernel(FwdArgs g) {
                 Y = fma(bb, zn, a * Y);
                 Z = zn;
                 const uint32_t off = lm.lane_el * uint32_t(sizeof(float)) + uint32_t(i) * out_row;
-                if constexpr (M == Mode::MixerState || M == Mode::MixerTrain) {
+                if constexpr (M == Mode::MixerState || M == Mode::MixerTrain ||
+                              M == Mode::ScanState || M == Mode::ScanTrain) {
                     // the state after rows kMixBwdRows * j - 1, j = 1, 2, ...
                     // (the last row's is not needed), as float64 pairs
                     // [j - 1][channel][lam, eta]
@@ -439,7 +445,7 @@ void kla_scan_kernel(FwdArgs g) {
                         g.lam_T[lm.q] = float(X * rz);
                         g.eta_T[lm.q] = float(Y * rz);
                     }
-                } else if constexpr (M != Mode::MixerState) {
+                } else if constexpr (M != Mode::MixerState && M != Mode::ScanState) {
                     const double r = recip(Z);
                     if (lm.valid) {
                         __builtin_nontemporal_store(float(X * r), reinterpret_cast<float*>(olam + off));
@@ -482,6 +488,10 @@ hipError_t launch_scan_fwd(const FwdArgs& args, kla_dtype dtype, FwdMode mode,
         launch<kFwdRows, kMixerRowsBf16, kFwdWaves, Mode::MixerTrain>(args, dtype, stream);
     else if (mode == FwdMode::kMixerState)
         launch<kFwdRows, kMixerRowsBf16, kFwdWaves, Mode::MixerState>(args, dtype, stream);
+    else if (mode == FwdMode::kScanState)
+        launch<kFwdRows, kScanRowsBf16, kFwdWaves, Mode::ScanState>(args, dtype, stream);
+    else if (mode == FwdMode::kScanTrain)
+        launch<kFwdRows, kScanRowsBf16, kFwdWaves, Mode::ScanTrain>(args, dtype, stream);
     else
         launch<kLtiRows, kLtiRows, kLtiWaves, Mode::Lti>(args, dtype, stream);
     return hipGetLastError();

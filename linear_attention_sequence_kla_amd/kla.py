@@ -63,6 +63,16 @@ def load_library(path: str) -> ctypes.CDLL:
     lib.kla_scan_fwd_noalloc.restype = ctypes.c_int
     lib.kla_scan_fwd_noalloc_max_workspace.argtypes = []
     lib.kla_scan_fwd_noalloc_max_workspace.restype = sz
+    lib.kla_scan_states_size.argtypes = [i64, i64, i64, i64]
+    lib.kla_scan_states_size.restype = sz
+    lib.kla_scan_fwd_states.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp,
+                                        i64, i64, i64, i64, vp, sz, vp]
+    lib.kla_scan_fwd_states.restype = ctypes.c_int
+    lib.kla_scan_bwd_states_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+    lib.kla_scan_bwd_states_workspace_size.restype = sz
+    lib.kla_scan_bwd_states.argtypes = [vp, vp, vp, vp, ctypes.c_int] + [vp] * 11 + [i64] * 4 + [
+        vp, sz, vp]
+    lib.kla_scan_bwd_states.restype = ctypes.c_int
     lib.kla_scan_bwd_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int]
     lib.kla_scan_bwd_workspace_size.restype = sz
     lib.kla_scan_bwd.argtypes = [vp, vp, ctypes.c_int] + [vp] * 12 + [i64] * 4 + [vp, sz, vp]
@@ -261,6 +271,20 @@ def scan_fwd_noalloc(a: torch.Tensor, p: torch.Tensor, phi: torch.Tensor, b: tor
     return lam, eta
 
 
+def _check_gates(a, p, phi, b):
+    if a.dim() != 4:
+        raise ValueError("gates must be [B, H, T, D], got shape %s" % (tuple(a.shape),))
+    for name, t in zip(("a", "p", "phi", "b"), (a, p, phi, b)):
+        if t is None:
+            raise ValueError("%s is required" % name)
+        if t.shape != a.shape or t.dtype != a.dtype:
+            raise ValueError("%s must match a in shape and dtype" % name)
+        if not t.is_cuda or t.device != a.device or not t.is_contiguous():
+            raise ValueError("%s must be contiguous on a's GPU" % name)
+    if a.dtype not in _DTYPES:
+        raise ValueError("gate dtype must be float32 or bfloat16, got %s" % a.dtype)
+
+
 def _check_f32(name, t, shape, device):
     if t is None:
         return
@@ -324,29 +348,133 @@ def scan_bwd(a: torch.Tensor, p: torch.Tensor, lam: torch.Tensor, eta: torch.Ten
     return g_a, g_p, g_phi, g_b, g_lam0, g_eta0
 
 
+def scan_states_shape(B: int, H: int, T: int, D: int) -> tuple:
+    """Shape of the float64 tensor of scan states (kla_scan_fwd_states'
+    `states`): the (lam, eta) of every channel after every 8th token."""
+    C = B * H * D
+    n = int(library().kla_scan_states_size(B, H, T, D))
+    return (n // (16 * C) if C else 0, C, 2)
+
+
+def _check_scan_states(states, shape4, dev):
+    if states is None:
+        return
+    want = scan_states_shape(*shape4)
+    if (tuple(states.shape) != want or states.dtype != torch.float64 or not states.is_cuda
+            or states.device != dev or not states.is_contiguous()):
+        raise ValueError("states must be a contiguous float64 %s tensor on %s" % (want, dev))
+
+
+def scan_fwd_states(a: torch.Tensor, p: torch.Tensor, phi: torch.Tensor, b: torch.Tensor,
+                    lam0: torch.Tensor | None = None, eta0: torch.Tensor | None = None,
+                    states: torch.Tensor | None = None, out: tuple | None = None,
+                    workspace: torch.Tensor | None = None):
+    """kla_scan_fwd_states: the forward scan that also keeps the float64 state
+    after every 8th token for ``scan_bwd_states``.  Arguments as for
+    ``scan_fwd``; ``states`` (float64, ``scan_states_shape``) is allocated
+    when None.  Returns (lam, eta, states)."""
+    _check_gates(a, p, phi, b)
+    B, H, T, D = a.shape
+    for name, t in (("lam0", lam0), ("eta0", eta0)):
+        _check_f32(name, t, (B, H, D), a.device)
+    if out is None:
+        out = (torch.empty(a.shape, dtype=torch.float32, device=a.device),
+               torch.empty(a.shape, dtype=torch.float32, device=a.device))
+    lam, eta = out
+    for name, t in (("lam", lam), ("eta", eta)):
+        if t is None:
+            raise ValueError("%s output is required" % name)
+        _check_f32(name, t, a.shape, a.device)
+    if states is None:
+        states = torch.empty(scan_states_shape(B, H, T, D), dtype=torch.float64,
+                             device=a.device)
+    _check_scan_states(states, (B, H, T, D), a.device)
+    stream = torch.cuda.current_stream(a.device)
+    if workspace is None:
+        workspace = get_workspace(workspace_size(B, H, T, D, a.dtype), a.device, stream)
+    _check(library().kla_scan_fwd_states(
+        _ptr(a), _ptr(p), _ptr(phi), _ptr(b), _DTYPES[a.dtype], _ptr(lam0), _ptr(eta0),
+        _ptr(lam), _ptr(eta), _ptr(states), B, H, T, D, _ptr(workspace), workspace.numel(),
+        ctypes.c_void_p(stream.cuda_stream)))
+    _after_call("kla_scan_fwd_states", workspace)
+    return lam, eta, states
+
+
+def bwd_states_workspace_size(B: int, H: int, T: int, D: int, dtype=torch.float32) -> int:
+    """Bytes of workspace kla_scan_bwd_states needs (0 for an empty problem)."""
+    return int(library().kla_scan_bwd_states_workspace_size(B, H, T, D, _DTYPES[dtype]))
+
+
+def scan_bwd_states(a: torch.Tensor, p: torch.Tensor, phi: torch.Tensor, b: torch.Tensor,
+                    g_lam: torch.Tensor | None, g_eta: torch.Tensor | None,
+                    lam0: torch.Tensor | None = None, eta0: torch.Tensor | None = None,
+                    states: torch.Tensor | None = None, need_state_grads: bool = True,
+                    workspace: torch.Tensor | None = None, out: tuple | None = None):
+    """kla_scan_bwd_states: the backward scan from float64 states (exact also
+    where the forward outputs overflow float32).  ``states``: what
+    ``scan_fwd_states`` kept for these inputs, or None (recomputed).  Returns
+    (g_a, g_p, g_phi, g_b, g_lam0, g_eta0) as ``scan_bwd``."""
+    _check_gates(a, p, phi, b)
+    B, H, T, D = a.shape
+    dev = a.device
+    for name, t in (("g_lam", g_lam), ("g_eta", g_eta)):
+        _check_f32(name, t, a.shape, dev)
+    for name, t in (("lam0", lam0), ("eta0", eta0)):
+        _check_f32(name, t, (B, H, D), dev)
+    _check_scan_states(states, (B, H, T, D), dev)
+    if out is None:
+        out = tuple(torch.empty(a.shape, dtype=torch.float32, device=dev) for _ in range(4))
+    for name, t in zip(("g_a", "g_p", "g_phi", "g_b"), out):
+        if t is None:
+            raise ValueError("%s output is required" % name)
+        _check_f32(name, t, a.shape, dev)
+    g_a, g_p, g_phi, g_b = out
+    g_lam0 = g_eta0 = None
+    if need_state_grads:
+        g_lam0 = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+        g_eta0 = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    if workspace is None:
+        workspace = get_workspace(max(bwd_states_workspace_size(B, H, T, D, a.dtype),
+                                      workspace_size(B, H, T, D, a.dtype)), dev, stream)
+    _check(library().kla_scan_bwd_states(
+        _ptr(a), _ptr(p), _ptr(phi), _ptr(b), _DTYPES[a.dtype], _ptr(lam0), _ptr(eta0),
+        _ptr(states), _ptr(g_lam), _ptr(g_eta), _ptr(g_a), _ptr(g_p), _ptr(g_phi), _ptr(g_b),
+        _ptr(g_lam0), _ptr(g_eta0), B, H, T, D, _ptr(workspace), workspace.numel(),
+        ctypes.c_void_p(stream.cuda_stream)))
+    _after_call("kla_scan_bwd_states", workspace)
+    return g_a, g_p, g_phi, g_b, g_lam0, g_eta0
+
+
 class KLAScan(torch.autograd.Function):
-    """Differentiable forward scan: kla_scan_fwd forward, kla_scan_bwd backward.
+    """Differentiable forward scan: kla_scan_fwd_states forward, which also
+    keeps the float64 state after every 8th token (about 2 bytes per
+    element), and kla_scan_bwd_states backward from those states (defined on
+    the whole domain, also where lam or eta overflow float32).
 
     Gradients are float32 and are cast to each input's dtype.
     """
 
     @staticmethod
     def forward(ctx, a, p, phi, b, lam0, eta0):
-        lam, eta = scan_fwd(a, p, phi, b, lam0, eta0)
-        ctx.save_for_backward(a, p, lam0, eta0, lam, eta)
-        ctx.has_state = (lam0 is not None, eta0 is not None)
+        if any(ctx.needs_input_grad):
+            lam, eta, states = scan_fwd_states(a, p, phi, b, lam0, eta0)
+        else:
+            (lam, eta), states = scan_fwd(a, p, phi, b, lam0, eta0), None
+        ctx.save_for_backward(a, p, phi, b, lam0, eta0, states)
         return lam, eta
 
     @staticmethod
     def backward(ctx, g_lam, g_eta):
-        a, p, lam0, eta0, lam, eta = ctx.saved_tensors
+        a, p, phi, b, lam0, eta0, states = ctx.saved_tensors
         g_lam = None if g_lam is None else g_lam.contiguous().float()
         g_eta = None if g_eta is None else g_eta.contiguous().float()
         need = ctx.needs_input_grad
-        g_a, g_p, g_phi, g_b, g_lam0, g_eta0 = scan_bwd(
-            a, p, lam, eta, g_lam, g_eta, lam0, eta0, need_state_grads=need[4] or need[5])
+        g_a, g_p, g_phi, g_b, g_lam0, g_eta0 = scan_bwd_states(
+            a, p, phi, b, g_lam, g_eta, lam0, eta0, states=states,
+            need_state_grads=need[4] or need[5])
         cast = (lambda g, x: g.to(x.dtype))  # noqa: E731
-        return (cast(g_a, a), cast(g_p, p), cast(g_phi, a), cast(g_b, a),
+        return (cast(g_a, a), cast(g_p, p), cast(g_phi, phi), cast(g_b, b),
                 g_lam0 if need[4] else None, g_eta0 if need[5] else None)
 
 

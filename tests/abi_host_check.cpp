@@ -26,7 +26,7 @@ hipError_t launch_scan_bwd(const BwdArgs&, kla_dtype, hipStream_t) {
     ++g_launches;
     return hipErrorInvalidValue;
 }
-hipError_t launch_mixer_bwd(const MixerBwdArgs&, kla_dtype, hipStream_t) {
+hipError_t launch_state_bwd(const StateBwdArgs&, kla_dtype, StateBwdMode, hipStream_t) {
     ++g_launches;
     return hipErrorInvalidValue;
 }

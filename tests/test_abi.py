@@ -272,3 +272,63 @@ def test_mixer_decode_argument_errors_before_launch(lib):
     assert st == 1 and "overlaps" in msg
     st, _ = call(k=0, n=0)
     assert st == 0
+
+
+def test_states_sizes(lib):
+    """The scan's float64 states: 16 bytes per channel per 8 tokens, as the
+    mixer's; the backward-from-states workspace holds them and the carry
+    records."""
+    for shape in ((1, 1, 256, 16), (8, 16, 2048, 64), (3, 5, 77, 9)):
+        B, H, T, D = shape
+        assert lib.kla_scan_states_size(*shape) == ((T + 7) // 8) * B * H * D * 16
+        assert lib.kla_scan_states_size(*shape) == lib.kla_mixer_states_size(*shape)
+        ws = lib.kla_scan_bwd_states_workspace_size(*shape, 0)
+        assert ws >= lib.kla_scan_states_size(*shape) and ws % 256 == 0
+        assert ws >= lib.kla_scan_fwd_workspace_size(*shape, 0)
+    assert lib.kla_scan_states_size(0, 1, 8, 1) == 0
+    assert lib.kla_scan_bwd_states_workspace_size(1, 1, 8, 1, 9) == 0
+
+
+def test_states_argument_errors_before_launch(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("uses fake device pointers; argument errors are tested on GPUs elsewhere")
+    vp = ctypes.c_void_p
+    shape = (2, 1, 40, 4)
+    fwd_need = lib.kla_scan_fwd_workspace_size(*shape, 0)
+    bwd_need = lib.kla_scan_bwd_states_workspace_size(*shape, 0)
+
+    def fwd(states=0x3000000, lam=0x1000000):
+        st = lib.kla_scan_fwd_states(vp(0x100000), vp(0x200000), vp(0x300000), vp(0x400000), 0,
+                                     None, None, vp(lam), vp(0x2000000), vp(states), *shape,
+                                     vp(0x4000000), fwd_need, None)
+        return st, lib.kla_last_error_detail().decode()
+
+    st, msg = fwd(states=0)
+    assert st == 1 and "states is NULL" in msg
+    st, msg = fwd(states=0x3000008)
+    assert st == 2 and "16-byte" in msg
+    st, msg = fwd(states=0x1000000 - 64)  # lam is written over the states
+    assert st == 1 and "overlaps" in msg
+
+    def bwd(a=0x100000, g_a=0x1000000, states=0, ws_bytes=bwd_need, g_lam=0x700000):
+        st = lib.kla_scan_bwd_states(vp(a), vp(0x200000), vp(0x300000), vp(0x400000), 0, None,
+                                     None, vp(states), vp(g_lam), None, vp(g_a),
+                                     vp(0x1100000), vp(0x1200000), vp(0x1300000), None, None,
+                                     *shape, vp(0x4000000), ws_bytes, None)
+        return st, lib.kla_last_error_detail().decode()
+
+    st, msg = bwd(a=0)
+    assert st == 1 and "a is NULL" in msg
+    st, msg = bwd(g_a=0)
+    assert st == 1 and "g_a is NULL" in msg
+    st, msg = bwd(ws_bytes=bwd_need - 8)
+    assert st == 3 and "needs" in msg
+    st, msg = bwd(g_a=0x700000)  # a gradient over the upstream gradient
+    assert st == 1 and "overlaps" in msg
+    st, msg = bwd(states=0x3000008)
+    assert st == 2 and "16-byte" in msg
+    # empty problem: nothing to do
+    st = lib.kla_scan_bwd_states(None, None, None, None, 0, None, None, None, None, None, None,
+                                 None, None, None, None, None, 1, 1, 0, 4, None, 0, None)
+    assert st == 0

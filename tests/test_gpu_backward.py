@@ -245,3 +245,149 @@ def test_backward_argument_errors():
     assert e.value.name == "KLA_ERR_WORKSPACE"
     with pytest.raises(ValueError):
         scan_bwd(d["a"], d["p"], None, d["a"].clone(), None, None)
+
+
+# ---------------------------------------------------------------------------
+# The backward pass from float64 states (kla_scan_fwd_states /
+# kla_scan_bwd_states): defined on the whole domain, so every channel is
+# compared, also where lam or eta overflow float32 (hard gates).
+
+STATE_SHAPES = SHAPES + [
+    (2, 3, 8, 5, "hard", "f32"),        # exactly one state block
+    (1, 2, 9, 7, "hard", "bf16"),       # one row past a state block
+    (2, 1, 64, 9, "hard", "f32"),       # exactly one backward tile (8 rows x 8 waves)
+    (2, 1, 65, 9, "std", "f32"),        # one row into a second tile
+    (1, 3, 129, 40, "hard", "f32"),
+    (4, 2, 600, 32, "hard", "f32"),     # hard gates: lam overflows float32 in places
+]
+
+
+def _bwd_states(g, g_lam, g_eta, keep_states):
+    from linear_attention_sequence_kla_amd import scan_bwd_states, scan_fwd_states
+    d = {k: v.to(DEV) for k, v in g.items()}
+    states = None
+    if keep_states:
+        _, _, states = scan_fwd_states(d["a"], d["p"], d["phi"], d["b"], d["lam0"], d["eta0"])
+    out = scan_bwd_states(d["a"], d["p"], d["phi"], d["b"],
+                          None if g_lam is None else g_lam.to(DEV),
+                          None if g_eta is None else g_eta.to(DEV), d["lam0"], d["eta0"],
+                          states=states)
+    torch.cuda.synchronize(DEV)
+    return dict(zip(("a", "p", "phi", "b", "lam0", "eta0"), out))
+
+
+@pytest.mark.parametrize("shape", STATE_SHAPES,
+                         ids=lambda s: "x".join(map(str, s[:4])) + s[4] + s[5])
+def test_backward_states_shapes(shape):
+    """Every channel, hard gates included; kept states and recomputed states
+    give identical bits."""
+    B, H, T, D, fam, dtype = shape
+    _say("backward from states, shape %s" % (shape,))
+    g = make_gates((B, H, T, D), fam, dtype, seed=B * 11 + T)
+    g["lam0"], g["eta0"] = make_initial_state(B, H, D, random=True, seed=T + 1)
+    g_lam, g_eta = upstream((B, H, T, D), T + 1)
+    kept = _bwd_states(g, g_lam, g_eta, keep_states=True)
+    again = _bwd_states(g, g_lam, g_eta, keep_states=False)
+    assert health() == 0
+    for k in kept:
+        assert torch.equal(kept[k], again[k]), k
+    grads, mags = oracle_grads(g, g_lam, g_eta)
+    rep = compare_grads({k: v.cpu() for k, v in kept.items()}, grads, mags)
+    _say("%s: %s" % (shape, rep))
+    assert_grad_parity(rep, TOL_BF16 if dtype == "bf16" else TOL_F32, str(shape))
+
+
+def compare_grads_by_slabs(g, g_lam, g_eta, got, shape, max_elements=1 << 23):
+    """Every gradient element against the backward oracle, a batch of (b, h)
+    slabs at a time (inputs copied to the host per batch)."""
+    B, H, T, D = shape
+    S = B * H
+    per = max(1, min(S, max_elements // max(1, T * D)))
+    rep = {"nan": 0, "range_violations": 0}
+    for s0 in range(0, S, per):
+        s1 = min(S, s0 + per)
+
+        def cut(x):
+            return x.reshape(S, T, D)[s0:s1].cpu().reshape(1, s1 - s0, T, D)
+
+        def cut3(x):
+            return x.reshape(S, D)[s0:s1].cpu().reshape(1, s1 - s0, D)
+
+        host = {k: cut(g[k]) for k in ("a", "p", "phi", "b")}
+        host["lam0"], host["eta0"] = cut3(g["lam0"]), cut3(g["eta0"])
+        grads, mags = oracle_grads(host, cut(g_lam), cut(g_eta))
+        mine = {k: cut(got[k]) for k in ("a", "p", "phi", "b")}
+        mine["lam0"], mine["eta0"] = cut3(got["lam0"]), cut3(got["eta0"])
+        r = compare_grads(mine, grads, mags)
+        for k, v in r.items():
+            rep[k] = rep.get(k, 0) + v if k in ("nan", "range_violations") else max(
+                rep.get(k, 0.0), v)
+        del host, grads, mags, mine
+    return rep
+
+
+@pytest.mark.parametrize("key", [0, 1, 2, 3, 4])
+def test_backward_states_workload_every_element(key):
+    """A workload at full size, drawn on the GPU as the benchmark draws it,
+    through the training pair (forward keeping the states, backward from
+    them); every gradient element of every channel against the oracle."""
+    from linear_attention_sequence_kla_amd import scan_bwd_states, scan_fwd_states
+    w = WORKLOADS[key]
+    _say("backward from states, workload %s (every element)" % w.describe())
+    g = make_workload(key, device=DEV)
+    g_lam, g_eta = upstream(w.shape, key, device=DEV)
+    _, _, states = scan_fwd_states(g["a"], g["p"], g["phi"], g["b"], g["lam0"], g["eta0"])
+    out = scan_bwd_states(g["a"], g["p"], g["phi"], g["b"], g_lam, g_eta, g["lam0"], g["eta0"],
+                          states=states)
+    torch.cuda.synchronize(DEV)
+    assert health() == 0
+    del states
+    got = dict(zip(("a", "p", "phi", "b", "lam0", "eta0"), out))
+    rep = compare_grads_by_slabs(g, g_lam, g_eta, got, w.shape)
+    _say("%s: %s" % (w.describe(), rep))
+    assert_grad_parity(rep, TOL_BF16 if w.dtype == "bf16" else TOL_F32, w.describe())
+    del g, g_lam, g_eta, out, got
+    torch.cuda.empty_cache()
+
+
+def test_autograd_hard_gates_every_channel():
+    """The autograd Function (forward keeping states, backward from them) on
+    hard gates whose forward outputs overflow float32 in places: every
+    channel matches the oracle."""
+    from linear_attention_sequence_kla_amd import kla_scan
+    shape = (8, 4, 2048, 32)
+    g = make_gates(shape, "hard", "f32", seed=44)
+    g["lam0"], g["eta0"] = make_initial_state(8, 4, 32, random=True, seed=44)
+    g_lam, g_eta = upstream(shape, 44)
+    x = {k: g[k].to(DEV).clone().requires_grad_(True) for k in g}
+    lam, eta = kla_scan(x["a"], x["p"], x["phi"], x["b"], x["lam0"], x["eta0"])
+    assert not bool(torch.isfinite(lam).all())  # the overflow case is exercised
+    # one backward pass for both outputs (the gradient of
+    # sum(g_lam * lam + g_eta * eta)): two separate passes would add two
+    # float32 results that can overflow with opposite signs where their sum
+    # does not
+    torch.autograd.backward([lam, eta], [g_lam.to(DEV), g_eta.to(DEV)])
+    torch.cuda.synchronize(DEV)
+    got = {k: x[k].grad.cpu() for k in x}
+    grads, mags = oracle_grads(g, g_lam, g_eta)
+    rep = compare_grads(got, grads, mags)
+    _say("autograd, hard gates: %s" % rep)
+    assert_grad_parity(rep, TOL_F32, "autograd, hard gates")
+
+
+def test_backward_states_argument_errors():
+    from linear_attention_sequence_kla_amd import KlaError, scan_bwd_states, scan_fwd_states
+    g = make_gates((1, 2, 100, 8), "std", "f32", seed=3)
+    d = {k: v.to(DEV) for k, v in g.items()}
+    small = torch.zeros(64, dtype=torch.uint8, device=DEV)
+    with pytest.raises(KlaError) as e:
+        scan_bwd_states(d["a"], d["p"], d["phi"], d["b"], None, None, workspace=small)
+    assert e.value.name == "KLA_ERR_WORKSPACE"
+    with pytest.raises(ValueError):  # states of the wrong shape
+        scan_bwd_states(d["a"], d["p"], d["phi"], d["b"], None, None,
+                        states=torch.zeros((3, 16, 2), dtype=torch.float64, device=DEV))
+    with pytest.raises(KlaError) as e:  # states overlapping an output
+        lam = torch.empty((1, 2, 100, 8), device=DEV)
+        scan_fwd_states(d["a"], d["p"], d["phi"], d["b"], out=(lam, torch.empty_like(lam)),
+                        states=lam.view(torch.float64).reshape(-1)[:13 * 16 * 2].reshape(13, 16, 2))
+    assert e.value.name == "KLA_ERR_INVALID_ARG"

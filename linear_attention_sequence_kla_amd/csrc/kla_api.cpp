@@ -97,6 +97,11 @@ bool known_dtype(const kla_dtype& d) {
 int fwd_rows(const kla_dtype& d, bool mixer) {
     return known_dtype(d) ? kla::fwd_rows(d, mixer) : kla::kFwdRows;
 }
+// The forward kernel's tile in the scan modes for this problem (the 4-wave
+// float32 tile for an unknown dtype, which common_checks then rejects).
+kla::FwdTile scan_tile(const kla_dtype& d, int64_t T) {
+    return known_dtype(d) ? kla::scan_tile(d, T) : kla::FwdTile{kla::kFwdRows, kla::kFwdWaves};
+}
 
 struct Buffer {
     const void* p;
@@ -183,7 +188,8 @@ bool mixer_bwd_layout(int64_t B, int64_t H, int64_t T, int64_t D, const kla_dtyp
 // states after every kMixBwdRows-th row.
 bool scan_bwd_states_layout(int64_t B, int64_t H, int64_t T, int64_t D, const kla_dtype& dt,
                             MixerBwdLayout* l) {
-    if (!kla::make_plan(B, H, T, D, fwd_rows(dt, false), kla::kFwdWaves, kla::kFwdMatrixWords,
+    const kla::FwdTile tile = scan_tile(dt, T);
+    if (!kla::make_plan(B, H, T, D, tile.rows, tile.waves, kla::kFwdMatrixWords,
                         kla::kFwdStateWords, &l->fwd) ||
         !kla::make_plan(B, H, T, D, kla::kMixBwdRows, kla::kMixBwdWaves, kla::kBwdMatrixWords,
                         kla::kBwdStateWords, &l->bwd))
@@ -200,8 +206,9 @@ kla_status scan_fwd_impl(const void* a, const void* p, const void* phi, const vo
                          int64_t D, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     Plan pl;
     bool empty = false;
-    kla_status st = common_checks(B, H, T, D, in_dtype, fwd_rows(in_dtype, false),
-                                  kla::kFwdWaves, kla::kFwdMatrixWords, kla::kFwdStateWords,
+    const kla::FwdTile tile = scan_tile(in_dtype, T);
+    kla_status st = common_checks(B, H, T, D, in_dtype, tile.rows, tile.waves,
+                                  kla::kFwdMatrixWords, kla::kFwdStateWords,
                                   &pl, &empty);
     if (st != KLA_OK || empty) return st;
 
@@ -249,6 +256,7 @@ kla_status scan_fwd_impl(const void* a, const void* p, const void* phi, const vo
     args.n_tiles = pl.n_tiles;
     args.HD = H * D;
     args.bstate = states;
+    args.tall = tile.tall();
     args.ws = kla::workspace_view(workspace, pl.ws);
     const hipError_t err = kla::launch_scan_fwd(
         args, in_dtype, states ? kla::FwdMode::kScanTrain : kla::FwdMode::kScan, stream);
@@ -264,8 +272,9 @@ size_t kla_scan_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int64_t D,
                                    kla_dtype in_dtype) {
     if (!known_dtype(in_dtype)) return 0;
     Plan pl;
-    if (!kla::make_plan(B, H, T, D, fwd_rows(in_dtype, false), kla::kFwdWaves,
-                        kla::kFwdMatrixWords, kla::kFwdStateWords, &pl) || pl.N == 0)
+    const kla::FwdTile tile = scan_tile(in_dtype, T);
+    if (!kla::make_plan(B, H, T, D, tile.rows, tile.waves, kla::kFwdMatrixWords,
+                        kla::kFwdStateWords, &pl) || pl.N == 0)
         return 0;
     return pl.ws.bytes;
 }
@@ -754,6 +763,7 @@ kla_status kla_scan_bwd_states(const void* a, const void* p, const void* phi, co
         fa.n_chunks = lay.fwd.n_chunks;
         fa.n_tiles = lay.fwd.n_tiles;
         fa.HD = H * D;
+        fa.tall = scan_tile(in_dtype, T).tall();
         fa.ws = kla::workspace_view(workspace, lay.fwd.ws);
         err = kla::launch_scan_fwd(fa, in_dtype, kla::FwdMode::kScanState, stream);
         if (err != hipSuccess)

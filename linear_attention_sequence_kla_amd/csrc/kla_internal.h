@@ -52,6 +52,7 @@ struct FwdArgs {
     float* eta_T;
     double* bstate;        // mixer states: [ceil(T / kMixBwdRows)][C][2] float64
                            // (kMixerState, kMixerTrain)
+    bool tall;             // scan modes: the tall tile (scan_tile)
     int64_t T, D, C, G, n_chunks, n_tiles, HD;
     Workspace ws;
 };
@@ -85,6 +86,22 @@ constexpr int kScanRowsBf16 = 24, kMixerRowsBf16 = 36;
 // modes or in the mixer modes.
 inline int fwd_rows(kla_dtype dt, bool mixer) {
     return dt == KLA_DTYPE_F32 ? kFwdRows : mixer ? kMixerRowsBf16 : kScanRowsBf16;
+}
+// Long float32 sequences take taller tiles in the scan modes: 8 waves of 18
+// rows (144-row tiles, two workgroups per CU), which measured 2% faster on
+// the long-context shape (1 x 32 x 131072 x 128) and within 1% elsewhere at
+// T >= 65536, while shorter sequences are up to 5% faster with the 4-wave
+// tiles.
+constexpr int kTallRows = 18, kTallWaves = 8;
+constexpr int64_t kTallMinT = 65536;
+struct FwdTile {
+    int rows, waves;
+    bool tall() const { return waves == kTallWaves; }
+};
+// The forward kernel's tile in the scan modes (Scan, ScanState, ScanTrain).
+inline FwdTile scan_tile(kla_dtype dt, int64_t T) {
+    if (dt == KLA_DTYPE_F32 && T >= kTallMinT) return FwdTile{kTallRows, kTallWaves};
+    return FwdTile{fwd_rows(dt, false), kFwdWaves};
 }
 constexpr int kLtiRows = 64, kLtiWaves = 4;
 constexpr int kMixBwdRows = 8, kMixBwdWaves = 8;

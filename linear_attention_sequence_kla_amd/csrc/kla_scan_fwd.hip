@@ -467,6 +467,14 @@ void kla_scan_kernel(FwdArgs g) {
         advance_epoch(g.ws, tag, (g.n_chunks - 1) * g.G, g.n_tiles, lane);
 }
 
+// The scan modes on float32 gates with the tall tile (long sequences).
+template <Mode M>
+void launch_tall(const FwdArgs& args, hipStream_t stream) {
+    const dim3 grid(unsigned(args.n_tiles)), block(kTallWaves * kWave);
+    hipLaunchKernelGGL((kla_scan_kernel<float, kTallRows, kTallWaves, M>), grid, block, 0, stream,
+                       args);
+}
+
 template <int L32, int L16, int W, Mode M>
 void launch(const FwdArgs& args, kla_dtype dtype, hipStream_t stream) {
     const dim3 grid(unsigned(args.n_tiles)), block(W * kWave);
@@ -480,7 +488,14 @@ void launch(const FwdArgs& args, kla_dtype dtype, hipStream_t stream) {
 
 hipError_t launch_scan_fwd(const FwdArgs& args, kla_dtype dtype, FwdMode mode,
                            hipStream_t stream) {
-    if (mode == FwdMode::kScan)
+    const bool tall = args.tall && dtype == KLA_DTYPE_F32;
+    if (tall && mode == FwdMode::kScan)
+        launch_tall<Mode::Scan>(args, stream);
+    else if (tall && mode == FwdMode::kScanState)
+        launch_tall<Mode::ScanState>(args, stream);
+    else if (tall && mode == FwdMode::kScanTrain)
+        launch_tall<Mode::ScanTrain>(args, stream);
+    else if (mode == FwdMode::kScan)
         launch<kFwdRows, kScanRowsBf16, kFwdWaves, Mode::Scan>(args, dtype, stream);
     else if (mode == FwdMode::kMixer)
         launch<kFwdRows, kMixerRowsBf16, kFwdWaves, Mode::Mixer>(args, dtype, stream);

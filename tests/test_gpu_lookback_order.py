@@ -23,7 +23,8 @@ pytestmark = pytest.mark.gpu
 
 DEV = torch.device("cuda:0")
 # a few columns with long chains of tiles, and many columns
-SHAPES = [(1, 2, 9000, 64), (2, 2, 3000, 96), (3, 3, 2000, 128)]
+SHAPES = [(1, 2, 9000, 64), (2, 2, 3000, 96), (3, 3, 2000, 128),
+          (1, 1, 70000, 64)]  # the tall tiles of long sequences
 
 
 @pytest.fixture
@@ -63,6 +64,17 @@ def test_scan_forward_and_backward(debug_build, shape):
                                   g_lam, g_eta)
     got = dict(zip(("a", "p", "phi", "b", "lam0", "eta0"), (t.cpu() for t in out)))
     assert_grad_parity(compare_grads(got, grads, mags), TOL_F32, "backward %s" % (shape,))
+
+    # the training pair: forward keeping float64 states, backward from them
+    from linear_attention_sequence_kla_amd import scan_bwd_states, scan_fwd_states
+    _, _, states = scan_fwd_states(d["a"], d["p"], d["phi"], d["b"], d["lam0"], d["eta0"])
+    out = scan_bwd_states(d["a"], d["p"], d["phi"], d["b"], g_lam.to(DEV), g_eta.to(DEV),
+                          d["lam0"], d["eta0"], states=states)
+    torch.cuda.synchronize(DEV)
+    assert _health() == 0
+    got = dict(zip(("a", "p", "phi", "b", "lam0", "eta0"), (t.cpu() for t in out)))
+    assert_grad_parity(compare_grads(got, grads, mags), TOL_F32,
+                       "backward from states %s" % (shape,))
 
 
 @pytest.mark.parametrize("shape", [(1, 2, 9000, 128), (3, 3, 2000, 256)],

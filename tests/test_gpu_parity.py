@@ -175,6 +175,13 @@ SHAPES = [
     (2, 2, 1153, 70, "std", "bf16"),     # bf16, many tiles, odd rows in the last wave
     (2, 3, 1, 40, "hard", "bf16"),       # bf16, a single token
     (1, 1, 2, 1, "std", "bf16"),         # bf16, two tokens, one channel
+    # long float32 sequences take the tall tiles (18 rows x 8 waves = 144 rows)
+    (1, 1, 65535, 3, "hard", "f32"),     # one token below the tall-tile length
+    (1, 1, 65536, 3, "hard", "f32"),     # the first tall length, ragged last tile
+    (1, 2, 65664, 64, "std", "f32"),     # exactly 456 tall tiles
+    (2, 1, 65665, 100, "slow", "f32"),   # one row into a tall tile, groups straddle slabs
+    (1, 1, 65553, 128, "std", "f32"),    # paired row halves, rows into the last tile's 2nd wave
+    (1, 1, 70000, 64, "std", "bf16"),    # bf16 keeps its 4-wave tiles at any length
 ]
 
 

@@ -37,11 +37,16 @@ bool make_plan(int64_t B, int64_t H, int64_t T, int64_t D, int rows_per_wave, in
     pl->n_chunks = (T + R - 1) / R;
     if (!mul_ok(pl->G, pl->n_chunks, &pl->n_tiles)) return false;
     if (pl->n_tiles > int64_t(INT32_MAX)) return false;
-    // Each wave addresses its rows with 32-bit byte offsets from one base: the
-    // 64 channels of a column group span at most ceil((D + 62) / D) slabs of
-    // T*D elements, plus one row before and the wave's own rows.
+    // Each wave addresses its rows with 32-bit byte offsets from one base.
+    // When D is a multiple of 64, a column group's 64 channels lie in one
+    // slab, so the offsets only span the wave's own rows (plus one row before)
+    // whatever T is; otherwise the 64 channels span up to ceil((D + 62) / D)
+    // slabs of T*D elements.
     int64_t span_el = 0;
-    if (D > 0) span_el = ((D + 62) / D) * T * D + 2 * D + int64_t(rows_per_wave) * D;
+    if (D > 0 && D % kWave == 0)
+        span_el = (int64_t(rows_per_wave) + 2) * D + kWave;
+    else if (D > 0)
+        span_el = ((D + 62) / D) * T * D + 2 * D + int64_t(rows_per_wave) * D;
     pl->offsets_fit = span_el < (int64_t(1) << 30);
     pl->ws = workspace_layout(size_t(pl->n_tiles), matrix_words, state_words);
     return true;
@@ -138,8 +143,9 @@ kla_status common_checks(int64_t B, int64_t H, int64_t T, int64_t D, const kla_d
     if (*empty) return KLA_OK;
     if (!pl->offsets_fit)
         return fail(KLA_ERR_UNSUPPORTED,
-                    "one [T, D] slab is too large (T*D = %lld elements; the limit is about 2^30 "
-                    "elements per 64 channels)", (long long)(T * D));
+                    "one [T, D] slab is too large for D = %lld (T*D = %lld elements; when D is not "
+                    "a multiple of 64 the limit is about 2^30 elements per 64 channels)",
+                    (long long)D, (long long)(T * D));
     return KLA_OK;
 }
 

@@ -142,9 +142,10 @@ C_CALLER int main() {
     CHECK("fwd unknown dtype", KLA_ERR_UNSUPPORTED, 0,
           fwd(at(0), at(6), at(8), ws_fwd, T, dtype_code(-3)));
     CHECK("fwd empty", KLA_OK, 0, fwd(0, 0, 0, 0, 0, KLA_DTYPE_F32));
+    // (D = 65: a wave's channels straddle two slabs of T * D elements)
     CHECK("fwd slab too large", KLA_ERR_UNSUPPORTED, 0,
           kla_scan_fwd(P(at(0)), P(at(1)), P(at(2)), P(at(3)), KLA_DTYPE_F32, nullptr, nullptr,
-                       F(at(6)), F(at(7)), 1, 1, int64_t(1) << 31, 64, P(at(8)), SIZE_MAX,
+                       F(at(6)), F(at(7)), 1, 1, int64_t(1) << 25, 65, P(at(8)), SIZE_MAX,
                        nullptr));
 
     // ---- kla_scan_bwd ----

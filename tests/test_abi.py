@@ -100,9 +100,14 @@ def test_argument_errors_before_launch(lib):
     # empty problem: nothing to do, no pointer needed
     st, _ = _call(lib, a=0, shape=(1, 1, 0, 4))
     assert st == 0
-    # slab too large for 32-bit offsets
-    st, msg = _call(lib, shape=(1, 1, 1 << 31, 64), ws_bytes=1 << 62)
-    assert st in (1, 2)
+    # a wave's 64 channels straddle slabs (D not a multiple of 64) too far
+    # apart for 32-bit offsets
+    st, msg = _call(lib, shape=(1, 1, 1 << 25, 65), ws_bytes=1 << 62)
+    assert st == 2 and "too large" in msg
+    # with D a multiple of 64 the offsets stay within the wave's rows: any T
+    # passes the size checks (here the fake buffers then overlap)
+    st, msg = _call(lib, shape=(1, 1, 1 << 25, 64), ws_bytes=1 << 62)
+    assert st == 1 and "overlaps" in msg
 
 
 def test_health_rejects_null(lib):

@@ -151,6 +151,34 @@ def test_largest_offsets():
     torch.cuda.empty_cache()
 
 
+def test_long_single_sequence():
+    """One sequence of 17M tokens at D = 64 (1.09G elements, 4.35 GB per
+    float32 tensor): with D a multiple of 64 the per-wave offsets stay within
+    a wave's rows, so such a sequence runs in one call.  The oracle checks
+    whole channels (the first, one in the middle, the last)."""
+    from linear_attention_sequence_kla_amd import scan_fwd
+    B, H, T, D = 1, 1, 17_000_000, 64
+    _say("long single sequence %s" % ((B, H, T, D),))
+    g = make_gates((B, H, T, D), "slow", "f32", seed=79, device=DEV)
+    lam0, eta0 = make_initial_state(B, H, D, random=True, seed=79, device=DEV)
+    lam, eta = scan_fwd(g["a"], g["p"], g["phi"], g["b"], lam0, eta0)
+    torch.cuda.synchronize(DEV)
+    assert health() == 0
+    q = np.array([0, 31, 63])
+    gs = {k: _gather(g[k], D, q).cpu() for k in ("a", "p", "phi", "b")}
+    qd = torch.as_tensor(q, device=DEV)
+    ref = oracle_scan(gs["a"], gs["p"], gs["phi"], gs["b"],
+                      lam0.reshape(-1)[qd].reshape(1, 1, -1).cpu(),
+                      eta0.reshape(-1)[qd].reshape(1, 1, -1).cpu())
+    rep = compare(_gather(lam, D, q).cpu(), _gather(eta, D, q).cpu(), *ref)
+    _say("long single sequence: %s" % rep)
+    assert_parity(rep, TOL_F32, "long single sequence")
+    assert max(rep["lam_max_rel"], rep["eta_max_scaled"]) <= TOL_REGRESSION, rep
+    assert bool(torch.isfinite(lam).all()) and bool(torch.isfinite(eta).all())
+    del g, lam, eta
+    torch.cuda.empty_cache()
+
+
 SHAPES = [
     # (B, H, T, D, gates, dtype)
     (1, 1, 1, 1, "std", "f32"),          # a single token, a single channel

@@ -179,7 +179,7 @@ bool mixer_bwd_layout(int64_t B, int64_t H, int64_t T, int64_t D, const kla_dtyp
                       MixerBwdLayout* l) {
     if (!kla::make_plan(B, H, T, D, fwd_rows(dt, true), kla::kFwdWaves, kla::kFwdMatrixWords,
                         kla::kFwdStateWords, &l->fwd) ||
-        !kla::make_plan(B, H, T, D, kla::kMixBwdRows, kla::kMixBwdWaves, kla::kBwdMatrixWords,
+        !kla::make_plan(B, H, T, D, kla::kMixBwdRows, kla::state_bwd_waves(T), kla::kBwdMatrixWords,
                         kla::kBwdStateWords, &l->bwd))
         return false;
     const size_t states = align256(mixer_states_bytes(l->fwd, T));
@@ -197,7 +197,7 @@ bool scan_bwd_states_layout(int64_t B, int64_t H, int64_t T, int64_t D, const kl
     const kla::FwdTile tile = scan_tile(dt, T);
     if (!kla::make_plan(B, H, T, D, tile.rows, tile.waves, kla::kFwdMatrixWords,
                         kla::kFwdStateWords, &l->fwd) ||
-        !kla::make_plan(B, H, T, D, kla::kMixBwdRows, kla::kMixBwdWaves, kla::kBwdMatrixWords,
+        !kla::make_plan(B, H, T, D, kla::kMixBwdRows, kla::state_bwd_waves(T), kla::kBwdMatrixWords,
                         kla::kBwdStateWords, &l->bwd))
         return false;
     l->off_bstate = align256(l->fwd.ws.bytes > l->bwd.ws.bytes ? l->fwd.ws.bytes : l->bwd.ws.bytes);
@@ -405,7 +405,7 @@ kla_status kla_mixer_bwd(const void* k, const void* v, const void* lam_v, const 
                          int64_t D, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     Plan pl;
     bool empty = false;
-    kla_status st = common_checks(B, H, T, D, in_dtype, kla::kMixBwdRows, kla::kMixBwdWaves,
+    kla_status st = common_checks(B, H, T, D, in_dtype, kla::kMixBwdRows, kla::state_bwd_waves(T),
                                   kla::kBwdMatrixWords, kla::kBwdStateWords, &pl, &empty);
     if (st != KLA_OK || empty) return st;
     MixerBwdLayout lay;
@@ -506,6 +506,7 @@ kla_status kla_mixer_bwd(const void* k, const void* v, const void* lam_v, const 
     ba.g_lam0 = g_lam0;
     ba.g_eta0 = g_eta0;
     ba.partial = reinterpret_cast<double*>(ws + lay.off_partial);
+    ba.waves = kla::state_bwd_waves(T);
     ba.T = T;
     ba.D = D;
     ba.C = lay.bwd.C;
@@ -699,7 +700,7 @@ kla_status kla_scan_bwd_states(const void* a, const void* p, const void* phi, co
                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
     Plan pl;
     bool empty = false;
-    kla_status st = common_checks(B, H, T, D, in_dtype, kla::kMixBwdRows, kla::kMixBwdWaves,
+    kla_status st = common_checks(B, H, T, D, in_dtype, kla::kMixBwdRows, kla::state_bwd_waves(T),
                                   kla::kBwdMatrixWords, kla::kBwdStateWords, &pl, &empty);
     if (st != KLA_OK || empty) return st;
     MixerBwdLayout lay;
@@ -793,6 +794,7 @@ kla_status kla_scan_bwd_states(const void* a, const void* p, const void* phi, co
     ba.out[3] = g_b;
     ba.g_lam0 = g_lam0;
     ba.g_eta0 = g_eta0;
+    ba.waves = kla::state_bwd_waves(T);
     ba.T = T;
     ba.D = D;
     ba.C = lay.bwd.C;

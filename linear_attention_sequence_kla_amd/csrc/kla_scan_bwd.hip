@@ -121,6 +121,15 @@ __device__ inline float load_f32(const char* base, uint32_t off) {
     return __builtin_nontemporal_load(reinterpret_cast<const float*>(base + off));
 }
 
+// A row of an optional float32 tensor: always loaded (from a stand-in of the
+// same shape when the tensor is absent) and ANDed with `mask` (all ones, or
+// zero for an absent tensor).  A load under a branch instead makes the
+// compiler wait for every load in flight where the branch rejoins, which
+// serialises a wave's row loads one row at a time.
+__device__ inline float masked_f32(const char* base, uint32_t off, uint32_t mask) {
+    return __uint_as_float(__float_as_uint(load_f32(base, off)) & mask);
+}
+
 // The carry exchange of a tile, run after its waves' maps are in s_adj.
 // Waves 1..W-2 each store the map from the tile's carry to their own in
 // s_suf[w] (the last wave's is the identity).  Wave 0 stores its own such
@@ -216,8 +225,12 @@ __global__ __launch_bounds__(W * kWave) void kla_scan_bwd_kernel(BwdArgs g) {
         const uint32_t f_off = lm.lane_el * uint32_t(sizeof(float));
         const char* pa = static_cast<const char*>(g.a) + lm.e0 * int64_t(sizeof(In));
         const char* pp = static_cast<const char*>(g.p) + lm.e0 * int64_t(sizeof(In));
-        const char* pgl = reinterpret_cast<const char*>(g.g_lam) + lm.e0 * 4;
-        const char* pge = reinterpret_cast<const char*>(g.g_eta) + lm.e0 * 4;
+        // optional upstream gradients: a NULL one is read from a stand-in of
+        // the same shape (the g_phi output) and masked to zero (branch-free
+        // loads; see masked_f32)
+        const char* pgl = reinterpret_cast<const char*>(g.g_lam ? g.g_lam : g.g_phi) + lm.e0 * 4;
+        const char* pge = reinterpret_cast<const char*>(g.g_eta ? g.g_eta : g.g_phi) + lm.e0 * 4;
+        const uint32_t ml = g.g_lam ? ~0u : 0u, me = g.g_eta ? ~0u : 0u;
         // saved states lam_{t-1}, eta_{t-1}: row t0 + i - 1; sh = 1 when the
         // wave starts the sequence (its row 0 takes lam0, eta0 instead)
         const int sh = t0 > 0 ? 0 : 1;
@@ -240,8 +253,8 @@ __global__ __launch_bounds__(W * kWave) void kla_scan_bwd_kernel(BwdArgs g) {
                     rl[i] = g.lam0 ? g.lam0[lm.qc] : 1.0f;
                     re[i] = g.eta0 ? g.eta0[lm.qc] : 0.0f;
                 }
-                rgl[i] = g.g_lam ? load_f32(pgl, f_off + uint32_t(ri) * f_row) : 0.0f;
-                rge[i] = g.g_eta ? load_f32(pge, f_off + uint32_t(ri) * f_row) : 0.0f;
+                rgl[i] = masked_f32(pgl, f_off + uint32_t(ri) * f_row, ml);
+                rge[i] = masked_f32(pge, f_off + uint32_t(ri) * f_row, me);
             }
         } else {
 #pragma unroll
@@ -404,8 +417,12 @@ void kla_state_bwd_kernel(StateBwdArgs g) {
         const char* p1 = static_cast<const char*>(g.in[1]) + in_base;
         const char* p2 = static_cast<const char*>(g.in[2]) + in_base;
         const char* p3 = static_cast<const char*>(g.in[3]) + in_base;
-        const char* pg0 = reinterpret_cast<const char*>(g.g0) + lm.e0 * 4;
-        const char* pg1 = reinterpret_cast<const char*>(g.g1) + lm.e0 * 4;
+        // optional upstream gradients: a NULL one is read from a stand-in of
+        // the same shape (the first output) and masked to zero (branch-free
+        // loads; see masked_f32)
+        const char* pg0 = reinterpret_cast<const char*>(g.g0 ? g.g0 : g.out[0]) + lm.e0 * 4;
+        const char* pg1 = reinterpret_cast<const char*>(g.g1 ? g.g1 : g.out[0]) + lm.e0 * 4;
+        const uint32_t m0 = g.g0 ? ~0u : 0u, m1 = g.g1 ? ~0u : 0u;
         double ac = 0.0, pc = 0.0;
         if constexpr (kMix) {
             const int64_t hd = lm.qc % g.HD;
@@ -438,8 +455,8 @@ void kla_state_bwd_kernel(StateBwdArgs g) {
                 r1[i] = load_gate<In>(p1, io);
                 r2[i] = load_gate<In>(p2, io);
                 r3[i] = load_gate<In>(p3, io);
-                rg0[i] = g.g0 ? load_f32(pg0, fo) : 0.0f;
-                rg1[i] = g.g1 ? load_f32(pg1, fo) : 0.0f;
+                rg0[i] = masked_f32(pg0, fo, m0);
+                rg1[i] = masked_f32(pg1, fo, m1);
             }
         } else {
 #pragma unroll
@@ -687,23 +704,28 @@ hipError_t launch_scan_bwd(const BwdArgs& args, kla_dtype dtype, hipStream_t str
     return hipGetLastError();
 }
 
-template <StateBwdMode M>
+template <int W, StateBwdMode M>
 void launch_state(const StateBwdArgs& args, kla_dtype dtype, hipStream_t stream) {
-    const dim3 grid(unsigned(args.n_tiles)), block(kMixBwdWaves * kWave);
+    const dim3 grid(unsigned(args.n_tiles)), block(W * kWave);
     if (dtype == KLA_DTYPE_F32)
-        hipLaunchKernelGGL((kla_state_bwd_kernel<float, kMixBwdRows, kMixBwdWaves, M>), grid,
-                           block, 0, stream, args);
+        hipLaunchKernelGGL((kla_state_bwd_kernel<float, kMixBwdRows, W, M>), grid, block, 0,
+                           stream, args);
     else
-        hipLaunchKernelGGL((kla_state_bwd_kernel<uint16_t, kMixBwdRows, kMixBwdWaves, M>), grid,
-                           block, 0, stream, args);
+        hipLaunchKernelGGL((kla_state_bwd_kernel<uint16_t, kMixBwdRows, W, M>), grid, block, 0,
+                           stream, args);
 }
 
 hipError_t launch_state_bwd(const StateBwdArgs& args, kla_dtype dtype, StateBwdMode mode,
                             hipStream_t stream) {
-    if (mode == StateBwdMode::kMixer)
-        launch_state<StateBwdMode::kMixer>(args, dtype, stream);
+    const bool tall = args.waves == 8;
+    if (mode == StateBwdMode::kMixer && tall)
+        launch_state<8, StateBwdMode::kMixer>(args, dtype, stream);
+    else if (mode == StateBwdMode::kMixer)
+        launch_state<4, StateBwdMode::kMixer>(args, dtype, stream);
+    else if (tall)
+        launch_state<8, StateBwdMode::kScan>(args, dtype, stream);
     else
-        launch_state<StateBwdMode::kScan>(args, dtype, stream);
+        launch_state<4, StateBwdMode::kScan>(args, dtype, stream);
     return hipGetLastError();
 }
 

@@ -259,6 +259,11 @@ STATE_SHAPES = SHAPES + [
     (2, 1, 65, 9, "std", "f32"),        # one row into a second tile
     (1, 3, 129, 40, "hard", "f32"),
     (4, 2, 600, 32, "hard", "f32"),     # hard gates: lam overflows float32 in places
+    (2, 1, 32, 9, "std", "f32"),        # exactly one short-sequence tile (8 rows x 4 waves)
+    (2, 1, 33, 9, "hard", "bf16"),      # one row into a second one
+    (1, 1, 8191, 5, "slow", "f32"),     # the longest sequence with 4-wave tiles
+    (1, 2, 8192, 70, "hard", "f32"),    # the first with 8-wave tiles
+    (1, 1, 8200, 64, "std", "bf16"),
 ]
 
 

@@ -469,8 +469,10 @@ void kla_state_bwd_kernel(StateBwdArgs g) {
         // upstream gradients for the scan), g_q for the mixer; and the wave's
         // map, the per-token adjoint maps multiplied in time order ----
         // rl[i], re[i]: the state after row i, kept for the reverse pass
-        // (which takes the state before row 0 from l_in, e_in).
-        S rl[L], re[L];
+        // (which takes the state before row 0 from l_in, e_in); rdv[i]: row
+        // i's 1 / (a^2 + p lam_{i-1}), kept too, so that the reverse pass
+        // takes no reciprocal (about 2% faster).
+        S rl[L], re[L], rdv[L];
         float rgl[L], rge[L];
         Adj m{1.0, 0.0, 0.0, 1.0, 0.0, 1.0};
         {
@@ -480,11 +482,11 @@ void kla_state_bwd_kernel(StateBwdArgs g) {
                 if (i < nr) {
                     double a, p, ph, bb;
                     if constexpr (kMix) {
-                        const double k = r0[i], lv = r2[i];
+                        const double k = r0[i], kl = k * double(r2[i]);
                         a = ac;
                         p = pc;
-                        ph = k * k * lv;
-                        bb = k * lv * double(r1[i]);
+                        ph = kl * k;
+                        bb = kl * double(r1[i]);
                     } else {
                         a = r0[i];
                         p = r1[i];
@@ -495,6 +497,7 @@ void kla_state_bwd_kernel(StateBwdArgs g) {
                     const double f = a * rd;
                     const double lt = fma(lp, rd, ph);
                     const double et = fma(f, ep, bb);
+                    rdv[i] = S(rd);
                     if constexpr (kMix) {
                         const double rlt = recip(lt);
                         const double go = rg0[i], gq = go * double(r3[i]);
@@ -527,6 +530,7 @@ void kla_state_bwd_kernel(StateBwdArgs g) {
                 } else {
                     rl[i] = S(1.0);
                     re[i] = S(0.0);
+                    rdv[i] = S(1.0);
                     rgl[i] = rge[i] = 0.0f;
                 }
                 if ((i % kRenormEvery) == kRenormEvery - 1 || i == L - 1) renorm(m);
@@ -536,7 +540,7 @@ void kla_state_bwd_kernel(StateBwdArgs g) {
 #pragma unroll
         for (int i = 0; i < L; ++i) {
             asm volatile("" : "+v"(r0[i]), "+v"(r1[i]), "+v"(rl[i]), "+v"(re[i]), "+v"(rgl[i]),
-                         "+v"(rge[i]));
+                         "+v"(rge[i]), "+v"(rdv[i]));
             if constexpr (kMix) asm volatile("" : "+v"(r2[i]));
         }
         asm volatile("" : "+v"(l_in), "+v"(e_in));
@@ -568,22 +572,27 @@ void kla_state_bwd_kernel(StateBwdArgs g) {
                 const double ep = i ? double(re[i - 1]) : e_in;
                 const double a = kMix ? ac : double(r0[i]);
                 const double p = kMix ? pc : double(r1[i]);
-                const double rd = recip(fma(p, lp, a * a));
+                const double rd = double(rdv[i]);
                 const double rd2 = rd * rd;
-                const double f = a * rd;
                 const double Lam = double(rgl[i]) + cl;
                 const double Eta = double(rge[i]) + ce;
-                const double ga = (Lam * (-2.0 * a * lp) + Eta * ep * fma(p, lp, -a * a)) * rd2;
-                const double gp = -lp * (Lam * lp + Eta * a * ep) * rd2;
+                // with d = a^2 + p lp (rd = 1 / d): d lam/da = -2 a lp / d^2,
+                // d eta/da = ep (p lp - a^2) / d^2, d lam/dp = -lp^2 / d^2,
+                // d eta/dp = -a lp ep / d^2; to the state before the row:
+                // d lam/d lp = a^2 / d^2, d eta/d lp = -p a ep / d^2,
+                // d eta/d ep = a / d
+                const double E = Eta * ep;
+                const double ga = rd2 * fma(E, fma(p, lp, -a * a), -2.0 * a * lp * Lam);
+                const double gp = -(lp * rd2) * fma(Lam, lp, a * E);
                 if (lm.valid) {
                     const uint32_t off = f_off + uint32_t(i) * f_row;
                     if constexpr (kMix) {
-                        const double k = r0[i], vv = r1[i], lv = r2[i];
-                        __builtin_nontemporal_store(float(fma(Lam * 2.0 * k, lv, Eta * lv * vv)),
+                        const double k = r0[i], lv = r2[i], ev = Eta * double(r1[i]);
+                        __builtin_nontemporal_store(float(lv * fma(Lam + Lam, k, ev)),
                                                     reinterpret_cast<float*>(o0 + off));
                         __builtin_nontemporal_store(float(Eta * k * lv),
                                                     reinterpret_cast<float*>(o1 + off));
-                        __builtin_nontemporal_store(float(fma(Lam * k, k, Eta * k * vv)),
+                        __builtin_nontemporal_store(float(k * fma(Lam, k, ev)),
                                                     reinterpret_cast<float*>(o2 + off));
                     } else {
                         __builtin_nontemporal_store(float(ga), reinterpret_cast<float*>(o0 + off));
@@ -596,8 +605,8 @@ void kla_state_bwd_kernel(StateBwdArgs g) {
                     sa += ga;
                     sp += gp;
                 }
-                cl = fma(f * f, Lam, -p * f * ep * rd * Eta);
-                ce = f * Eta;
+                cl = (a * rd2) * fma(a, Lam, -p * E);
+                ce = (a * rd) * Eta;
             }
             if (t0 == 0 && lm.valid) {
                 if (g.g_lam0) g.g_lam0[lm.q] = float(cl);

@@ -169,11 +169,11 @@ template <Mode M>
 __device__ inline void token_gates(float x0, float x1, float x2, float x3, double ac, double pc,
                                    double fc, double& a, double& p, double& ph, double& b) {
     if constexpr (M == Mode::Mixer || M == Mode::MixerState || M == Mode::MixerTrain) {
-        const double k = x0, lv = x2;
+        const double k = x0, kl = k * double(x2);
         a = ac;
         p = pc;
-        ph = k * k * lv;
-        b = k * lv * double(x1);
+        ph = kl * k;
+        b = kl * double(x1);
     } else if constexpr (M == Mode::Lti) {
         a = ac;
         p = pc;

@@ -94,6 +94,19 @@ def merge_reports(reps) -> dict:
     return out
 
 
+_COUNT_KEYS = _SUM_KEYS + ("zero_q_nonzero_out",)
+
+
+def merge_any(reps) -> dict:
+    """merge_reports for any of the reports of this module (compare_mixer's,
+    compare_grads'): count keys add, every other key takes the largest."""
+    out: dict = {}
+    for r in reps:
+        for k, v in r.items():
+            out[k] = out.get(k, 0) + v if k in _COUNT_KEYS else max(out.get(k, 0.0), v)
+    return out
+
+
 def assert_parity(rep: dict, tol: float, what: str = ""):
     msg = "%s %r" % (what, rep)
     assert rep["nan"] == 0, msg

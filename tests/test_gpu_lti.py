@@ -11,7 +11,7 @@ import torch
 
 from kla_inputs import (LTI_WORKLOADS, broadcast_lti, make_initial_state, make_lti_inputs,
                         make_lti_workload)
-from kla_metric import TOL_BF16, TOL_F32, assert_parity, compare
+from kla_metric import TOL_BF16, TOL_F32, TOL_REGRESSION, assert_parity, compare, merge_reports
 from oracle import oracle_scan
 
 pytestmark = pytest.mark.gpu
@@ -81,6 +81,37 @@ def test_lti_workload_full_size_sampled(key):
         rep = compare(lam[bi:bi + 1, hi:hi + 1].cpu(), eta[bi:bi + 1, hi:hi + 1].cpu(), *ref)
         _say("slab (%d, %d): %s" % (bi, hi, rep))
         assert_parity(rep, TOL_BF16 if w.dtype == "bf16" else TOL_F32, "slab %d" % s)
+
+
+@pytest.mark.parametrize("key", [2, 3])
+def test_lti_workload_every_element(key):
+    """A full-size workload drawn on the GPU exactly as the benchmark draws it,
+    in the benchmark's launch; the oracle runs on host copies, a batch of
+    (b, h) slabs at a time with the gates of those h broadcast over time, and
+    every output element is compared."""
+    w = LTI_WORKLOADS[key]
+    _say("LTI workload %s (every element)" % w.describe())
+    g = make_lti_workload(key, device=DEV)
+    lam, eta = run_gpu(g)
+    assert health() == 0
+    B, H, T, D = w.shape
+    per = max(1, min(H, (1 << 25) // (T * D)))
+    reps = []
+    for b in range(B):
+        for h0 in range(0, H, per):
+            h1 = min(H, h0 + per)
+            sub = {n: g[n][h0:h1].cpu() for n in ("a", "p", "phi")}
+            sub["b"] = g["b"][b:b + 1, h0:h1].cpu()
+            f = broadcast_lti(sub)
+            ref = oracle_scan(f["a"], f["p"], f["phi"], f["b"], g["lam0"][b:b + 1, h0:h1].cpu(),
+                              g["eta0"][b:b + 1, h0:h1].cpu())
+            reps.append(compare(lam[b:b + 1, h0:h1].cpu(), eta[b:b + 1, h0:h1].cpu(), *ref))
+            del sub, f, ref
+    rep = merge_reports(reps)
+    _say("%s: %s" % (w.describe(), rep))
+    assert rep["n"] == w.elements
+    assert_parity(rep, TOL_BF16 if w.dtype == "bf16" else TOL_F32, w.describe())
+    assert max(rep["lam_max_rel"], rep["eta_max_scaled"]) <= TOL_REGRESSION, rep
 
 
 SHAPES = [(1, 1, 1, 1), (1, 1, 5, 3), (2, 3, 113, 7), (1, 2, 337, 64), (3, 1, 450, 65),

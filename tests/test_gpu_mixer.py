@@ -11,7 +11,8 @@ import torch
 
 from kla_inputs import (MIXER_WORKLOADS, make_initial_state, make_mixer_inputs,
                         make_mixer_workload)
-from kla_metric import TOL_BF16, TOL_F32, assert_mixer_parity, compare_mixer
+from kla_metric import (TOL_BF16, TOL_F32, TOL_REGRESSION, assert_mixer_parity, compare_mixer,
+                        merge_any)
 from oracle import oracle_mixer
 
 pytestmark = pytest.mark.gpu
@@ -104,6 +105,39 @@ def test_mixer_workload_full_size_sampled(key):
     et = eta_T.reshape(-1)[qd].cpu().double().numpy()
     assert np.max(np.abs(lt - ref["lam_T"][0, 0]) / ref["lam_T"][0, 0]) < 1e-5
     assert np.all(np.isfinite(et))
+
+
+@pytest.mark.parametrize("key", [2, 3])
+def test_mixer_workload_every_element(key):
+    """A full-size workload drawn on the GPU exactly as the benchmark draws it,
+    in the benchmark's launch; the oracle runs on host copies of the inputs,
+    a batch of (b, h) slabs at a time (the channel gates of those h), and
+    every readout and variance element is compared."""
+    w = MIXER_WORKLOADS[key]
+    _say("mixer workload %s (every element)" % w.describe())
+    g = make_mixer_workload(key, device=DEV)
+    out, var, _, _ = run_gpu(g)
+    assert health() == 0
+    B, H, T, D = w.shape
+    per = max(1, min(H, (1 << 25) // (T * D)))
+    reps = []
+    for b in range(B):
+        for h0 in range(0, H, per):
+            h1 = min(H, h0 + per)
+            host = {n: g[n][b:b + 1, h0:h1].cpu() for n in TOKEN}
+            ref = oracle_mixer(*(host[n] for n in TOKEN), g["a"][h0:h1].cpu(),
+                               g["p"][h0:h1].cpu(), g["lam0"][b:b + 1, h0:h1].cpu(),
+                               g["eta0"][b:b + 1, h0:h1].cpu())
+            reps.append(compare_mixer(out[b:b + 1, h0:h1].cpu(), var[b:b + 1, h0:h1].cpu(),
+                                      host["q"], ref["out"], ref["var"], ref["mu_abs"]))
+            del host, ref
+    rep = merge_any(reps)
+    _say("%s: %s" % (w.describe(), rep))
+    assert rep["n"] == w.elements
+    assert_mixer_parity(rep, TOL_BF16 if w.dtype == "bf16" else TOL_F32, w.describe())
+    # float64 arithmetic on the very values the oracle reads: only the final
+    # float32 rounding remains
+    assert max(rep["out_max_scaled"], rep["var_max_rel"]) <= TOL_REGRESSION, rep
 
 
 SHAPES = [

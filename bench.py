@@ -30,6 +30,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -251,44 +253,90 @@ def workloads_for(direction: str):
             "lti": LTI_WORKLOADS}.get(direction, WORKLOADS)
 
 
-def cpu_baseline(w, g_dev, budget_s: float = 10.0):
-    """Times the float64 oracle on the host on a bounded sample of the
-    workload (whole slabs, full T), scaled to elements per second."""
-    from oracle import oracle_scan, oracle_threads
+def cpu_baseline(w, g_dev, direction: str = "fwd", budget_s: float = 10.0):
+    """Times the float64 oracle of a direction on the host, on a bounded sample
+    of the workload (its leading (b, h) slabs with every channel and the full
+    sequence; every channel for the decode steps), scaled to the direction's
+    unit.  The backward and training-step directions time the backward
+    oracle, which runs the forward recursion and then the adjoint one."""
+    from oracle import (oracle_mixer, oracle_mixer_bwd, oracle_scan, oracle_scan_bwd,
+                        oracle_threads)
+    d = direction
     threads = len(os.sched_getaffinity(0))
     used = oracle_threads(threads)
-    # Sample: leading slabs (b, h) with every channel and the full sequence.
-    slabs_total = w.B * w.H
-    per_slab = w.T * w.D
-    n_slabs = max(1, min(slabs_total, int(2e8 // max(per_slab, 1))))
-    sel = {}
-    for k in ("a", "p", "phi", "b"):
-        x = g_dev[k].reshape(slabs_total, w.T, w.D)[:n_slabs]
-        sel[k] = x.to("cpu").double().numpy().reshape(1, n_slabs, w.T, w.D)
-    lam0 = g_dev["lam0"].reshape(slabs_total, w.D)[:n_slabs].cpu().double().numpy()
-    eta0 = g_dev["eta0"].reshape(slabs_total, w.D)[:n_slabs].cpu().double().numpy()
-    lam0 = lam0.reshape(1, n_slabs, w.D)
-    eta0 = eta0.reshape(1, n_slabs, w.D)
-    elems = n_slabs * per_slab
+    decoding = d in ("decode", "mixer_decode")
+    S, T = w.B * w.H, (1 if decoding else w.T)
+    per_slab = T * w.D
+    # about 10 s of oracle work at its rate on the box's host cores
+    cap = 2e8 if d in ("fwd", "lti", "mixer") else 5e7
+    n = S if decoding else max(1, min(S, int(cap // max(per_slab, 1))))
+    heads = np.arange(n) % w.H  # slab s is (b, h) = divmod(s, H)
+
+    def tok(name):  # the sampled slabs of a [B, H, T, D] input, [1, n, T, D] float64
+        return (g_dev[name].reshape(S, T, w.D)[:n].to("cpu").double().numpy()
+                .reshape(1, n, T, w.D))
+
+    def head(name):  # a per-(h, d) input for the sampled slabs, [n, D]
+        return np.ascontiguousarray(g_dev[name].to("cpu").double().numpy()[heads])
+
+    def init(name):  # the sampled slabs' initial state, [1, n, D], or None (1 and 0)
+        x = g_dev.get(name)
+        return None if x is None else (x.reshape(S, w.D)[:n].to("cpu").double().numpy()
+                                       .reshape(1, n, w.D))
+
+    def cut(x, sl):
+        return None if x is None else x[:, sl]
+
+    lam0, eta0 = init("lam0"), init("eta0")
+    if d in ("mixer", "mixer_decode", "mixer_bwd", "mixer_train"):
+        tokens = [tok(k) for k in ("k", "v", "lam_v", "q")]
+        a, p = head("a"), head("p")
+        if d in ("mixer_bwd", "mixer_train"):
+            go, gv = tok("g_out"), tok("g_var")
+
+            def run(sl, nt):
+                oracle_mixer_bwd(*(t[:, sl] for t in tokens), a[sl], p[sl], cut(lam0, sl),
+                                 cut(eta0, sl), go[:, sl], gv[:, sl], nthreads=nt)
+        else:
+            def run(sl, nt):
+                oracle_mixer(*(t[:, sl] for t in tokens), a[sl], p[sl], cut(lam0, sl),
+                             cut(eta0, sl), nthreads=nt)
+    else:
+        if d == "lti":  # the channel gates broadcast over the sequence, as the oracle reads them
+            b = tok("b")
+            gates = [np.ascontiguousarray(np.broadcast_to(head(k)[None, :, None, :], b.shape))
+                     for k in ("a", "p", "phi")] + [b]
+        else:
+            gates = [tok(k) for k in ("a", "p", "phi", "b")]
+        if d in ("bwd", "bwd_states", "scan_train"):
+            gl, ge = tok("g_lam"), tok("g_eta")
+
+            def run(sl, nt):
+                oracle_scan_bwd(*(t[:, sl] for t in gates), cut(lam0, sl), cut(eta0, sl),
+                                gl[:, sl], ge[:, sl], nthreads=nt)
+        else:
+            def run(sl, nt):
+                oracle_scan(*(t[:, sl] for t in gates), cut(lam0, sl), cut(eta0, sl),
+                            nthreads=nt)
+
     reps, t_total = 0, 0.0
     while t_total < budget_s and reps < 100000:
         t0 = time.perf_counter()
-        oracle_scan(sel["a"], sel["p"], sel["phi"], sel["b"], lam0, eta0, nthreads=used)
+        run(slice(0, n), used)
         t_total += time.perf_counter() - t0
         reps += 1
     # one thread, on one slab
-    one = {k: v[:, :1] for k, v in sel.items()}
     reps1, t1 = 0, 0.0
     while t1 < budget_s / 4 and reps1 < 100000:
         t0 = time.perf_counter()
-        oracle_scan(one["a"], one["p"], one["phi"], one["b"], lam0[:, :1], eta0[:, :1],
-                    nthreads=1)
+        run(slice(0, 1), 1)
         t1 += time.perf_counter() - t0
         reps1 += 1
-    return {"value": elems * reps / t_total, "unit": "elements/sec", "cores": used,
+    what = "one token" if decoding else "full T=%d" % w.T
+    return {"value": n * per_slab * reps / t_total, "unit": "elements/sec", "cores": used,
             "kind": "oracle",
-            "sample": "%d of %d slabs (all %d channels, full T=%d), %d runs, %.1f s"
-                      % (n_slabs, slabs_total, w.D, w.T, reps, t_total),
+            "sample": "%d of %d slabs (all %d channels, %s), %d runs, %.1f s"
+                      % (n, S, w.D, what, reps, t_total),
             "value_1thread": per_slab * reps1 / t1,
             "sample_1thread": "1 slab, %d runs, %.1f s, 1 thread" % (reps1, t1)}
 
@@ -602,8 +650,8 @@ def main(argv=None):
         for key in args.per_config:
             if key != args.workload:
                 rec["per_config"].append(per_config_entry(run_one(key), d))
-    if not args.no_cpu_baseline and d == "fwd":
-        rec["cpu_baseline"] = cpu_baseline(w, m["first_set"])
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, m["first_set"], d)
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -107,3 +107,33 @@ def test_summarize_counters_arithmetic(tmp_path, monkeypatch):
     assert bench.load_traffic(1, "fwd") == pytest.approx(rec["hbm_bytes_per_launch"])
     md = open(tmp_path / "profiles" / "kla_scan_kernel_small-lm-layer.md").read()
     assert "cmd" in md and "80000" in md
+
+
+@pytest.mark.parametrize("direction", ["fwd", "bwd", "bwd_states", "scan_train", "lti", "mixer",
+                                       "mixer_bwd", "mixer_train", "decode", "mixer_decode"])
+def test_cpu_baseline_every_direction(direction):
+    """The oracle timing of every bench direction runs on the tiny workload's
+    inputs as the bench builds them (host tensors here), with a short budget,
+    and reports a positive rate over the whole sample and on one thread."""
+    import torch
+    from kla_inputs import (make_gates, make_lti_workload, make_mixer_inputs,
+                            make_mixer_workload, make_workload)
+    w = bench.workloads_for(direction)[0]
+    if direction in ("mixer", "mixer_bwd", "mixer_train"):
+        g = make_mixer_workload(0)
+        g["g_out"], g["g_var"] = torch.randn(w.shape), torch.randn(w.shape)
+    elif direction == "lti":
+        g = make_lti_workload(0)
+    elif direction == "decode":
+        g = {n: v[:, :, 0].contiguous()
+             for n, v in make_gates((w.B, w.H, 1, w.D), w.gates, w.dtype, 1).items()}
+    elif direction == "mixer_decode":
+        g = {n: (v[:, :, 0] if v.dim() == 4 else v).contiguous()
+             for n, v in make_mixer_inputs((w.B, w.H, 1, w.D), w.dtype, 1).items()}
+    else:
+        g = make_workload(0)
+        g["g_lam"], g["g_eta"] = torch.randn(w.shape), torch.randn(w.shape)
+    rec = bench.cpu_baseline(w, g, direction, budget_s=0.05)
+    assert rec["kind"] == "oracle" and rec["cores"] >= 1
+    assert rec["value"] > 0 and rec["value_1thread"] > 0
+    assert ("one token" in rec["sample"]) == direction.endswith("decode")

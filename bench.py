@@ -267,9 +267,10 @@ def cpu_baseline(w, g_dev, direction: str = "fwd", budget_s: float = 10.0):
     decoding = d in ("decode", "mixer_decode")
     S, T = w.B * w.H, (1 if decoding else w.T)
     per_slab = T * w.D
-    # about 10 s of oracle work at its rate on the machine's host cores
+    # about 10 s of oracle work at its rate on the machine's host cores, and at
+    # least one slab per thread (the oracle runs its slabs in parallel)
     cap = 2e8 if d in ("fwd", "lti", "mixer") else 5e7
-    n = S if decoding else max(1, min(S, int(cap // max(per_slab, 1))))
+    n = S if decoding else max(1, min(S, max(used, int(cap // max(per_slab, 1)))))
     heads = np.arange(n) % w.H  # slab s is (b, h) = divmod(s, H)
 
     def tok(name):  # the sampled slabs of a [B, H, T, D] input, [1, n, T, D] float64

@@ -322,11 +322,13 @@ __global__ __launch_bounds__(W * kWave) void kla_scan_bwd_kernel(BwdArgs g) {
                 const double a = ra[i], p = rp[i], lp = rl[i], ep = re[i];
                 const double rd = recip(fma(p, lp, a * a));
                 const double rd2 = rd * rd;
-                const double f = a * rd;
                 const double Lam = double(rgl[i]) + cl;
                 const double Eta = double(rge[i]) + ce;
-                const double ga = (Lam * (-2.0 * a * lp) + Eta * ep * fma(p, lp, -a * a)) * rd2;
-                const double gp = -lp * (Lam * lp + Eta * a * ep) * rd2;
+                // d = a^2 + p lp, rd = 1 / d; the derivatives are listed in
+                // kla_state_bwd_kernel below
+                const double E = Eta * ep;
+                const double ga = rd2 * fma(E, fma(p, lp, -a * a), -2.0 * a * lp * Lam);
+                const double gp = -(lp * rd2) * fma(Lam, lp, a * E);
                 if (lm.valid) {
                     const uint32_t off = f_off + uint32_t(i) * f_row;
                     __builtin_nontemporal_store(float(ga), reinterpret_cast<float*>(oa + off));
@@ -334,8 +336,8 @@ __global__ __launch_bounds__(W * kWave) void kla_scan_bwd_kernel(BwdArgs g) {
                     __builtin_nontemporal_store(float(Lam), reinterpret_cast<float*>(of + off));
                     __builtin_nontemporal_store(float(Eta), reinterpret_cast<float*>(ob + off));
                 }
-                cl = fma(f * f, Lam, -p * f * ep * rd * Eta);
-                ce = f * Eta;
+                cl = (a * rd2) * fma(a, Lam, -p * E);
+                ce = (a * rd) * Eta;
             }
             if (t0 == 0 && lm.valid) {
                 if (g.g_lam0) g.g_lam0[lm.q] = float(cl);

@@ -104,6 +104,11 @@ int fwd_rows(const kla_dtype& d, bool mixer) {
 }
 // The forward kernel's tile in the scan modes for this problem (the 4-wave
 // float32 tile for an unknown dtype, which common_checks then rejects).
+// Waves per tile of the backward kernel from states (4 for an unknown dtype,
+// which common_checks then rejects).
+int state_bwd_waves(const kla_dtype& d, int64_t T) {
+    return known_dtype(d) ? kla::state_bwd_waves(d, T) : 4;
+}
 kla::FwdTile scan_tile(const kla_dtype& d, int64_t T) {
     return known_dtype(d) ? kla::scan_tile(d, T) : kla::FwdTile{kla::kFwdRows, kla::kFwdWaves};
 }
@@ -179,7 +184,7 @@ bool mixer_bwd_layout(int64_t B, int64_t H, int64_t T, int64_t D, const kla_dtyp
                       MixerBwdLayout* l) {
     if (!kla::make_plan(B, H, T, D, fwd_rows(dt, true), kla::kFwdWaves, kla::kFwdMatrixWords,
                         kla::kFwdStateWords, &l->fwd) ||
-        !kla::make_plan(B, H, T, D, kla::kMixBwdRows, kla::state_bwd_waves(T), kla::kBwdMatrixWords,
+        !kla::make_plan(B, H, T, D, kla::kMixBwdRows, state_bwd_waves(dt, T), kla::kBwdMatrixWords,
                         kla::kBwdStateWords, &l->bwd))
         return false;
     const size_t states = align256(mixer_states_bytes(l->fwd, T));
@@ -197,7 +202,7 @@ bool scan_bwd_states_layout(int64_t B, int64_t H, int64_t T, int64_t D, const kl
     const kla::FwdTile tile = scan_tile(dt, T);
     if (!kla::make_plan(B, H, T, D, tile.rows, tile.waves, kla::kFwdMatrixWords,
                         kla::kFwdStateWords, &l->fwd) ||
-        !kla::make_plan(B, H, T, D, kla::kMixBwdRows, kla::state_bwd_waves(T), kla::kBwdMatrixWords,
+        !kla::make_plan(B, H, T, D, kla::kMixBwdRows, state_bwd_waves(dt, T), kla::kBwdMatrixWords,
                         kla::kBwdStateWords, &l->bwd))
         return false;
     l->off_bstate = align256(l->fwd.ws.bytes > l->bwd.ws.bytes ? l->fwd.ws.bytes : l->bwd.ws.bytes);
@@ -405,7 +410,7 @@ kla_status kla_mixer_bwd(const void* k, const void* v, const void* lam_v, const 
                          int64_t D, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     Plan pl;
     bool empty = false;
-    kla_status st = common_checks(B, H, T, D, in_dtype, kla::kMixBwdRows, kla::state_bwd_waves(T),
+    kla_status st = common_checks(B, H, T, D, in_dtype, kla::kMixBwdRows, state_bwd_waves(in_dtype, T),
                                   kla::kBwdMatrixWords, kla::kBwdStateWords, &pl, &empty);
     if (st != KLA_OK || empty) return st;
     MixerBwdLayout lay;
@@ -506,7 +511,7 @@ kla_status kla_mixer_bwd(const void* k, const void* v, const void* lam_v, const 
     ba.g_lam0 = g_lam0;
     ba.g_eta0 = g_eta0;
     ba.partial = reinterpret_cast<double*>(ws + lay.off_partial);
-    ba.waves = kla::state_bwd_waves(T);
+    ba.waves = state_bwd_waves(in_dtype, T);
     ba.T = T;
     ba.D = D;
     ba.C = lay.bwd.C;
@@ -700,7 +705,7 @@ kla_status kla_scan_bwd_states(const void* a, const void* p, const void* phi, co
                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
     Plan pl;
     bool empty = false;
-    kla_status st = common_checks(B, H, T, D, in_dtype, kla::kMixBwdRows, kla::state_bwd_waves(T),
+    kla_status st = common_checks(B, H, T, D, in_dtype, kla::kMixBwdRows, state_bwd_waves(in_dtype, T),
                                   kla::kBwdMatrixWords, kla::kBwdStateWords, &pl, &empty);
     if (st != KLA_OK || empty) return st;
     MixerBwdLayout lay;
@@ -794,7 +799,7 @@ kla_status kla_scan_bwd_states(const void* a, const void* p, const void* phi, co
     ba.out[3] = g_b;
     ba.g_lam0 = g_lam0;
     ba.g_eta0 = g_eta0;
-    ba.waves = kla::state_bwd_waves(T);
+    ba.waves = state_bwd_waves(in_dtype, T);
     ba.T = T;
     ba.D = D;
     ba.C = lay.bwd.C;

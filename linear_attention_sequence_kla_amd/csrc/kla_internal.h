@@ -106,11 +106,17 @@ inline FwdTile scan_tile(kla_dtype dt, int64_t T) {
 constexpr int kLtiRows = 64, kLtiWaves = 4;
 constexpr int kMixBwdRows = 8;
 // Waves per workgroup of the backward kernel from states (kMixBwdRows rows
-// each): 8 (64-row tiles) from T = 8192 on, 4 (32-row tiles, four workgroups
-// per CU) below, which measured 4-10% faster on the small-LM layer
-// (T = 2048), level at T = 8192 and 4-7% slower on the long context.
+// each).  float32 inputs: 8 (64-row tiles) from T = 8192 on, 4 (32-row
+// tiles, four workgroups per CU) below, which measured 4-10% faster on the
+// small-LM layer (T = 2048), level at T = 8192 and 4-7% slower on the long
+// context.  bfloat16 inputs: always 4, since their instances fit in 96
+// registers and run 5 waves per SIMD, which only workgroups of one wave
+// per SIMD can fill (8-10% faster on the 1B-scale layer than 8 waves at 4
+// per SIMD).
 constexpr int64_t kStateBwdTallT = 8192;
-inline int state_bwd_waves(int64_t T) { return T >= kStateBwdTallT ? 8 : 4; }
+inline int state_bwd_waves(kla_dtype dt, int64_t T) {
+    return dt == KLA_DTYPE_F32 && T >= kStateBwdTallT ? 8 : 4;
+}
 constexpr int kBwdRows = 14, kBwdWaves = 8, kBwdMatrixWords = 6, kBwdStateWords = 2;
 
 // kMixerState: the mixer's gates; writes the float64 states (lam, eta) after
@@ -146,7 +152,7 @@ struct StateBwdArgs {
     float* g_lam0;  // may be NULL
     float* g_eta0;  // may be NULL
     double* partial;  // kMixer only
-    int waves;        // state_bwd_waves(T)
+    int waves;        // state_bwd_waves(dtype, T)
     int64_t T, D, C, G, n_chunks, n_tiles, HD;
     Workspace ws;
 };

@@ -227,6 +227,50 @@ __device__ inline float load_gate<uint16_t>(const char* base, uint32_t off) {
     return __uint_as_float(bits << 16);
 }
 
+// One token input of a wave's L rows, held in registers across a kernel's passes.
+// float32 values are kept as loaded; bfloat16 values stay packed, two rows
+// per register (row 2j in the low half), and widen when read, which halves
+// the registers the rows take.
+template <typename In, int L>
+struct GateRows {
+    float v[L];
+    __device__ void load(int i, const char* base, uint32_t off) {
+        v[i] = __builtin_nontemporal_load(reinterpret_cast<const float*>(base + off));
+    }
+    __device__ void set(int i, float x) { v[i] = x; }
+    __device__ float operator[](int i) const { return v[i]; }
+    // pins the values in registers: a later pass reads them there, and the
+    // compiler neither reloads nor rematerialises them
+    __device__ void keep() {
+#pragma unroll
+        for (int i = 0; i < L; ++i) asm volatile("" : "+v"(v[i]));
+    }
+};
+
+template <int L>
+struct GateRows<uint16_t, L> {
+    uint32_t v[(L + 1) / 2];
+    __device__ void put(int i, uint32_t bits) {
+        if (i & 1)
+            v[i >> 1] |= bits << 16;
+        else
+            v[i >> 1] = bits;
+    }
+    __device__ void load(int i, const char* base, uint32_t off) {
+        put(i, __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(base + off)));
+    }
+    // (x exact in bfloat16)
+    __device__ void set(int i, float x) { put(i, __float_as_uint(x) >> 16); }
+    __device__ float operator[](int i) const {
+        const uint32_t x = v[i >> 1];
+        return __uint_as_float((i & 1) ? (x & 0xffff0000u) : (x << 16));
+    }
+    __device__ void keep() {
+#pragma unroll
+        for (int i = 0; i < (L + 1) / 2; ++i) asm volatile("" : "+v"(v[i]));
+    }
+};
+
 // Lane coordinates of a tile: 64 consecutive channels q0..q0+63 of the
 // flattened (b, h, d) index, starting at time row t0.  Each lane addresses its
 // rows with a 32-bit byte offset from the wave's base element e0, so every row

@@ -387,10 +387,17 @@ template <StateBwdMode M> struct StateOf { typedef float T; };
 template <> struct StateOf<StateBwdMode::kScan> { typedef double T; };
 
 template <typename In, int L, int W, StateBwdMode M>
-__global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ __launch_bounds__(W * kWave)
+__attribute__((amdgpu_waves_per_eu(sizeof(In) == 2 ? 5 : 4)))
 void kla_state_bwd_kernel(StateBwdArgs g) {
     static_assert(L == kMixBwdRows, "the forward keeps a state every kMixBwdRows rows");
     constexpr bool kMix = M == StateBwdMode::kMixer;
+    // float32 instances keep each row's 1 / (a^2 + p lam_{t-1}) from the
+    // forward replay for the reverse pass (2% faster); bfloat16 instances
+    // recompute it, which with their rows held packed keeps them within 96
+    // registers: 5 waves per SIMD instead of 4, 8-10% faster on the
+    // 1B-scale layer.
+    constexpr bool kKeepRd = sizeof(In) == 4;
     typedef typename StateOf<M>::T S;  // the per-row states kept for the reverse pass
     __shared__ double s_adj[W][6][kWave];
     __shared__ double s_suf[W][6][kWave];  // the maps tile_carry leaves
@@ -436,7 +443,8 @@ void kla_state_bwd_kernel(StateBwdArgs g) {
         // (row t0 - 1's boundary state, or the initial state at t0 = 0)
         // mixer: r0..r3 = k, v, lam_v, q; rg0, rg1 = g_out, g_var
         // scan:  r0..r3 = a, p, phi, b;   rg0, rg1 = g_lam, g_eta
-        float r0[L], r1[L], r2[L], r3[L], rg0[L], rg1[L];
+        GateRows<In, L> r0, r1, r2, r3;
+        float rg0[L], rg1[L];
         double l_in = 1.0, e_in = 0.0;
         if (nr > 0) {
             if (t0 > 0) {
@@ -453,16 +461,22 @@ void kla_state_bwd_kernel(StateBwdArgs g) {
                 const int ri = min(i, nr - 1);
                 const uint32_t io = in_off + uint32_t(ri) * in_row;
                 const uint32_t fo = f_off + uint32_t(ri) * f_row;
-                r0[i] = load_gate<In>(p0, io);
-                r1[i] = load_gate<In>(p1, io);
-                r2[i] = load_gate<In>(p2, io);
-                r3[i] = load_gate<In>(p3, io);
+                r0.load(i, p0, io);
+                r1.load(i, p1, io);
+                r2.load(i, p2, io);
+                r3.load(i, p3, io);
                 rg0[i] = masked_f32(pg0, fo, m0);
                 rg1[i] = masked_f32(pg1, fo, m1);
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < L; ++i) r0[i] = r1[i] = r2[i] = r3[i] = rg0[i] = rg1[i] = 0.0f;
+            for (int i = 0; i < L; ++i) {
+                r0.set(i, 0.0f);
+                r1.set(i, 0.0f);
+                r2.set(i, 0.0f);
+                r3.set(i, 0.0f);
+                rg0[i] = rg1[i] = 0.0f;
+            }
         }
         if (w == 0) tag = read_tag(g.ws);
 
@@ -472,9 +486,8 @@ void kla_state_bwd_kernel(StateBwdArgs g) {
         // map, the per-token adjoint maps multiplied in time order ----
         // rl[i], re[i]: the state after row i, kept for the reverse pass
         // (which takes the state before row 0 from l_in, e_in); rdv[i]: row
-        // i's 1 / (a^2 + p lam_{i-1}), kept too, so that the reverse pass
-        // takes no reciprocal (about 2% faster).
-        S rl[L], re[L], rdv[L];
+        // i's 1 / (a^2 + p lam_{i-1}) (kKeepRd).
+        S rl[L], re[L], rdv[kKeepRd ? L : 1];
         float rgl[L], rge[L];
         Adj m{1.0, 0.0, 0.0, 1.0, 0.0, 1.0};
         {
@@ -499,7 +512,7 @@ void kla_state_bwd_kernel(StateBwdArgs g) {
                     const double f = a * rd;
                     const double lt = fma(lp, rd, ph);
                     const double et = fma(f, ep, bb);
-                    rdv[i] = S(rd);
+                    if constexpr (kKeepRd) rdv[i] = S(rd);
                     if constexpr (kMix) {
                         const double rlt = recip(lt);
                         const double go = rg0[i], gq = go * double(r3[i]);
@@ -532,7 +545,7 @@ void kla_state_bwd_kernel(StateBwdArgs g) {
                 } else {
                     rl[i] = S(1.0);
                     re[i] = S(0.0);
-                    rdv[i] = S(1.0);
+                    if constexpr (kKeepRd) rdv[i] = S(1.0);
                     rgl[i] = rge[i] = 0.0f;
                 }
                 if ((i % kRenormEvery) == kRenormEvery - 1 || i == L - 1) renorm(m);
@@ -541,10 +554,12 @@ void kla_state_bwd_kernel(StateBwdArgs g) {
         // keep the reverse pass's operands as they are (no recomputation)
 #pragma unroll
         for (int i = 0; i < L; ++i) {
-            asm volatile("" : "+v"(r0[i]), "+v"(r1[i]), "+v"(rl[i]), "+v"(re[i]), "+v"(rgl[i]),
-                         "+v"(rge[i]), "+v"(rdv[i]));
-            if constexpr (kMix) asm volatile("" : "+v"(r2[i]));
+            asm volatile("" : "+v"(rl[i]), "+v"(re[i]), "+v"(rgl[i]), "+v"(rge[i]));
+            if constexpr (kKeepRd) asm volatile("" : "+v"(rdv[i]));
         }
+        r0.keep();
+        r1.keep();
+        if constexpr (kMix) r2.keep();
         asm volatile("" : "+v"(l_in), "+v"(e_in));
         s_adj[w][0][lane] = m.u;
         s_adj[w][1][lane] = m.v;
@@ -574,7 +589,11 @@ void kla_state_bwd_kernel(StateBwdArgs g) {
                 const double ep = i ? double(re[i - 1]) : e_in;
                 const double a = kMix ? ac : double(r0[i]);
                 const double p = kMix ? pc : double(r1[i]);
-                const double rd = double(rdv[i]);
+                double rd;
+                if constexpr (kKeepRd)
+                    rd = double(rdv[i]);
+                else
+                    rd = recip(fma(p, lp, a * a));
                 const double rd2 = rd * rd;
                 const double Lam = double(rgl[i]) + cl;
                 const double Eta = double(rge[i]) + ce;
@@ -715,28 +734,28 @@ hipError_t launch_scan_bwd(const BwdArgs& args, kla_dtype dtype, hipStream_t str
     return hipGetLastError();
 }
 
-template <int W, StateBwdMode M>
-void launch_state(const StateBwdArgs& args, kla_dtype dtype, hipStream_t stream) {
+template <typename In, int W, StateBwdMode M>
+void launch_state(const StateBwdArgs& args, hipStream_t stream) {
     const dim3 grid(unsigned(args.n_tiles)), block(W * kWave);
-    if (dtype == KLA_DTYPE_F32)
-        hipLaunchKernelGGL((kla_state_bwd_kernel<float, kMixBwdRows, W, M>), grid, block, 0,
-                           stream, args);
-    else
-        hipLaunchKernelGGL((kla_state_bwd_kernel<uint16_t, kMixBwdRows, W, M>), grid, block, 0,
-                           stream, args);
+    hipLaunchKernelGGL((kla_state_bwd_kernel<In, kMixBwdRows, W, M>), grid, block, 0, stream, args);
 }
 
 hipError_t launch_state_bwd(const StateBwdArgs& args, kla_dtype dtype, StateBwdMode mode,
                             hipStream_t stream) {
-    const bool tall = args.waves == 8;
-    if (mode == StateBwdMode::kMixer && tall)
-        launch_state<8, StateBwdMode::kMixer>(args, dtype, stream);
-    else if (mode == StateBwdMode::kMixer)
-        launch_state<4, StateBwdMode::kMixer>(args, dtype, stream);
-    else if (tall)
-        launch_state<8, StateBwdMode::kScan>(args, dtype, stream);
+    const bool mix = mode == StateBwdMode::kMixer;
+    if (dtype != KLA_DTYPE_F32 && args.waves != 4) return hipErrorInvalidValue;
+    if (dtype != KLA_DTYPE_F32 && mix)  // bfloat16: 4-wave tiles only (state_bwd_waves)
+        launch_state<uint16_t, 4, StateBwdMode::kMixer>(args, stream);
+    else if (dtype != KLA_DTYPE_F32)
+        launch_state<uint16_t, 4, StateBwdMode::kScan>(args, stream);
+    else if (args.waves == 8 && mix)
+        launch_state<float, 8, StateBwdMode::kMixer>(args, stream);
+    else if (mix)
+        launch_state<float, 4, StateBwdMode::kMixer>(args, stream);
+    else if (args.waves == 8)
+        launch_state<float, 8, StateBwdMode::kScan>(args, stream);
     else
-        launch_state<4, StateBwdMode::kScan>(args, dtype, stream);
+        launch_state<float, 4, StateBwdMode::kScan>(args, stream);
     return hipGetLastError();
 }
 

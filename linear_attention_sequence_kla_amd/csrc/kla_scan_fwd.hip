@@ -187,49 +187,6 @@ __device__ inline void token_gates(float x0, float x1, float x2, float x3, doubl
     }
 }
 
-// One token input of a wave's L rows, held in registers across both passes.
-// float32 values are kept as loaded; bfloat16 values stay packed, two rows
-// per register (row 2j in the low half), and widen when read, which halves
-// the registers the rows take.
-template <typename In, int L>
-struct GateRows {
-    float v[L];
-    __device__ void load(int i, const char* base, uint32_t off) {
-        v[i] = __builtin_nontemporal_load(reinterpret_cast<const float*>(base + off));
-    }
-    __device__ void set(int i, float x) { v[i] = x; }
-    __device__ float operator[](int i) const { return v[i]; }
-    // pins the values in registers (see the first pass)
-    __device__ void keep() {
-#pragma unroll
-        for (int i = 0; i < L; ++i) asm volatile("" : "+v"(v[i]));
-    }
-};
-
-template <int L>
-struct GateRows<uint16_t, L> {
-    uint32_t v[(L + 1) / 2];
-    __device__ void put(int i, uint32_t bits) {
-        if (i & 1)
-            v[i >> 1] |= bits << 16;
-        else
-            v[i >> 1] = bits;
-    }
-    __device__ void load(int i, const char* base, uint32_t off) {
-        put(i, __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(base + off)));
-    }
-    // (x exact in bfloat16)
-    __device__ void set(int i, float x) { put(i, __float_as_uint(x) >> 16); }
-    __device__ float operator[](int i) const {
-        const uint32_t x = v[i >> 1];
-        return __uint_as_float((i & 1) ? (x & 0xffff0000u) : (x << 16));
-    }
-    __device__ void keep() {
-#pragma unroll
-        for (int i = 0; i < (L + 1) / 2; ++i) asm volatile("" : "+v"(v[i]));
-    }
-};
-
 template <typename In, int L, int W, Mode M>
 __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(3)))
 void kla_scan_kernel(FwdArgs g) {

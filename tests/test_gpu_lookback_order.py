@@ -95,6 +95,31 @@ def test_scan_forward_bf16(debug_build, shape):
     assert_parity(compare(lam.cpu(), eta.cpu(), *ref), TOL_BF16, "bf16 forward %s" % (shape,))
 
 
+@pytest.mark.parametrize("shape", [(1, 2, 9000, 128), (2, 2, 3000, 64)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_scan_training_pair_bf16(debug_build, shape):
+    """bfloat16 gates through the forward keeping states and the backward
+    from them (the backward's bfloat16 tiles: 4 waves, 5 per SIMD)."""
+    from kla_metric import TOL_BF16
+    from linear_attention_sequence_kla_amd import scan_bwd_states, scan_fwd_states
+    B, H, T, D = shape
+    g = make_gates(shape, "std", "bf16", seed=T + 2)
+    g["lam0"], g["eta0"] = make_initial_state(B, H, D, random=True, seed=T + 2)
+    d = {n: v.to(DEV) for n, v in g.items()}
+    gen = torch.Generator().manual_seed(11)
+    g_lam, g_eta = torch.randn(shape, generator=gen), torch.randn(shape, generator=gen)
+    _, _, states = scan_fwd_states(d["a"], d["p"], d["phi"], d["b"], d["lam0"], d["eta0"])
+    out = scan_bwd_states(d["a"], d["p"], d["phi"], d["b"], g_lam.to(DEV), g_eta.to(DEV),
+                          d["lam0"], d["eta0"], states=states)
+    torch.cuda.synchronize(DEV)
+    assert _health() == 0
+    grads, mags = oracle_scan_bwd(g["a"], g["p"], g["phi"], g["b"], g["lam0"], g["eta0"],
+                                  g_lam, g_eta)
+    got = dict(zip(("a", "p", "phi", "b", "lam0", "eta0"), (t.cpu() for t in out)))
+    assert_grad_parity(compare_grads(got, grads, mags), TOL_BF16, "bf16 training pair")
+    assert_grad_parity(compare_grads(got, grads, mags), TOL_F32, "bf16 training pair")
+
+
 @pytest.mark.parametrize("shape", [(1, 2, 6000, 64), (2, 4, 1500, 128)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_mixer_forward_and_backward(debug_build, shape):

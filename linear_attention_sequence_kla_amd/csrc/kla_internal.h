@@ -111,7 +111,7 @@ constexpr int kMixBwdRows = 8;
 // small-LM layer (T = 2048), level at T = 8192 and 4-7% slower on the long
 // context.  bfloat16 inputs: always 4, since their instances fit in 96
 // registers and run 5 waves per SIMD, which only workgroups of one wave
-// per SIMD can fill (8-10% faster on the 1B-scale layer than 8 waves at 4
+// per SIMD can fill (8-13% faster on the 1B-scale layer than 8 waves at 4
 // per SIMD).
 constexpr int64_t kStateBwdTallT = 8192;
 inline int state_bwd_waves(kla_dtype dt, int64_t T) {

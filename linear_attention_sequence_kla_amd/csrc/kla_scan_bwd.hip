@@ -395,7 +395,7 @@ void kla_state_bwd_kernel(StateBwdArgs g) {
     // float32 instances keep each row's 1 / (a^2 + p lam_{t-1}) from the
     // forward replay for the reverse pass (2% faster); bfloat16 instances
     // recompute it, which with their rows held packed keeps them within 96
-    // registers: 5 waves per SIMD instead of 4, 8-10% faster on the
+    // registers: 5 waves per SIMD instead of 4, 8-13% faster on the
     // 1B-scale layer.
     constexpr bool kKeepRd = sizeof(In) == 4;
     typedef typename StateOf<M>::T S;  // the per-row states kept for the reverse pass

@@ -164,11 +164,11 @@ kla_status check_workspace(void* workspace, size_t bytes, const Plan& pl) {
 
 // Workspace of kla_mixer_bwd: the look-back region (shared in turn by the
 // forward recompute and the backward kernel), the recomputed float64 states
-// after every kMixBwdRows-th row, and the per-tile sums of the channel-gate
-// gradients.
+// after every kMixBwdRows-th row, the per-tile sums of the channel-gate
+// gradients and their per-slice totals (kla::mixer_grad_slices).
 struct MixerBwdLayout {
     Plan fwd, bwd;
-    size_t off_bstate, off_partial, bytes;
+    size_t off_bstate, off_partial, off_slices, bytes;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -190,7 +190,10 @@ bool mixer_bwd_layout(int64_t B, int64_t H, int64_t T, int64_t D, const kla_dtyp
     const size_t states = align256(mixer_states_bytes(l->fwd, T));
     l->off_bstate = align256(l->fwd.ws.bytes > l->bwd.ws.bytes ? l->fwd.ws.bytes : l->bwd.ws.bytes);
     l->off_partial = l->off_bstate + states;
-    l->bytes = l->off_partial + size_t(l->bwd.n_tiles) * 2 * kla::kWave * sizeof(double);
+    l->off_slices =
+        align256(l->off_partial + size_t(l->bwd.n_tiles) * 2 * kla::kWave * sizeof(double));
+    const int64_t slices = kla::mixer_grad_slices(B, H, D, l->bwd.n_chunks);
+    l->bytes = l->off_slices + size_t(slices) * 2 * size_t(H * D) * sizeof(double);
     return true;
 }
 
@@ -207,6 +210,7 @@ bool scan_bwd_states_layout(int64_t B, int64_t H, int64_t T, int64_t D, const kl
         return false;
     l->off_bstate = align256(l->fwd.ws.bytes > l->bwd.ws.bytes ? l->fwd.ws.bytes : l->bwd.ws.bytes);
     l->off_partial = l->off_bstate + align256(mixer_states_bytes(l->fwd, T));
+    l->off_slices = l->off_partial;
     l->bytes = l->off_partial;
     return true;
 }
@@ -524,8 +528,9 @@ kla_status kla_mixer_bwd(const void* k, const void* v, const void* lam_v, const 
     if (err != hipSuccess) return fail(KLA_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
 
     // 3. channel-gate gradients
-    err = kla::launch_mixer_grad_reduce(ba.partial, g_a, g_p, B, H, D, lay.bwd.G,
-                                        lay.bwd.n_chunks, s);
+    err = kla::launch_mixer_grad_reduce(ba.partial,
+                                        reinterpret_cast<double*>(ws + lay.off_slices), g_a,
+                                        g_p, B, H, D, lay.bwd.G, lay.bwd.n_chunks, s);
     if (err != hipSuccess) return fail(KLA_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
     return KLA_OK;
 }

@@ -160,10 +160,21 @@ struct StateBwdArgs {
 hipError_t launch_state_bwd(const StateBwdArgs& args, kla_dtype dtype, StateBwdMode mode,
                             hipStream_t stream);
 // g_a[h, d], g_p[h, d]: the per-tile sums added over the batch and the chunks
-// in a fixed order.
-hipError_t launch_mixer_grad_reduce(const double* partial, float* g_a, float* g_p, int64_t B,
-                                    int64_t H, int64_t D, int64_t G, int64_t n_chunks,
-                                    hipStream_t stream);
+// in a fixed order: in mixer_grad_slices slices of the (b, chunk) pairs
+// ([slices][2][H*D] float64 in `slices`), then over the slices; with one
+// slice, directly.  One slice up to 512 pairs per channel (two rounds of
+// loads per wave); beyond, a slice per 256 pairs (one round), up to 64.
+inline int64_t mixer_grad_slices(int64_t B, int64_t H, int64_t D, int64_t n_chunks) {
+    (void)H;
+    (void)D;
+    const int64_t n = B * n_chunks;
+    if (n <= 512) return 1;
+    const int64_t s = (n + 255) / 256;
+    return s > 64 ? 64 : s;
+}
+hipError_t launch_mixer_grad_reduce(const double* partial, double* slices, float* g_a,
+                                    float* g_p, int64_t B, int64_t H, int64_t D, int64_t G,
+                                    int64_t n_chunks, hipStream_t stream);
 hipError_t launch_decode(const void* a, const void* p, const void* phi, const void* b,
                          kla_dtype dtype, float* lam, float* eta, int64_t n, hipStream_t stream);
 // One mixer token per channel: k, v, lam_v, q [n] of dtype; a, p [hd] float32

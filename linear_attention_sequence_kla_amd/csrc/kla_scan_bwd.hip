@@ -657,54 +657,63 @@ void kla_state_bwd_kernel(StateBwdArgs g) {
         advance_epoch(g.ws, tag, (g.n_chunks - 1) * g.G, g.n_tiles, lane);
 }
 
-// g_a[h, d] and g_p[h, d]: a workgroup of kReduceWaves waves per 64 channels
-// (h, d); wave w adds the per-tile sums of the (b, chunk) pairs j = w,
-// w + kReduceWaves, ... and wave 0 adds the waves' totals in order, so the
-// result does not depend on timing (deterministic).
+// g_a[h, d] and g_p[h, d] in fixed-order steps, so the result does not
+// depend on timing (deterministic).  kla_mixer_grad_slice_kernel: a
+// workgroup of kReduceWaves waves per 64 channels (h, d) and slice s of the
+// (b, chunk) pairs; wave w adds the per-tile sums of the slice's pairs
+// first + w, first + w + kReduceWaves, ..., and wave 0 adds the waves'
+// totals in order, into g_a, g_p if there is one slice, else into
+// slices[s][2][HD], which kla_mixer_grad_final_kernel adds in order.  (Long
+// sequences and many batch entries give each channel thousands of pairs:
+// slices give them enough workgroups to fill the chip, 35 against 55 us on
+// the long-context layer, where one workgroup per 64 channels left most of
+// it idle.)
 constexpr int kReduceWaves = 16;
 
-__global__ __launch_bounds__(kReduceWaves * kWave) void kla_mixer_grad_reduce_kernel(
-    const double* partial, float* g_a, float* g_p, int64_t B, int64_t H, int64_t D, int64_t G,
-    int64_t n_chunks) {
+__global__ __launch_bounds__(kReduceWaves * kWave) void kla_mixer_grad_slice_kernel(
+    const double* partial, double* slices, float* g_a, float* g_p, int64_t B, int64_t HD,
+    int64_t G, int64_t n_chunks, int64_t per) {
     __shared__ double s_sum[kReduceWaves][2][kWave];
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x / kWave;
-    const int64_t HD = H * D;
     const int64_t hd = int64_t(blockIdx.x) * kWave + lane;
+    const int64_t hdc = hd < HD ? hd : HD - 1;  // (lanes past HD read a channel that exists)
     const int64_t n = B * n_chunks;
+    const int64_t first = int64_t(blockIdx.y) * per;
+    const int64_t last = min(n, first + per);
     double sa = 0.0, sp = 0.0;
-    if (hd < HD) {
-        // pair j = b * n_chunks + cc; (b, cc) advance with j, so the loop
-        // divides once, and a batch of kBatch pairs' loads is in flight
-        // before the first one is added
-        constexpr int kBatch = 16;
-        int64_t j = w, b = j / n_chunks, cc = j - b * n_chunks;
-        while (j < n) {
-            size_t off[kBatch];
-            bool in[kBatch];
+    // pair j = b * n_chunks + cc; (b, cc) advance with j, so the loop
+    // divides once; a batch of kBatch pairs' loads is in flight before the
+    // first one is added, and pairs past the slice load a valid word and add
+    // zero (no branch around a load: the wait for it would serialise them)
+    constexpr int kBatch = 16;
+    int64_t j = first + w, b = j / n_chunks, cc = j - b * n_chunks;
+    while (j < last) {
+        size_t off[kBatch];
+        bool in[kBatch];
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                in[u] = j < n;
-                const uint64_t q = uint64_t(b * HD + hd);
-                off[u] = size_t(cc * G + int64_t(q / kWave)) * 2 * kWave + size_t(q % kWave);
-                j += kReduceWaves;
-                cc += kReduceWaves;
-                while (cc >= n_chunks) {
-                    cc -= n_chunks;
-                    ++b;
-                }
+        for (int u = 0; u < kBatch; ++u) {
+            in[u] = j < last;
+            const uint64_t q = uint64_t(b * HD + hdc);
+            off[u] = in[u] ? size_t(cc * G + int64_t(q / kWave)) * 2 * kWave + size_t(q % kWave)
+                           : 0;
+            j += kReduceWaves;
+            cc += kReduceWaves;
+            while (cc >= n_chunks) {
+                cc -= n_chunks;
+                ++b;
             }
-            double va[kBatch], vp[kBatch];
+        }
+        double va[kBatch], vp[kBatch];
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                va[u] = in[u] ? partial[off[u]] : 0.0;
-                vp[u] = in[u] ? partial[off[u] + kWave] : 0.0;
-            }
+        for (int u = 0; u < kBatch; ++u) {
+            va[u] = partial[off[u]];
+            vp[u] = partial[off[u] + kWave];
+        }
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                sa += va[u];
-                sp += vp[u];
-            }
+        for (int u = 0; u < kBatch; ++u) {
+            sa += in[u] ? va[u] : 0.0;
+            sp += in[u] ? vp[u] : 0.0;
         }
     }
     s_sum[w][0][lane] = sa;
@@ -712,13 +721,33 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void kla_mixer_grad_reduce_ke
     __syncthreads();
     if (w == 0 && hd < HD) {
         double ta = 0.0, tp = 0.0;
-        for (int j = 0; j < kReduceWaves; ++j) {
-            ta += s_sum[j][0][lane];
-            tp += s_sum[j][1][lane];
+        for (int k = 0; k < kReduceWaves; ++k) {
+            ta += s_sum[k][0][lane];
+            tp += s_sum[k][1][lane];
         }
-        g_a[hd] = float(ta);
-        g_p[hd] = float(tp);
+        if (gridDim.y == 1) {
+            g_a[hd] = float(ta);
+            g_p[hd] = float(tp);
+        } else {
+            slices[(int64_t(blockIdx.y) * 2) * HD + hd] = ta;
+            slices[(int64_t(blockIdx.y) * 2 + 1) * HD + hd] = tp;
+        }
     }
+}
+
+__global__ __launch_bounds__(kWave) void kla_mixer_grad_final_kernel(const double* slices,
+                                                                     float* g_a, float* g_p,
+                                                                     int64_t HD, int64_t S) {
+    const int64_t hd = int64_t(blockIdx.x) * kWave + threadIdx.x;
+    if (hd >= HD) return;
+    double ta = 0.0, tp = 0.0;
+#pragma unroll 8
+    for (int64_t s = 0; s < S; ++s) {
+        ta += slices[(s * 2) * HD + hd];
+        tp += slices[(s * 2 + 1) * HD + hd];
+    }
+    g_a[hd] = float(ta);
+    g_p[hd] = float(tp);
 }
 
 }  // namespace
@@ -759,13 +788,18 @@ hipError_t launch_state_bwd(const StateBwdArgs& args, kla_dtype dtype, StateBwdM
     return hipGetLastError();
 }
 
-hipError_t launch_mixer_grad_reduce(const double* partial, float* g_a, float* g_p, int64_t B,
-                                    int64_t H, int64_t D, int64_t G, int64_t n_chunks,
-                                    hipStream_t stream) {
-    const int64_t n = H * D;
-    hipLaunchKernelGGL(kla_mixer_grad_reduce_kernel, dim3(unsigned((n + kWave - 1) / kWave)),
-                       dim3(kReduceWaves * kWave), 0, stream, partial, g_a, g_p, B, H, D, G,
-                       n_chunks);
+hipError_t launch_mixer_grad_reduce(const double* partial, double* slices, float* g_a,
+                                    float* g_p, int64_t B, int64_t H, int64_t D, int64_t G,
+                                    int64_t n_chunks, hipStream_t stream) {
+    const int64_t HD = H * D, groups = (HD + kWave - 1) / kWave;
+    const int64_t S = mixer_grad_slices(B, H, D, n_chunks);
+    const int64_t per = (B * n_chunks + S - 1) / S;
+    hipLaunchKernelGGL(kla_mixer_grad_slice_kernel, dim3(unsigned(groups), unsigned(S)),
+                       dim3(kReduceWaves * kWave), 0, stream, partial, slices, g_a, g_p, B, HD,
+                       G, n_chunks, per);
+    if (S > 1)
+        hipLaunchKernelGGL(kla_mixer_grad_final_kernel, dim3(unsigned(groups)), dim3(kWave), 0,
+                           stream, slices, g_a, g_p, HD, S);
     return hipGetLastError();
 }
 

@@ -131,7 +131,7 @@ __device__ inline void publish(uint64_t* flag, int lane, uint64_t value) {
 __device__ inline bool give_up(uint32_t spins, uint32_t* header, uint32_t tag) {
     if ((spins & 255) != 0) return false;
     const uint32_t g = __hip_atomic_load(&header[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (__builtin_amdgcn_readfirstlane(g) == tag || spins >= kSpinLimit) {
+    if (uint32_t(__builtin_amdgcn_readfirstlane(g)) == tag || spins >= kSpinLimit) {
         __hip_atomic_store(&header[1], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_fetch_or(&header[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return true;

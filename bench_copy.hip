@@ -10,13 +10,16 @@
 //           order: one chunk of every 64-channel column, then the next chunk
 //           (the order that keeps a look-back a few tiles deep);
 //   addr    the same tiles in address order: every chunk of one column, then
-//           the next column.
+//           the next column;
+//   skew    the scan order with column g (column pair g / 2 when pairing)
+//           started (g mod K) * M chunks late, arg = K + 1000 M, so that the
+//           columns' active chunks sit at different offsets.
 // `pair` gives tiles 2m and 2m + 1 of each aligned block of 16 to workgroups
 // x and x + 8 (one XCD), as the library does for D a multiple of 128.
 //
 //   hipcc --offload-arch=gfx950 -O3 -std=c++17 -Xclang -target-feature \
 //       -Xclang -packed-fp32-ops bench_copy.hip -o bench_copy
-//   ./bench_copy <shape 1..3> <stream|scan|addr|band|super> <arg> <L> <W> <pair>
+//   ./bench_copy <shape 1..3> <stream|scan|addr|band|super|skew|xcdcol> <arg> <L> <W> <pair>
 // shape 1: 128 slabs x 2048 x 64 f32, 2: 128 x 8192 x 128 bf16,
 // 3: 32 x 131072 x 128 f32.  Prints the mean of 20 launches (two input and
 // output sets alternate) as time and fraction of 8 TB/s.
@@ -128,6 +131,14 @@ std::vector<std::pair<int,int>> make_order(const std::string& kind, int arg, int
       const int64_t kb = std::min<int64_t>(arg, nc - c0);
       for (int64_t g = 0; g < G; ++g) for (int64_t j = 0; j < kb; ++j) v.push_back({int(c0 + j), int(g)});
     }
+  } else if (kind == "skew") {  // scan order with column g started (g % K) * M chunks late (arg = K + 1000 M)
+    const int64_t K = std::max(1, arg % 1000), M = std::max(1, arg / 1000), shift = pair ? 1 : 0;
+    auto off = [&](int64_t g) { return ((g >> shift) % K) * M; };
+    for (int64_t s = 0; s < nc + (K - 1) * M; ++s)
+      for (int64_t g = 0; g < G; ++g) {
+        const int64_t c = s - off(g);
+        if (c >= 0 && c < nc) v.push_back({int(c), int(g)});
+      }
   } else if (kind == "xcdcol") {  // scan order, but XCD x (wg mod 8) walks its own contiguous block of columns
     // wg = 8 * m + x ; tile list per XCD: columns [x*G/8, (x+1)*G/8) in scan order
     const int64_t per = G / 8;
@@ -185,7 +196,7 @@ void run(const char* label, int kind, int arg, int L, int W, int pair, uint32_t 
   float ms; CK(hipEventElapsedTime(&ms, e0, e1));
   const double us = ms * 1000.0 / K;
   const double bytes = double(N) * (4 * sizeof(In) + 8);
-  printf("%-5s %-7s arg=%3d L=%2d W=%d pair=%d pause=%5u  %9.1f us  %6.0f GB/s  frac %.3f\n", sh.name, label, arg, L, W, pair, pause, us, bytes / us * 1e-3, bytes / us * 1e-3 / 8000.0);
+  printf("%-5s %-7s arg=%5d L=%2d W=%d pair=%d pause=%5u  %9.1f us  %6.0f GB/s  frac %.3f\n", sh.name, label, arg, L, W, pair, pause, us, bytes / us * 1e-3, bytes / us * 1e-3 / 8000.0);
   fflush(stdout);
   CK(hipEventDestroy(e0)); CK(hipEventDestroy(e1));
 }

@@ -165,10 +165,11 @@ kla_status check_workspace(void* workspace, size_t bytes, const Plan& pl) {
 // Workspace of kla_mixer_bwd: the look-back region (shared in turn by the
 // forward recompute and the backward kernel), the recomputed float64 states
 // after every kMixBwdRows-th row, the per-tile sums of the channel-gate
-// gradients and their per-slice totals (kla::mixer_grad_slices).
+// gradients, their per-slice totals (kla::mixer_grad_slices) and the
+// reduction's arrival counts.
 struct MixerBwdLayout {
     Plan fwd, bwd;
-    size_t off_bstate, off_partial, off_slices, bytes;
+    size_t off_bstate, off_partial, off_slices, off_counts, bytes;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -193,7 +194,9 @@ bool mixer_bwd_layout(int64_t B, int64_t H, int64_t T, int64_t D, const kla_dtyp
     l->off_slices =
         align256(l->off_partial + size_t(l->bwd.n_tiles) * 2 * kla::kWave * sizeof(double));
     const int64_t slices = kla::mixer_grad_slices(B, H, D, l->bwd.n_chunks);
-    l->bytes = l->off_slices + size_t(slices) * 2 * size_t(H * D) * sizeof(double);
+    l->off_counts = align256(l->off_slices + size_t(slices) * 2 * size_t(H * D) * sizeof(double));
+    l->bytes = align256(l->off_counts +
+                        size_t((H * D + kla::kWave - 1) / kla::kWave) * sizeof(uint32_t));
     return true;
 }
 
@@ -211,6 +214,7 @@ bool scan_bwd_states_layout(int64_t B, int64_t H, int64_t T, int64_t D, const kl
     l->off_bstate = align256(l->fwd.ws.bytes > l->bwd.ws.bytes ? l->fwd.ws.bytes : l->bwd.ws.bytes);
     l->off_partial = l->off_bstate + align256(mixer_states_bytes(l->fwd, T));
     l->off_slices = l->off_partial;
+    l->off_counts = l->off_partial;
     l->bytes = l->off_partial;
     return true;
 }
@@ -515,6 +519,8 @@ kla_status kla_mixer_bwd(const void* k, const void* v, const void* lam_v, const 
     ba.g_lam0 = g_lam0;
     ba.g_eta0 = g_eta0;
     ba.partial = reinterpret_cast<double*>(ws + lay.off_partial);
+    ba.counts = reinterpret_cast<uint32_t*>(ws + lay.off_counts);
+    ba.n_counts = (H * D + kla::kWave - 1) / kla::kWave;
     ba.waves = state_bwd_waves(in_dtype, T);
     ba.T = T;
     ba.D = D;
@@ -529,8 +535,9 @@ kla_status kla_mixer_bwd(const void* k, const void* v, const void* lam_v, const 
 
     // 3. channel-gate gradients
     err = kla::launch_mixer_grad_reduce(ba.partial,
-                                        reinterpret_cast<double*>(ws + lay.off_slices), g_a,
-                                        g_p, B, H, D, lay.bwd.G, lay.bwd.n_chunks, s);
+                                        reinterpret_cast<double*>(ws + lay.off_slices),
+                                        ba.counts, g_a, g_p, B, H, D, lay.bwd.G,
+                                        lay.bwd.n_chunks, s);
     if (err != hipSuccess) return fail(KLA_ERR_HIP, "kernel launch: %s", hipGetErrorString(err));
     return KLA_OK;
 }

@@ -152,6 +152,8 @@ struct StateBwdArgs {
     float* g_lam0;  // may be NULL
     float* g_eta0;  // may be NULL
     double* partial;  // kMixer only
+    uint32_t* counts; // kMixer only: the reduction's arrival counts, zeroed here
+    int64_t n_counts;
     int waves;        // state_bwd_waves(dtype, T)
     int64_t T, D, C, G, n_chunks, n_tiles, HD;
     Workspace ws;
@@ -161,20 +163,22 @@ hipError_t launch_state_bwd(const StateBwdArgs& args, kla_dtype dtype, StateBwdM
                             hipStream_t stream);
 // g_a[h, d], g_p[h, d]: the per-tile sums added over the batch and the chunks
 // in a fixed order: in mixer_grad_slices slices of the (b, chunk) pairs
-// ([slices][2][H*D] float64 in `slices`), then over the slices; with one
-// slice, directly.  One slice up to 512 pairs per channel (two rounds of
-// loads per wave); beyond, a slice per 256 pairs (one round), up to 64.
+// ([slices][2][H*D] float64 in `slices`), then over the slices by the
+// workgroup that finishes its slice last (counts: one uint32 per 64
+// channels, zeroed by the backward kernel); with one slice, directly.  A
+// slice per kReducePairs pairs (one round of loads per wave of the
+// reduction), up to kMaxReduceSlices.
+constexpr int64_t kReducePairs = 64;
+constexpr int64_t kMaxReduceSlices = 128;
 inline int64_t mixer_grad_slices(int64_t B, int64_t H, int64_t D, int64_t n_chunks) {
     (void)H;
     (void)D;
-    const int64_t n = B * n_chunks;
-    if (n <= 512) return 1;
-    const int64_t s = (n + 255) / 256;
-    return s > 64 ? 64 : s;
+    const int64_t s = (B * n_chunks + kReducePairs - 1) / kReducePairs;
+    return s < 1 ? 1 : s > kMaxReduceSlices ? kMaxReduceSlices : s;
 }
-hipError_t launch_mixer_grad_reduce(const double* partial, double* slices, float* g_a,
-                                    float* g_p, int64_t B, int64_t H, int64_t D, int64_t G,
-                                    int64_t n_chunks, hipStream_t stream);
+hipError_t launch_mixer_grad_reduce(const double* partial, double* slices, uint32_t* counts,
+                                    float* g_a, float* g_p, int64_t B, int64_t H, int64_t D,
+                                    int64_t G, int64_t n_chunks, hipStream_t stream);
 hipError_t launch_decode(const void* a, const void* p, const void* phi, const void* b,
                          kla_dtype dtype, float* lam, float* eta, int64_t n, hipStream_t stream);
 // One mixer token per channel: k, v, lam_v, q [n] of dtype; a, p [hd] float32

@@ -409,6 +409,12 @@ void kla_state_bwd_kernel(StateBwdArgs g) {
     const int64_t ticket = tile_of_workgroup(blockIdx.x, g.G, g.D, g.n_tiles);
     uint32_t tag = 0;
 
+    // the mixer: clear the arrival counts of the channel-gate reduction,
+    // which runs after this kernel
+    if constexpr (kMix)
+        if (blockIdx.x == 0 && w == 0)
+            for (int64_t k = lane; k < g.n_counts; k += kWave) g.counts[k] = 0u;
+
     if (ticket < g.n_tiles) {
         // ---- tile and lane coordinates; tiles run from the sequence's end ----
         const int64_t cc = ticket / g.G;
@@ -658,26 +664,29 @@ void kla_state_bwd_kernel(StateBwdArgs g) {
 }
 
 // g_a[h, d] and g_p[h, d] in fixed-order steps, so the result does not
-// depend on timing (deterministic).  kla_mixer_grad_slice_kernel: a
-// workgroup of kReduceWaves waves per 64 channels (h, d) and slice s of the
-// (b, chunk) pairs; wave w adds the per-tile sums of the slice's pairs
-// first + w, first + w + kReduceWaves, ..., and wave 0 adds the waves'
-// totals in order, into g_a, g_p if there is one slice, else into
-// slices[s][2][HD], which kla_mixer_grad_final_kernel adds in order.  (Long
-// sequences and many batch entries give each channel thousands of pairs:
-// slices give them enough workgroups to fill the chip, 35 against 55 us on
-// the long-context layer, where one workgroup per 64 channels left most of
-// it idle.)
-constexpr int kReduceWaves = 16;
+// depend on timing (deterministic).  Workgroup (x, s) takes 64 channels
+// (h, d) and slice s of the (b, chunk) pairs: wave w adds the per-tile sums
+// of pairs first + w, first + w + kReduceWaves, ..., and wave 0 adds the
+// waves' totals in order.  With one slice that is the result; otherwise it
+// goes to slices[s][2][HD], the workgroup counts itself in counts[x] (zeroed
+// by the backward kernel before this one runs), and the one that counts
+// last adds slices 0, 1, ..., S - 1 in order.  Slices and counts are
+// agent-coherent atomics: the count is taken once the slice's stores have
+// completed, and the last workgroup loads the slices after its count, as in
+// the look-back.  Small slices give the reduction one workgroup per CU or
+// more even on short layers, where a few workgroups per 64 channels left
+// the chip idle for 13 us of a 200-us backward.
+constexpr int kReduceWaves = 8;
 
-__global__ __launch_bounds__(kReduceWaves * kWave) void kla_mixer_grad_slice_kernel(
-    const double* partial, double* slices, float* g_a, float* g_p, int64_t B, int64_t HD,
-    int64_t G, int64_t n_chunks, int64_t per) {
+__global__ __launch_bounds__(kReduceWaves * kWave) void kla_mixer_grad_reduce_kernel(
+    const double* partial, double* slices, uint32_t* counts, float* g_a, float* g_p,
+    int64_t B, int64_t HD, int64_t G, int64_t n_chunks, int64_t per) {
     __shared__ double s_sum[kReduceWaves][2][kWave];
     const int lane = threadIdx.x & (kWave - 1);
-    const int w = threadIdx.x / kWave;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t hd = int64_t(blockIdx.x) * kWave + lane;
-    const int64_t hdc = hd < HD ? hd : HD - 1;  // (lanes past HD read a channel that exists)
+    const bool in_hd = hd < HD;
+    const int64_t hdc = in_hd ? hd : HD - 1;  // (lanes past HD read a channel that exists)
     const int64_t n = B * n_chunks;
     const int64_t first = int64_t(blockIdx.y) * per;
     const int64_t last = min(n, first + per);
@@ -686,7 +695,7 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void kla_mixer_grad_slice_ker
     // divides once; a batch of kBatch pairs' loads is in flight before the
     // first one is added, and pairs past the slice load a valid word and add
     // zero (no branch around a load: the wait for it would serialise them)
-    constexpr int kBatch = 16;
+    constexpr int kBatch = 8;
     int64_t j = first + w, b = j / n_chunks, cc = j - b * n_chunks;
     while (j < last) {
         size_t off[kBatch];
@@ -719,35 +728,51 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void kla_mixer_grad_slice_ker
     s_sum[w][0][lane] = sa;
     s_sum[w][1][lane] = sp;
     __syncthreads();
-    if (w == 0 && hd < HD) {
-        double ta = 0.0, tp = 0.0;
-        for (int k = 0; k < kReduceWaves; ++k) {
-            ta += s_sum[k][0][lane];
-            tp += s_sum[k][1][lane];
-        }
-        if (gridDim.y == 1) {
+    if (w != 0) return;
+    double ta = 0.0, tp = 0.0;
+#pragma unroll
+    for (int k = 0; k < kReduceWaves; ++k) {
+        ta += s_sum[k][0][lane];
+        tp += s_sum[k][1][lane];
+    }
+    const int64_t S = gridDim.y;
+    if (S == 1) {
+        if (in_hd) {
             g_a[hd] = float(ta);
             g_p[hd] = float(tp);
-        } else {
-            slices[(int64_t(blockIdx.y) * 2) * HD + hd] = ta;
-            slices[(int64_t(blockIdx.y) * 2 + 1) * HD + hd] = tp;
+        }
+        return;
+    }
+    if (in_hd) {
+        rec_store(&slices[(int64_t(blockIdx.y) * 2) * HD + hd], ta);
+        rec_store(&slices[(int64_t(blockIdx.y) * 2 + 1) * HD + hd], tp);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    uint32_t before = 0;
+    if (lane == 0)
+        before = __hip_atomic_fetch_add(&counts[blockIdx.x], 1u, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+    if (__builtin_amdgcn_readfirstlane(before) != uint32_t(S - 1)) return;
+    asm volatile("" ::: "memory");
+    double fa = 0.0, fp = 0.0;
+    for (int64_t s0 = 0; s0 < S; s0 += kBatch) {
+        double va[kBatch], vp[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int64_t sl = s0 + u < S ? s0 + u : S - 1;
+            va[u] = rec_load(&slices[(sl * 2) * HD + hdc]);
+            vp[u] = rec_load(&slices[(sl * 2 + 1) * HD + hdc]);
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            fa += s0 + u < S ? va[u] : 0.0;
+            fp += s0 + u < S ? vp[u] : 0.0;
         }
     }
-}
-
-__global__ __launch_bounds__(kWave) void kla_mixer_grad_final_kernel(const double* slices,
-                                                                     float* g_a, float* g_p,
-                                                                     int64_t HD, int64_t S) {
-    const int64_t hd = int64_t(blockIdx.x) * kWave + threadIdx.x;
-    if (hd >= HD) return;
-    double ta = 0.0, tp = 0.0;
-#pragma unroll 8
-    for (int64_t s = 0; s < S; ++s) {
-        ta += slices[(s * 2) * HD + hd];
-        tp += slices[(s * 2 + 1) * HD + hd];
+    if (in_hd) {
+        g_a[hd] = float(fa);
+        g_p[hd] = float(fp);
     }
-    g_a[hd] = float(ta);
-    g_p[hd] = float(tp);
 }
 
 }  // namespace
@@ -788,18 +813,15 @@ hipError_t launch_state_bwd(const StateBwdArgs& args, kla_dtype dtype, StateBwdM
     return hipGetLastError();
 }
 
-hipError_t launch_mixer_grad_reduce(const double* partial, double* slices, float* g_a,
-                                    float* g_p, int64_t B, int64_t H, int64_t D, int64_t G,
-                                    int64_t n_chunks, hipStream_t stream) {
+hipError_t launch_mixer_grad_reduce(const double* partial, double* slices, uint32_t* counts,
+                                    float* g_a, float* g_p, int64_t B, int64_t H, int64_t D,
+                                    int64_t G, int64_t n_chunks, hipStream_t stream) {
     const int64_t HD = H * D, groups = (HD + kWave - 1) / kWave;
     const int64_t S = mixer_grad_slices(B, H, D, n_chunks);
     const int64_t per = (B * n_chunks + S - 1) / S;
-    hipLaunchKernelGGL(kla_mixer_grad_slice_kernel, dim3(unsigned(groups), unsigned(S)),
-                       dim3(kReduceWaves * kWave), 0, stream, partial, slices, g_a, g_p, B, HD,
-                       G, n_chunks, per);
-    if (S > 1)
-        hipLaunchKernelGGL(kla_mixer_grad_final_kernel, dim3(unsigned(groups)), dim3(kWave), 0,
-                           stream, slices, g_a, g_p, HD, S);
+    hipLaunchKernelGGL(kla_mixer_grad_reduce_kernel, dim3(unsigned(groups), unsigned(S)),
+                       dim3(kReduceWaves * kWave), 0, stream, partial, slices, counts, g_a, g_p,
+                       B, HD, G, n_chunks, per);
     return hipGetLastError();
 }
 

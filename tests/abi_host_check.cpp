@@ -30,8 +30,8 @@ hipError_t launch_state_bwd(const StateBwdArgs&, kla_dtype, StateBwdMode, hipStr
     ++g_launches;
     return hipErrorInvalidValue;
 }
-hipError_t launch_mixer_grad_reduce(const double*, double*, float*, float*, int64_t, int64_t,
-                                    int64_t, int64_t, int64_t, hipStream_t) {
+hipError_t launch_mixer_grad_reduce(const double*, double*, uint32_t*, float*, float*, int64_t,
+                                    int64_t, int64_t, int64_t, int64_t, hipStream_t) {
     ++g_launches;
     return hipErrorInvalidValue;
 }

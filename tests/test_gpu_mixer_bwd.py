@@ -73,9 +73,11 @@ SHAPES = [(1, 1, 1, 1), (1, 1, 7, 3), (2, 3, 113, 7), (1, 2, 337, 64), (3, 1, 45
           (2, 3, 8, 5), (1, 2, 9, 7), (2, 1, 64, 9), (2, 1, 65, 9), (1, 3, 129, 40),
           # 8-row waves: 4 per workgroup below T = 8192, 8 from there on
           (2, 1, 32, 9), (2, 1, 33, 9), (1, 1, 8191, 5), (1, 2, 8192, 70),
-          # more than 512 (b, chunk) pairs per channel: g_a, g_p summed in
-          # slices (3 of 188 pairs, the last one short), then over them
-          (3, 1, 6000, 64)]
+          # g_a, g_p are summed in slices of 64 (b, chunk) pairs, then over
+          # the slices by the workgroup that finishes last: 9 slices of 564
+          # pairs, the last one short; at most 128 slices, so 8750 pairs
+          # give slices of 69 and leave the last one empty
+          (3, 1, 6000, 64), (70, 1, 4000, 2)]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))

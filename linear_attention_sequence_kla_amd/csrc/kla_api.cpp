@@ -183,9 +183,7 @@ size_t mixer_states_bytes(const Plan& pl, int64_t T) {
 
 bool mixer_bwd_layout(int64_t B, int64_t H, int64_t T, int64_t D, const kla_dtype& dt,
                       MixerBwdLayout* l) {
-    const kla::FwdTile tile = known_dtype(dt) ? kla::mixer_state_tile(dt)
-                                              : kla::FwdTile{kla::kFwdRows, kla::kFwdWaves};
-    if (!kla::make_plan(B, H, T, D, tile.rows, tile.waves, kla::kFwdMatrixWords,
+    if (!kla::make_plan(B, H, T, D, fwd_rows(dt, true), kla::kFwdWaves, kla::kFwdMatrixWords,
                         kla::kFwdStateWords, &l->fwd) ||
         !kla::make_plan(B, H, T, D, kla::kMixBwdRows, state_bwd_waves(dt, T), kla::kBwdMatrixWords,
                         kla::kBwdStateWords, &l->bwd))

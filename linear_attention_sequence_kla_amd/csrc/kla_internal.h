@@ -103,18 +103,6 @@ inline FwdTile scan_tile(kla_dtype dt, int64_t T) {
     if (dt == KLA_DTYPE_F32 && T >= kTallMinT) return FwdTile{kTallRows, kTallWaves};
     return FwdTile{fwd_rows(dt, false), kFwdWaves};
 }
-// The mixer backward's state recompute (MixerState: three token inputs held
-// per row, a float64 state written after every kMixBwdRows-th row).  With
-// one input fewer than the other modes it takes its own tiles: 36 float32
-// rows per wave (158 VGPRs, 3 waves/SIMD) and 32 bfloat16 rows (128 VGPRs,
-// 4 waves/SIMD), 1-1.5% faster for the whole mixer backward call than the
-// mixer's 28- and 36-row tiles; 8-wave tiles were 2-6% slower.
-constexpr int kMixStateRows = 36, kMixStateWaves = 4;
-constexpr int kMixStateRowsBf16 = 32, kMixStateWavesBf16 = 4;
-inline FwdTile mixer_state_tile(kla_dtype dt) {
-    return dt == KLA_DTYPE_F32 ? FwdTile{kMixStateRows, kMixStateWaves}
-                               : FwdTile{kMixStateRowsBf16, kMixStateWavesBf16};
-}
 constexpr int kLtiRows = 64, kLtiWaves = 4;
 constexpr int kMixBwdRows = 8;
 // Waves per workgroup of the backward kernel from states (kMixBwdRows rows

@@ -458,14 +458,8 @@ hipError_t launch_scan_fwd(const FwdArgs& args, kla_dtype dtype, FwdMode mode,
         launch<kFwdRows, kMixerRowsBf16, kFwdWaves, Mode::Mixer>(args, dtype, stream);
     else if (mode == FwdMode::kMixerTrain)
         launch<kFwdRows, kMixerRowsBf16, kFwdWaves, Mode::MixerTrain>(args, dtype, stream);
-    else if (mode == FwdMode::kMixerState && dtype == KLA_DTYPE_F32)
-        hipLaunchKernelGGL((kla_scan_kernel<float, kMixStateRows, kMixStateWaves, Mode::MixerState>),
-                           dim3(unsigned(args.n_tiles)), dim3(kMixStateWaves * kWave), 0, stream,
-                           args);
     else if (mode == FwdMode::kMixerState)
-        hipLaunchKernelGGL(
-            (kla_scan_kernel<uint16_t, kMixStateRowsBf16, kMixStateWavesBf16, Mode::MixerState>),
-            dim3(unsigned(args.n_tiles)), dim3(kMixStateWavesBf16 * kWave), 0, stream, args);
+        launch<kFwdRows, kMixerRowsBf16, kFwdWaves, Mode::MixerState>(args, dtype, stream);
     else if (mode == FwdMode::kScanState)
         launch<kFwdRows, kScanRowsBf16, kFwdWaves, Mode::ScanState>(args, dtype, stream);
     else if (mode == FwdMode::kScanTrain)

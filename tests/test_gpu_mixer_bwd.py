@@ -197,6 +197,35 @@ def test_kla_mixer_autograd():
     assert_grad_parity(rep, TOL_F32, "autograd")
 
 
+def test_workspace_left_dirty_by_other_calls():
+    """Past its header a shared workspace may hold another call's leftovers,
+    the channel-gate reduction's arrival counts among them (the backward
+    kernel clears those before the reduction runs): filled with 0xFF bytes
+    between two calls of a shape whose g_a, g_p take two slices, the mixer
+    backward gives the same gradients bit for bit, healthy and equal to the
+    oracle."""
+    from linear_attention_sequence_kla_amd import (mixer_bwd, mixer_bwd_workspace_size,
+                                                   workspace_health)
+    shape = (3, 2, 1000, 33)
+    g = _case(shape, seed=21)
+    d = {n: (None if t is None else t.to(DEV)) for n, t in g.items()}
+    ws = torch.zeros(mixer_bwd_workspace_size(*shape, torch.float32), dtype=torch.uint8,
+                     device=DEV)
+    args = (*(d[n] for n in TOKEN), d["a"], d["p"], d["g_out"], d["g_var"], d["lam0"], d["eta0"])
+    first = mixer_bwd(*args, workspace=ws)
+    torch.cuda.synchronize(DEV)
+    ws[256:].fill_(255)
+    again = mixer_bwd(*args, workspace=ws)
+    torch.cuda.synchronize(DEV)
+    assert workspace_health(ws) == 0
+    for n, x, y in zip(NAMES, first, again):
+        assert torch.equal(x, y), n
+    grads, mags = oracle(g)
+    rep = compare_grads(dict(zip(NAMES, (t.cpu() for t in again))), grads, mags)
+    _say("dirty workspace: %s" % rep)
+    assert_grad_parity(rep, TOL_F32, "dirty workspace")
+
+
 @pytest.mark.parametrize("shape,dtype", [((2, 3, 500, 24), "f32"), ((3, 3, 300, 128), "f32"),
                                          ((2, 2, 601, 48), "bf16"), ((1, 1, 7, 3), "f32"),
                                          ((2, 1, 289, 40), "bf16")],

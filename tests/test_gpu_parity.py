@@ -267,6 +267,28 @@ def test_repeated_calls_reuse_workspace():
     assert torch.allclose(first[0], again[0], rtol=1e-6)
 
 
+def test_workspace_left_dirty_by_other_calls():
+    """Past its header a shared workspace may hold another call's leftovers
+    (flags of other tags, records, counts): filled with 0xFF bytes between two
+    calls, the forward gives the same outputs bit for bit, healthy and equal
+    to the oracle."""
+    from linear_attention_sequence_kla_amd import scan_fwd, workspace_health, workspace_size
+    shape = (2, 3, 1500, 64)
+    g = make_gates(shape, "std", "f32", seed=23)
+    g["lam0"], g["eta0"] = make_initial_state(2, 3, 64, random=True, seed=23)
+    d = {k: v.to(DEV) for k, v in g.items()}
+    ws = torch.zeros(workspace_size(*shape, torch.float32), dtype=torch.uint8, device=DEV)
+    first = scan_fwd(d["a"], d["p"], d["phi"], d["b"], d["lam0"], d["eta0"], workspace=ws)
+    torch.cuda.synchronize(DEV)
+    ws[256:].fill_(255)
+    again = scan_fwd(d["a"], d["p"], d["phi"], d["b"], d["lam0"], d["eta0"], workspace=ws)
+    torch.cuda.synchronize(DEV)
+    assert workspace_health(ws) == 0
+    assert torch.equal(first[0], again[0]) and torch.equal(first[1], again[1])
+    ref = oracle_scan(g["a"], g["p"], g["phi"], g["b"], g["lam0"], g["eta0"])
+    assert_parity(compare(again[0].cpu(), again[1].cpu(), *ref), TOL_F32, "dirty workspace")
+
+
 def test_side_stream():
     """The call runs on the caller's current stream."""
     g = make_gates((2, 2, 700, 64), "std", "f32", seed=17)

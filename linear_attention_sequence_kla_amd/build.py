@@ -1,7 +1,9 @@
 """Builds libkla.so (the HIP kernels and the C ABI) in-tree for gfx950, and
 libkla_debug.so, the same library with pseudo-random pauses before every
-carry flag is published (a test build that forces the look-back through all
-its orders; see kla_lookback.h).
+carry flag is published and before each slice of the mixer's channel-gate
+reduction counts itself (a test build that forces the look-back through all
+its orders and the reduction's last arrival onto other workgroups; see
+kla_lookback.h).
 
     python -m linear_attention_sequence_kla_amd.build
 """

@@ -749,6 +749,12 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void kla_mixer_grad_reduce_ke
         rec_store(&slices[(int64_t(blockIdx.y) * 2 + 1) * HD + hd], tp);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#ifdef KLA_DEBUG_DELAYS
+    // test builds: slices count themselves in a pseudo-random order, so
+    // that a different workgroup adds them up
+    debug_delay(reinterpret_cast<const uint64_t*>(counts + blockIdx.x),
+                uint64_t(blockIdx.y) << 32);
+#endif
     uint32_t before = 0;
     if (lane == 0)
         before = __hip_atomic_fetch_add(&counts[blockIdx.x], 1u, __ATOMIC_RELAXED,

@@ -3,8 +3,9 @@ operations whichever way the look-back reaches it (the inclusive state of its
 predecessor, or an older inclusive state with the intervening tile matrices
 applied one by one: each application is exactly the step that produced the
 predecessor's state), and the channel-gate gradients of the mixer are added
-in a fixed order.  So repeated calls -- and calls through the debug build,
-whose pauses force other look-back paths -- give identical bits."""
+in a fixed order whichever workgroup adds the slices.  So repeated calls --
+and calls through the debug build, whose pauses force other look-back paths
+and other orders of the slices' arrival -- give identical bits."""
 
 from __future__ import annotations
 

@@ -676,7 +676,7 @@ void kla_state_bwd_kernel(StateBwdArgs g) {
 // the look-back.  Slices of 64 pairs spread the reduction over many
 // workgroups even on short layers: 128 on the small-LM layer (8 x 16 x 2048
 // x 64), where one workgroup per 64 channels took 13 us of a 200-us mixer
-// backward and the slices take 6.5 us.
+// backward and the slices take 6.5-7 us.
 constexpr int kReduceWaves = 8;
 
 __global__ __launch_bounds__(kReduceWaves * kWave) void kla_mixer_grad_reduce_kernel(

@@ -13,13 +13,18 @@
 //           the next column;
 //   skew    the scan order with column g (column pair g / 2 when pairing)
 //           started (g mod K) * M chunks late, arg = K + 1000 M, so that the
-//           columns' active chunks sit at different offsets.
+//           columns' active chunks sit at different offsets;
+//   colstream  no tiles dispatched at all: one workgroup per arg = 16, 32
+//           or 64 channels of a slab walks all T rows itself, tile after
+//           tile, with the next tile's loads in flight while the current one
+//           is stored (the carry of such a structure would stay on chip, with
+//           no look-back); a wave's lanes cover 64 / arg row slices.
 // `pair` gives tiles 2m and 2m + 1 of each aligned block of 16 to workgroups
 // x and x + 8 (one XCD), as the library does for D a multiple of 128.
 //
 //   hipcc --offload-arch=gfx950 -O3 -std=c++17 -Xclang -target-feature \
 //       -Xclang -packed-fp32-ops bench_copy.hip -o bench_copy
-//   ./bench_copy <shape 1..3> <stream|scan|addr|band|super|skew|xcdcol> <arg> <L> <W> <pair>
+//   ./bench_copy <shape 1..3> <stream|scan|addr|band|super|skew|xcdcol|colstream> <arg> <L> <W> <pair>
 // shape 1: 128 slabs x 2048 x 64 f32, 2: 128 x 8192 x 128 bf16,
 // 3: 32 x 131072 x 128 f32.  Prints the mean of 20 launches (two input and
 // output sets alternate) as time and fraction of 8 TB/s.
@@ -112,6 +117,71 @@ __global__ __launch_bounds__(256) void k_stream(Bufs b, int64_t N) {
   __builtin_nontemporal_store(o1, (f4v*)b.out[1] + i);
 }
 
+// colstream: workgroup = NCH channels of one slab for all T; lane = (channel,
+// row slice); tile k+1 loaded while tile k is summed, exchanged and stored.
+template <typename In, int L>
+struct ColBuf {
+  float a[L], p[L], f[L], b[L];
+  __device__ void load(const In* A, const In* P, const In* F, const In* B, int64_t o, int64_t D, int nr) {
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const int64_t oo = o + int64_t(min(i, nr - 1)) * D;
+      a[i] = ld(A + oo); p[i] = ld(P + oo); f[i] = ld(F + oo); b[i] = ld(B + oo);
+    }
+  }
+};
+
+template <typename In, int L, int W, int NCH>
+__global__ __launch_bounds__(W * 64) void k_col(Bufs bf, int64_t S, int64_t T, int64_t D) {
+  constexpr int SUB = 64 / NCH;
+  constexpr int64_t R = int64_t(L) * W * SUB;
+  __shared__ float s_sum[2][W][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int ch = lane % NCH, sub = lane / NCH;
+  const int64_t units = D / NCH;
+  const int64_t slab = blockIdx.x / units;
+  const int64_t base = slab * T * D + (blockIdx.x - slab * units) * NCH + ch;
+  const In* A = (const In*)bf.in[0] + base; const In* P = (const In*)bf.in[1] + base;
+  const In* F = (const In*)bf.in[2] + base; const In* B = (const In*)bf.in[3] + base;
+  float* o0 = bf.out[0] + base; float* o1 = bf.out[1] + base;
+  const int64_t nc = (T + R - 1) / R;
+  const int rowoff = (w * SUB + sub) * L;
+  ColBuf<In, L> x, y;
+  float carry = 0.f;
+  auto rows = [&](int64_t k) { return int(min(int64_t(L), T - (k * R + rowoff))); };
+  auto process = [&](ColBuf<In, L>& u, int64_t k) {
+    const int nr = rows(k);
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < L; ++i) s += u.a[i] * u.p[i] + u.f[i] * u.b[i];
+    s_sum[k & 1][w][lane] = s;
+    __syncthreads();
+    carry += s_sum[k & 1][(w + 1) % W][lane] * 1e-30f;
+    if (nr > 0) {
+      const int64_t o = (k * R + rowoff) * D;
+#pragma unroll
+      for (int i = 0; i < L; ++i) {
+        if (i >= nr) continue;
+        __builtin_nontemporal_store(u.a[i] + u.p[i] + carry, o0 + o + int64_t(i) * D);
+        __builtin_nontemporal_store(u.f[i] * u.b[i], o1 + o + int64_t(i) * D);
+      }
+    }
+  };
+  auto fetch = [&](ColBuf<In, L>& u, int64_t k) {
+    const int nr = rows(k);
+    if (nr > 0) u.load(A, P, F, B, (k * R + rowoff) * D, D, nr);
+  };
+  if (nc > 0) fetch(x, 0);
+  for (int64_t k = 0; k < nc; k += 2) {
+    if (k + 1 < nc) fetch(y, k + 1);
+    process(x, k);
+    if (k + 1 < nc) {
+      if (k + 2 < nc) fetch(x, k + 2);
+      process(y, k + 1);
+    }
+  }
+}
+
 struct Shape { const char* name; int64_t S, T, D; int bf16; };
 
 // Orders: tile list as (chunk, group) pairs in dispatch order.
@@ -165,6 +235,7 @@ void run(const char* label, int kind, int arg, int L, int W, int pair, uint32_t 
   const int64_t N = sh.S * sh.T * sh.D, C = sh.S * sh.D, G = (C + 63) / 64;
   const int64_t R = int64_t(L) * W, nc = R > 0 ? (sh.T + R - 1) / R : 0;
   int64_t ntiles = 0;
+  if (kind == 2 && (arg <= 0 || 64 % arg != 0 || sh.D % arg != 0)) { printf("bad channel count %d\n", arg); exit(1); }
   if (kind == 1) {
     auto v = make_order(label, arg, G, nc, pair);
     ntiles = int64_t(v.size());
@@ -178,6 +249,12 @@ void run(const char* label, int kind, int arg, int L, int W, int pair, uint32_t 
       const int64_t blocks = (N / 4 + 255) / 256;
       hipLaunchKernelGGL(k_stream<In>, dim3(blocks), dim3(256), 0, st, b, N);
       return;
+    }
+    if (kind == 2) {
+      const dim3 cgrid{unsigned(sh.S * (sh.D / arg))}, cblock{unsigned(W * 64)};
+#define TC(LL, WW, NN) if (L == LL && W == WW && arg == NN) { hipLaunchKernelGGL((k_col<In, LL, WW, NN>), cgrid, cblock, 0, st, b, sh.S, sh.T, sh.D); return; }
+      TC(4, 16, 64) TC(8, 8, 64) TC(4, 16, 32) TC(8, 8, 32) TC(8, 4, 32) TC(16, 4, 16) TC(8, 8, 16)
+      printf("no colstream variant L=%d W=%d arg=%d\n", L, W, arg); exit(1);
     }
     const dim3 grid{unsigned(ntiles)}, block{unsigned(W * 64)};
 #define TR(LL, WW) if (L == LL && W == WW) { hipLaunchKernelGGL((k_tile_reg<In, LL, WW>), grid, block, 0, st, b, sh.S, sh.T, sh.D, pause, dtable); return; }
@@ -216,7 +293,7 @@ int main(int argc, char** argv) {
   int2* dtable; CK(hipMalloc(&dtable, sizeof(int2) * (N / 64 / 16 + 1024)));
   hipStream_t st; CK(hipStreamCreate(&st));
   const std::string order = argv[2];
-  const int kind = order == "stream" ? 0 : 1;
+  const int kind = order == "stream" ? 0 : order == "colstream" ? 2 : 1;
   const int arg = atoi(argv[3]), L = atoi(argv[4]), W = atoi(argv[5]), pair = atoi(argv[6]);
   if (sh.bf16) run<uint16_t>(order.c_str(), kind, arg, L, W, pair, 0, sh, sets, st, dtable);
   else run<float>(order.c_str(), kind, arg, L, W, pair, 0, sh, sets, st, dtable);

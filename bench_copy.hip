@@ -14,6 +14,8 @@
 //   skew    the scan order with column g (column pair g / 2 when pairing)
 //           started (g mod K) * M chunks late, arg = K + 1000 M, so that the
 //           columns' active chunks sit at different offsets;
+//   pol     the scan order, loads and stores with the cache-policy bits
+//           arg = 100 * LP + SP (see k_tile_pol; 202 = non-temporal both);
 //   colstream  no tiles dispatched at all: one workgroup per arg = 16, 32
 //           or 64 channels of a slab walks all T rows itself, tile after
 //           tile, with the next tile's loads in flight while the current one
@@ -24,10 +26,10 @@
 //
 //   hipcc --offload-arch=gfx950 -O3 -std=c++17 -Xclang -target-feature \
 //       -Xclang -packed-fp32-ops bench_copy.hip -o bench_copy
-//   ./bench_copy <shape 1..3> <stream|scan|addr|band|super|skew|xcdcol|colstream> <arg> <L> <W> <pair>
+//   ./bench_copy <shape 1..3> <stream|scan|addr|band|super|skew|xcdcol|pol|colstream> <arg> <L> <W> <pair> [sets]
 // shape 1: 128 slabs x 2048 x 64 f32, 2: 128 x 8192 x 128 bf16,
-// 3: 32 x 131072 x 128 f32.  Prints the mean of 20 launches (two input and
-// output sets alternate) as time and fraction of 8 TB/s.
+// 3: 32 x 131072 x 128 f32.  Prints the mean of 20 launches (`sets` input
+// and output sets, default 2, used in turn) as time and fraction of 8 TB/s.
 #include <hip/hip_runtime.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -91,6 +93,58 @@ __global__ __launch_bounds__(W * 64) void k_tile_reg(Bufs b, int64_t S, int64_t 
       if (i >= nr) continue;
       __builtin_nontemporal_store(ra[i] + rp[i] + tot, o0 + int64_t(i) * D);
       __builtin_nontemporal_store(rf[i] * rb[i], o1 + int64_t(i) * D);
+    }
+  }
+}
+
+// pol: the scan order's tiles read and written with buffer instructions whose
+// cache-policy immediate is LP (loads) and SP (stores): bit 0 sc0, bit 1 nt,
+// bit 4 sc1 (sc1:sc0 the coherence scope: wave, group, device, system; nt
+// non-temporal).  A wave's buffer descriptors start at its first element.
+template <int POL> __device__ inline float bld(__amdgpu_buffer_rsrc_t r, uint32_t off, float*) { return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, POL); }
+template <int POL> __device__ inline float bld(__amdgpu_buffer_rsrc_t r, uint32_t off, uint16_t*) { return __uint_as_float(uint32_t(__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, POL)) << 16); }
+template <typename In, int L, int W, int LP, int SP>
+__global__ __launch_bounds__(W * 64) void k_tile_pol(Bufs b, int64_t S, int64_t T, int64_t D, const int2* table) {
+  __shared__ float s_sum[W][64];
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t C = S * D;
+  const int2 cg = table[blockIdx.x];
+  const int64_t c = cg.x, g = cg.y;
+  const int64_t R = int64_t(L) * W;
+  const int64_t q0 = g * 64;
+  const int64_t slab0 = q0 / D, d0 = q0 - slab0 * D;
+  const int64_t q = q0 + lane;
+  const bool valid = q < C;
+  const int64_t qc = valid ? q : q0;
+  const int64_t slab = qc / D, d = qc - slab * D;
+  const int64_t t0 = c * R + int64_t(w) * L;
+  const int nr = int(min(int64_t(L), T - t0));
+  const int64_t e0 = (slab0 * T + t0) * D + d0;
+  const uint32_t lane_el = uint32_t((slab - slab0) * T * D + d - d0);
+  auto rs = [&](const void* p, int esz) { return __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)p + e0 * esz), 0, 0x7fffffff, 0x00020000); };
+  const auto ra_ = rs(b.in[0], sizeof(In)), rp_ = rs(b.in[1], sizeof(In)), rf_ = rs(b.in[2], sizeof(In)), rb_ = rs(b.in[3], sizeof(In));
+  float ra[L], rp[L], rf[L], rb[L];
+  float s = 0.f;
+  if (nr > 0) {
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const uint32_t o = (lane_el + uint32_t(min(i, nr - 1)) * uint32_t(D)) * sizeof(In);
+      ra[i] = bld<LP>(ra_, o, (In*)0); rp[i] = bld<LP>(rp_, o, (In*)0); rf[i] = bld<LP>(rf_, o, (In*)0); rb[i] = bld<LP>(rb_, o, (In*)0);
+    }
+#pragma unroll
+    for (int i = 0; i < L; ++i) s += ra[i] * rp[i] + rf[i] * rb[i];
+  }
+  s_sum[w][lane] = s;
+  __syncthreads();
+  const float tot = s_sum[(w + 1) % W][lane] * 1e-30f;
+  const auto o0 = rs(b.out[0], 4), o1 = rs(b.out[1], 4);
+  if (nr > 0 && valid) {
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      if (i >= nr) continue;
+      const uint32_t o = (lane_el + uint32_t(i) * uint32_t(D)) * 4;
+      __builtin_amdgcn_raw_buffer_store_b32(ra[i] + rp[i] + tot, o0, o, 0, SP);
+      __builtin_amdgcn_raw_buffer_store_b32(rf[i] * rb[i], o1, o, 0, SP);
     }
   }
 }
@@ -231,13 +285,13 @@ std::vector<std::pair<int,int>> make_order(const std::string& kind, int arg, int
 }
 
 template <typename In>
-void run(const char* label, int kind, int arg, int L, int W, int pair, uint32_t pause, const Shape& sh, Bufs* sets, hipStream_t st, int2* dtable) {
+void run(const char* label, int kind, int arg, int L, int W, int pair, uint32_t pause, const Shape& sh, Bufs* sets, int nsets, hipStream_t st, int2* dtable) {
   const int64_t N = sh.S * sh.T * sh.D, C = sh.S * sh.D, G = (C + 63) / 64;
   const int64_t R = int64_t(L) * W, nc = R > 0 ? (sh.T + R - 1) / R : 0;
   int64_t ntiles = 0;
   if (kind == 2 && (arg <= 0 || 64 % arg != 0 || sh.D % arg != 0)) { printf("bad channel count %d\n", arg); exit(1); }
-  if (kind == 1) {
-    auto v = make_order(label, arg, G, nc, pair);
+  if (kind == 1 || kind == 3) {
+    auto v = make_order(kind == 3 ? "scan" : label, arg, G, nc, pair);
     ntiles = int64_t(v.size());
     if (ntiles != G * nc) { printf("bad order size\n"); exit(1); }
     std::vector<int2> h(ntiles);
@@ -250,6 +304,14 @@ void run(const char* label, int kind, int arg, int L, int W, int pair, uint32_t 
       hipLaunchKernelGGL(k_stream<In>, dim3(blocks), dim3(256), 0, st, b, N);
       return;
     }
+    if (kind == 3) {
+      const dim3 grid{unsigned(ntiles)}, block{unsigned(W * 64)};
+#define TP(LL, WW, LPP, SPP) if (L == LL && W == WW && arg == LPP * 100 + SPP) { hipLaunchKernelGGL((k_tile_pol<In, LL, WW, LPP, SPP>), grid, block, 0, st, b, sh.S, sh.T, sh.D, dtable); return; }
+#define TPS(LL, WW) TP(LL, WW, 2, 2) TP(LL, WW, 3, 2) TP(LL, WW, 18, 2) TP(LL, WW, 19, 2) TP(LL, WW, 16, 2) TP(LL, WW, 1, 2) \
+      TP(LL, WW, 2, 3) TP(LL, WW, 2, 18) TP(LL, WW, 2, 19) TP(LL, WW, 2, 16) TP(LL, WW, 18, 18) TP(LL, WW, 19, 19) TP(LL, WW, 0, 2) TP(LL, WW, 2, 0)
+      TPS(28, 4) TPS(24, 4) TPS(14, 8)
+      printf("no pol variant\n"); exit(1);
+    }
     if (kind == 2) {
       const dim3 cgrid{unsigned(sh.S * (sh.D / arg))}, cblock{unsigned(W * 64)};
 #define TC(LL, WW, NN) if (L == LL && W == WW && arg == NN) { hipLaunchKernelGGL((k_col<In, LL, WW, NN>), cgrid, cblock, 0, st, b, sh.S, sh.T, sh.D); return; }
@@ -261,13 +323,13 @@ void run(const char* label, int kind, int arg, int L, int W, int pair, uint32_t 
     TR(28, 4) TR(24, 4) TR(16, 4) TR(32, 4) TR(14, 8) TR(20, 4)
     printf("no variant L=%d W=%d\n", L, W); exit(1);
   };
-  for (int i = 0; i < 3; ++i) launch(sets[i & 1]);
+  for (int i = 0; i < 3; ++i) launch(sets[i % nsets]);
   CK(hipGetLastError());
   hipEvent_t e0, e1;
   CK(hipEventCreate(&e0)); CK(hipEventCreate(&e1));
   const int K = 20;
   CK(hipEventRecord(e0, st));
-  for (int i = 0; i < K; ++i) launch(sets[i & 1]);
+  for (int i = 0; i < K; ++i) launch(sets[i % nsets]);
   CK(hipEventRecord(e1, st));
   CK(hipEventSynchronize(e1));
   float ms; CK(hipEventElapsedTime(&ms, e0, e1));
@@ -285,17 +347,19 @@ int main(int argc, char** argv) {
   const Shape sh = shapes[which - 1];
   const int64_t N = sh.S * sh.T * sh.D;
   const size_t esz = sh.bf16 ? 2 : 4;
-  Bufs sets[2];
-  for (int s = 0; s < 2; ++s) {
+  const int nsets = argc > 7 ? atoi(argv[7]) : 2;
+  if (nsets < 1 || nsets > 16) { printf("sets must be 1..16\n"); return 2; }
+  Bufs sets[16];
+  for (int s = 0; s < nsets; ++s) {
     for (int i = 0; i < 4; ++i) { void* p; CK(hipMalloc(&p, N * esz)); CK(hipMemset(p, 0x3c, N * esz)); sets[s].in[i] = p; }
     for (int i = 0; i < 2; ++i) { CK(hipMalloc(&sets[s].out[i], N * 4)); }
   }
   int2* dtable; CK(hipMalloc(&dtable, sizeof(int2) * (N / 64 / 16 + 1024)));
   hipStream_t st; CK(hipStreamCreate(&st));
   const std::string order = argv[2];
-  const int kind = order == "stream" ? 0 : order == "colstream" ? 2 : 1;
+  const int kind = order == "stream" ? 0 : order == "colstream" ? 2 : order == "pol" ? 3 : 1;
   const int arg = atoi(argv[3]), L = atoi(argv[4]), W = atoi(argv[5]), pair = atoi(argv[6]);
-  if (sh.bf16) run<uint16_t>(order.c_str(), kind, arg, L, W, pair, 0, sh, sets, st, dtable);
-  else run<float>(order.c_str(), kind, arg, L, W, pair, 0, sh, sets, st, dtable);
+  if (sh.bf16) run<uint16_t>(order.c_str(), kind, arg, L, W, pair, 0, sh, sets, nsets, st, dtable);
+  else run<float>(order.c_str(), kind, arg, L, W, pair, 0, sh, sets, nsets, st, dtable);
   return 0;
 }

@@ -53,7 +53,25 @@ def build_debug(verbose: bool = False) -> str:
     return build(DEBUG_LIBRARY, extra=("-DKLA_DEBUG_DELAYS",), verbose=verbose)
 
 
+COPY_SOURCE = os.path.join(ROOT, "bench_copy.hip")
+COPY_BINARY = os.path.join(ROOT, "bench_copy")
+
+
+def build_copy_bench(verbose: bool = False) -> str:
+    """Builds bench_copy (the standalone copy prototypes of the forward
+    scan's memory structure, a measurement tool outside the library)."""
+    tmp = COPY_BINARY + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", COPY_SOURCE, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, COPY_BINARY)
+    return COPY_BINARY
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
     print(build_debug(verbose=True))
+    print(build_copy_bench(verbose=True))
     sys.exit(0)
